@@ -1,0 +1,337 @@
+"""Float64 reference implementation (test infrastructure only; see package doc).
+
+Array conventions (logical layouts; the oracle never looks at strides):
+
+* q     [B, L, Hq, Dqk]   k [B, L, Hkv, Dqk]   v [B, L, Hkv, Dv]
+* o     [B, L, Hq, Dv]    lse [B, Hq, L]       (natural log)
+* query head h reads kv head  h // (Hq // Hkv).
+
+Readings of the sources that the code below relies on (each is also listed in
+the design notes of the repository):
+
+* the window of query block qb is the union of the global blocks
+  [0, n_global) and the local blocks [qb - n_local + 1, qb], clipped to
+  [0, qb]; blocks are counted once (a 0/1 mask, "LoZA: ZigZag sparse
+  attention" page, section 2.1, equation (2));
+* inside the query's own block the rule is causal, key j <= query i,
+  self included (same page, section 2.2.1);
+* the scale is a caller-supplied constant, 1/sqrt(d) by default (same page,
+  section 2.1, equation (1));
+* rows at or beyond L do not exist and keys at or beyond L are never read.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from fractions import Fraction
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Window:
+    """Block-window geometry: 1 global + 7 local blocks of 128 tokens by default
+    (QbitAI report on LongCat LoZA, sparse-window paragraph)."""
+    block_size: int = 128
+    n_global: int = 1
+    n_local: int = 7
+
+    @property
+    def width(self) -> int:
+        return self.n_global + self.n_local
+
+
+DEFAULT_WINDOW = Window()
+
+
+# ---------------------------------------------------------------------------
+# block index
+# ---------------------------------------------------------------------------
+
+def window_blocks(qb: int, win: Window = DEFAULT_WINDOW) -> list[int]:
+    """Ascending, distinct block ids readable from query block ``qb``."""
+    glob = set(range(0, min(win.n_global, qb + 1)))
+    local = set(range(max(0, qb - win.n_local + 1), qb + 1))
+    return sorted(glob | local)
+
+
+def block_index(n_qblocks: int, win: Window = DEFAULT_WINDOW):
+    """idx int32 [n_qblocks, W] (ascending, -1 padded), cnt int32 [n_qblocks]."""
+    W = win.width
+    idx = np.full((n_qblocks, W), -1, np.int32)
+    cnt = np.zeros(n_qblocks, np.int32)
+    for qb in range(n_qblocks):
+        ids = window_blocks(qb, win)
+        idx[qb, :len(ids)] = ids
+        cnt[qb] = len(ids)
+    return idx, cnt
+
+
+def block_index_seq(seq_lens, win: Window = DEFAULT_WINDOW):
+    """Decode rows: the query of a sequence of length n sits at position n - 1."""
+    seq_lens = np.asarray(seq_lens)
+    W = win.width
+    idx = np.full((len(seq_lens), W), -1, np.int32)
+    cnt = np.zeros(len(seq_lens), np.int32)
+    for b, n in enumerate(seq_lens):
+        ids = window_blocks((int(n) - 1) // win.block_size, win)
+        idx[b, :len(ids)] = ids
+        cnt[b] = len(ids)
+    return idx, cnt
+
+
+# ---------------------------------------------------------------------------
+# masked softmax attention, the plain definition
+# ---------------------------------------------------------------------------
+
+def _attend(qr: np.ndarray, kr: np.ndarray, vr: np.ndarray, allowed: np.ndarray, scale: float):
+    """Softmax attention of rows ``qr`` [R, D] over keys ``kr`` [N, D] / values
+    ``vr`` [N, Dv], restricted to ``allowed`` [R, N]; every row allows >= 1 key.
+
+    s = scale * q.k ; m = max over allowed ; w = exp(s - m) ; o = sum w v / sum w ;
+    lse = m + ln(sum w).
+    """
+    s = scale * (qr @ kr.T)
+    s = np.where(allowed, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    w = np.exp(s - m)
+    l = w.sum(axis=1, keepdims=True)
+    o = (w @ vr) / l
+    return o, m[:, 0] + np.log(l[:, 0])
+
+
+def _kv_head(h: int, Hq: int, Hkv: int) -> int:
+    return h // (Hq // Hkv)
+
+
+def ssa_rows(q_rows, row0, k_seq, v_seq, scale, heads, Hq, win: Window = DEFAULT_WINDOW):
+    """SSA output for rows ``row0 .. row0+R-1`` of ONE sequence.
+
+    q_rows [R, len(heads), Dqk] are those rows for the query heads ``heads``;
+    k_seq [L, Hkv, Dqk] / v_seq [L, Hkv, Dv] hold (at least) every key the rows
+    may read.  The rows must lie in a single query block.
+    Returns o [R, len(heads), Dv], lse [R, len(heads)].
+    """
+    q_rows = np.asarray(q_rows, np.float64)
+    R = q_rows.shape[0]
+    bs = win.block_size
+    qb = row0 // bs
+    assert (row0 + R - 1) // bs == qb, "rows must share one query block"
+    L, Hkv = k_seq.shape[0], k_seq.shape[1]
+    pos = np.concatenate([np.arange(t * bs, min((t + 1) * bs, L)) for t in window_blocks(qb, win)])
+    rows = row0 + np.arange(R)
+    allowed = pos[None, :] <= rows[:, None]
+    o = np.empty((R, len(heads), v_seq.shape[2]))
+    lse = np.empty((R, len(heads)))
+    for n, h in enumerate(heads):
+        g = _kv_head(h, Hq, Hkv)
+        o[:, n], lse[:, n] = _attend(q_rows[:, n], np.asarray(k_seq[pos, g], np.float64),
+                                     np.asarray(v_seq[pos, g], np.float64), allowed, scale)
+    return o, lse
+
+
+def ssa_attention(q, k, v, scale, win: Window = DEFAULT_WINDOW):
+    """Full SSA output: o [B, L, Hq, Dv], lse [B, Hq, L]."""
+    B, L, Hq, _ = q.shape
+    Dv = v.shape[3]
+    o = np.empty((B, L, Hq, Dv))
+    lse = np.empty((B, Hq, L))
+    heads = list(range(Hq))
+    bs = win.block_size
+    for b in range(B):
+        for r0 in range(0, L, bs):
+            r1 = min(r0 + bs, L)
+            ob, lb = ssa_rows(q[b, r0:r1], r0, k[b], v[b], scale, heads, Hq, win)
+            o[b, r0:r1] = ob
+            lse[b, :, r0:r1] = lb.T
+    return o, lse
+
+
+def dense_causal_rows(q_rows, row0, k_seq, v_seq, scale, heads, Hq):
+    """Causal attention (key j <= query i) for rows row0 .. row0+R-1 of one sequence."""
+    q_rows = np.asarray(q_rows, np.float64)
+    R = q_rows.shape[0]
+    Hkv = k_seq.shape[1]
+    end = row0 + R
+    allowed = np.arange(end)[None, :] <= (row0 + np.arange(R))[:, None]
+    o = np.empty((R, len(heads), v_seq.shape[2]))
+    lse = np.empty((R, len(heads)))
+    for n, h in enumerate(heads):
+        g = _kv_head(h, Hq, Hkv)
+        o[:, n], lse[:, n] = _attend(q_rows[:, n], np.asarray(k_seq[:end, g], np.float64),
+                                     np.asarray(v_seq[:end, g], np.float64), allowed, scale)
+    return o, lse
+
+
+def dense_causal(q, k, v, scale, chunk: int = 128):
+    B, L, Hq, _ = q.shape
+    o = np.empty((B, L, Hq, v.shape[3]))
+    lse = np.empty((B, Hq, L))
+    heads = list(range(Hq))
+    for b in range(B):
+        for r0 in range(0, L, chunk):
+            r1 = min(r0 + chunk, L)
+            ob, lb = dense_causal_rows(q[b, r0:r1], r0, k[b], v[b], scale, heads, Hq)
+            o[b, r0:r1] = ob
+            lse[b, :, r0:r1] = lb.T
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# decode over a paged cache
+# ---------------------------------------------------------------------------
+
+def decode(q, k_pages, v_pages, block_table, seq_lens, scale, win: Window = DEFAULT_WINDOW,
+           batches=None):
+    """One new query per sequence over a paged cache.
+
+    q [B, Hq, Dqk]; k_pages [P, Hkv, page, Dqk]; v_pages [P, Hkv, page, Dv]
+    (page == block size); block_table [B, max_blocks] maps logical block ->
+    physical page; seq_lens [B] counts the new token, whose key/value are
+    already in the cache, so the query sits at position n - 1.
+    Returns o [B, Hq, Dv], lse [B, Hq] (rows of ``batches`` only, if given).
+    """
+    B, Hq, _ = q.shape
+    Hkv = k_pages.shape[1]
+    bs = win.block_size
+    assert k_pages.shape[2] == bs
+    batches = range(B) if batches is None else batches
+    o = np.full((B, Hq, v_pages.shape[3]), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    for b in batches:
+        n = int(seq_lens[b])
+        blocks = window_blocks((n - 1) // bs, win)
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            ks, vs = [], []
+            for t in blocks:
+                page = int(block_table[b, t])
+                valid = min(bs, n - t * bs)
+                ks.append(np.asarray(k_pages[page, g, :valid], np.float64))
+                vs.append(np.asarray(v_pages[page, g, :valid], np.float64))
+            kr, vr = np.concatenate(ks), np.concatenate(vs)
+            qr = np.asarray(q[b, h], np.float64)[None, :]
+            ob, lb = _attend(qr, kr, vr, np.ones((1, kr.shape[0]), bool), scale)
+            o[b, h], lse[b, h] = ob[0], lb[0]
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# page selection (sink page + local pages + top-M scored pages)
+# ---------------------------------------------------------------------------
+
+def block_sums(x, block: int = 128):
+    """Per-block sums over the sequence axis: [B, L, H, D] -> [B, nblocks, H, D] (fp64).
+
+    The query-block-mean . page-mean score of the variant ranks pages exactly
+    like the sum . sum score (a positive factor per query block), so sums are used.
+    """
+    x = np.asarray(x, np.float64)
+    B, L, H, D = x.shape
+    nb = (L + block - 1) // block
+    out = np.zeros((B, nb, H, D))
+    for t in range(nb):
+        out[:, t] = x[:, t * block:min((t + 1) * block, L)].sum(axis=1)
+    return out
+
+
+def _exact_scores(qsum_exact, ksum_exact, cands):
+    return [sum(a * b for a, b in zip(qsum_exact, ksum_exact[c])) for c in cands]
+
+
+def page_select(q, k, win: Window = DEFAULT_WINDOW, top_m: int = 8):
+    """Block lists for page-selected attention (LongCat sparse attention article,
+    section 3: sink + sliding window kept, top-M pages by a coarse page score).
+
+    For query head h and query block qb the list is the window of ``qb`` plus the
+    ``top_m`` candidate pages c in [n_global, qb - n_local] with the highest
+    score <sum of q over block qb, sum of k over page c> (kv head of h); equal
+    scores prefer the lower page.  When there are at most ``top_m`` candidates
+    all are taken.  Lists are ascending and padded with -1 to
+    W = n_global + n_local + top_m.
+
+    Returns idx int32 [B, Hq, nqb, W], cnt int32 [B, Hq, nqb] and
+    near bool [B, Hq, nqb]: rows whose float64 scores left the top-M boundary
+    within rounding error and were therefore re-decided with exact rationals
+    (any selection within that error band is an equally valid float answer).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    B, L, Hq, D = q.shape
+    Hkv = k.shape[2]
+    bs = win.block_size
+    nqb = (L + bs - 1) // bs
+    W = win.width + top_m
+    qs = block_sums(q, bs)
+    ks = block_sums(k, bs)
+    idx = np.full((B, Hq, nqb, W), -1, np.int32)
+    cnt = np.zeros((B, Hq, nqb), np.int32)
+    near = np.zeros((B, Hq, nqb), bool)
+    for b in range(B):
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            for qb in range(nqb):
+                base = window_blocks(qb, win)
+                cands = list(range(win.n_global, qb - win.n_local + 1))
+                if len(cands) <= top_m:
+                    chosen = cands
+                else:
+                    a = qs[b, qb, h]
+                    kc = ks[b, cands, g]
+                    sc = kc @ a
+                    err = 1e-9 * (np.abs(kc) @ np.abs(a))
+                    order = sorted(range(len(cands)), key=lambda n: (-sc[n], cands[n]))
+                    sm, sn = sc[order[top_m - 1]], sc[order[top_m]]
+                    if sm - sn > 2.0 * err.max():
+                        chosen = [cands[n] for n in order[:top_m]]
+                    else:
+                        near[b, h, qb] = True
+                        rq = q[b, qb * bs:min((qb + 1) * bs, L), h]
+                        qsum_exact = [sum(Fraction(float(x)) for x in rq[:, d]) for d in range(D)]
+                        ksum_exact = {}
+                        for c in cands:
+                            rk = np.asarray(k[b, c * bs:(c + 1) * bs, g])
+                            ksum_exact[c] = [sum(Fraction(float(x)) for x in rk[:, d]) for d in range(D)]
+                        ex = _exact_scores(qsum_exact, ksum_exact, cands)
+                        order = sorted(range(len(cands)), key=lambda n: (-ex[n], cands[n]))
+                        chosen = [cands[n] for n in order[:top_m]]
+                ids = sorted(set(base) | set(chosen))
+                idx[b, h, qb, :len(ids)] = ids
+                cnt[b, h, qb] = len(ids)
+    return idx, cnt, near
+
+
+def block_list_rows(q_rows, row0, k_seq, v_seq, scale, heads, Hq, lists, block: int = 128):
+    """Attention of rows row0.. (one query block, one sequence) over explicit block
+    lists: ``lists[n]`` is the list of readable block ids for query head heads[n];
+    keys must also satisfy j <= i."""
+    q_rows = np.asarray(q_rows, np.float64)
+    R = q_rows.shape[0]
+    L, Hkv = k_seq.shape[0], k_seq.shape[1]
+    rows = row0 + np.arange(R)
+    o = np.empty((R, len(heads), v_seq.shape[2]))
+    lse = np.empty((R, len(heads)))
+    for n, h in enumerate(heads):
+        ids = [int(t) for t in lists[n] if t >= 0]
+        pos = np.concatenate([np.arange(t * block, min((t + 1) * block, L)) for t in ids])
+        allowed = pos[None, :] <= rows[:, None]
+        g = _kv_head(h, Hq, Hkv)
+        o[:, n], lse[:, n] = _attend(q_rows[:, n], np.asarray(k_seq[pos, g], np.float64),
+                                     np.asarray(v_seq[pos, g], np.float64), allowed, scale)
+    return o, lse
+
+
+def block_list_attention(q, k, v, scale, idx, cnt, block: int = 128):
+    """Full output of attention over per-(b, h, qb) lists idx [B, Hq, nqb, W]."""
+    B, L, Hq, _ = q.shape
+    o = np.empty((B, L, Hq, v.shape[3]))
+    lse = np.empty((B, Hq, L))
+    heads = list(range(Hq))
+    for b in range(B):
+        for r0 in range(0, L, block):
+            r1 = min(r0 + block, L)
+            qb = r0 // block
+            lists = [idx[b, h, qb, :cnt[b, h, qb]] for h in heads]
+            ob, lb = block_list_rows(q[b, r0:r1], r0, k[b], v[b], scale, heads, Hq, lists, block)
+            o[b, r0:r1] = ob
+            lse[b, :, r0:r1] = lb.T
+    return o, lse

@@ -1,0 +1,420 @@
+"""Pins of the float64 oracle against facts that do not come from the oracle.
+
+* brute force: pure-Python loops over an explicit mask that is built by walking
+  back from the query's block (the window described in the QbitAI report on
+  LongCat LoZA: one global block plus the seven most recent blocks of 128
+  tokens), with math.exp and no max subtraction;
+* the dense special case against torch's own scaled_dot_product_attention;
+* closed forms: block counts, keys per query, total pairs, lse of a zero query;
+* structural outputs: one-hot values per block, constant values, the first row;
+* decode of a sequence of length n == row n - 1 of the prefill on the same data;
+* page selection re-decided with exact rationals on tiny inputs.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import Window
+
+RNG = np.random.default_rng(12345)
+
+
+# ---------------------------------------------------------------------------
+# independent brute force
+# ---------------------------------------------------------------------------
+
+def brute_window_keys(i, bs, n_global, n_local):
+    """Keys a query i may read: walk back n_local blocks from its own block, add
+    the global blocks, keep causally earlier keys."""
+    qb = i // bs
+    blocks = []
+    t = qb
+    while t >= 0 and len(blocks) < n_local:
+        blocks.append(t)
+        t -= 1
+    for g in range(n_global):
+        if g <= qb and g not in blocks:
+            blocks.append(g)
+    return [j for j in range(i + 1) if j // bs in blocks]
+
+
+def brute_rows(q, k, v, scale, rows, keys_of):
+    """Pure-Python attention for the listed rows; no max subtraction (inputs are
+    small enough that exp never overflows)."""
+    B, L, Hq, D = q.shape
+    Hkv, Dv = k.shape[2], v.shape[3]
+    out = {}
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            for i in rows:
+                keys = keys_of(i)
+                w = [math.exp(scale * math.fsum(float(q[b, i, h, c]) * float(k[b, j, g, c]) for c in range(D)))
+                     for j in keys]
+                den = math.fsum(w)
+                o = [math.fsum(w[n] * float(v[b, j, g, c]) for n, j in enumerate(keys)) / den for c in range(Dv)]
+                out[(b, h, i)] = (np.array(o), math.log(den))
+    return out
+
+
+@pytest.mark.parametrize("L,bs,ng,nl,Hq,Hkv", [
+    (37, 4, 1, 3, 2, 1),   # ragged, GQA 2:1
+    (40, 4, 1, 3, 2, 2),
+    (29, 4, 2, 2, 1, 1),   # two global blocks
+    (17, 8, 1, 7, 1, 1),   # L below the window: dense
+])
+def test_ssa_bruteforce_small(L, bs, ng, nl, Hq, Hkv):
+    D, Dv = 3, 2
+    q = RNG.standard_normal((1, L, Hq, D))
+    k = RNG.standard_normal((1, L, Hkv, D))
+    v = RNG.standard_normal((1, L, Hkv, Dv))
+    win = Window(bs, ng, nl)
+    o, lse = oracle.ssa_attention(q, k, v, 0.7, win)
+    ref = brute_rows(q, k, v, 0.7, range(L), lambda i: brute_window_keys(i, bs, ng, nl))
+    for (b, h, i), (ob, lb) in ref.items():
+        np.testing.assert_allclose(o[b, i, h], ob, rtol=1e-12, atol=1e-12)
+        assert abs(lse[b, h, i] - lb) < 1e-12
+
+
+def test_ssa_bruteforce_real_geometry():
+    """Real window (128-token blocks, 1 + 7) at L = 2304, on rows chosen around
+    every block edge that changes the window, and the ragged end."""
+    L, D = 2304, 2
+    q = RNG.standard_normal((1, L, 1, D))
+    k = RNG.standard_normal((1, L, 1, D))
+    v = RNG.standard_normal((1, L, 1, D))
+    rows = [0, 1, 127, 128, 895, 896, 1023, 1024, 1025, 1151, 1152, 1279, 2047, 2048, 2303]
+    o, lse = oracle.ssa_attention(q, k, v, 1 / math.sqrt(D))
+    ref = brute_rows(q, k, v, 1 / math.sqrt(D), rows, lambda i: brute_window_keys(i, 128, 1, 7))
+    for (b, h, i), (ob, lb) in ref.items():
+        np.testing.assert_allclose(o[b, i, h], ob, rtol=1e-11, atol=1e-12)
+        assert abs(lse[b, h, i] - lb) < 1e-11
+
+
+# ---------------------------------------------------------------------------
+# library routine: torch's attention on the dense special case and with a mask
+# ---------------------------------------------------------------------------
+
+def torch_sdpa(q, k, v, scale, mask=None, causal=False):
+    Hq, Hkv = q.shape[2], k.shape[2]
+    rep = Hq // Hkv
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(rep, dim=1)
+    vt = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(rep, dim=1)
+    m = None if mask is None else torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, is_causal=causal, scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+@pytest.mark.parametrize("L", [1, 100, 777, 1024])
+def test_short_sequences_equal_textbook_causal(L):
+    """For L <= 1024 every key before the query lies in the window, so SSA is
+    textbook causal attention (and so is the separately written dense oracle)."""
+    D = 16
+    q = RNG.standard_normal((1, L, 2, D))
+    k = RNG.standard_normal((1, L, 2, D))
+    v = RNG.standard_normal((1, L, 2, 8))
+    ref = torch_sdpa(q, k, v, 0.25, causal=True)
+    o_s, _ = oracle.ssa_attention(q, k, v, 0.25)
+    o_d, _ = oracle.dense_causal(q, k, v, 0.25)
+    np.testing.assert_allclose(o_s, ref, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(o_d, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_dense_causal_long_matches_torch():
+    L, D = 1500, 8
+    q = RNG.standard_normal((1, L, 2, D))
+    k = RNG.standard_normal((1, L, 1, D))
+    v = RNG.standard_normal((1, L, 1, 4))
+    ref = torch_sdpa(q, k, v, 0.3, causal=True)
+    o_d, _ = oracle.dense_causal(q, k, v, 0.3)
+    np.testing.assert_allclose(o_d, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_ssa_long_matches_torch_with_walked_mask():
+    L, D = 1700, 16
+    q = RNG.standard_normal((1, L, 2, D))
+    k = RNG.standard_normal((1, L, 2, D))
+    v = RNG.standard_normal((1, L, 2, 16))
+    mask = np.zeros((L, L), bool)
+    for i in range(L):
+        mask[i, brute_window_keys(i, 128, 1, 7)] = True
+    ref = torch_sdpa(q, k, v, 1 / 4, mask=mask)
+    o, _ = oracle.ssa_attention(q, k, v, 1 / 4)
+    np.testing.assert_allclose(o, ref, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+
+def nkeys_closed(i):
+    """Keys per query for the default window: i + 1 below 1024, else one full
+    global block + 6 full local blocks + the causal part of the own block."""
+    return i + 1 if i < 1024 else 128 + 6 * 128 + (i % 128) + 1
+
+
+def pairs_closed(L):
+    if L <= 1024:
+        return L * (L + 1) // 2
+    assert L % 128 == 0
+    return 524800 + (1921 * (L - 1024)) // 2
+
+
+def test_block_index_closed_form():
+    idx, cnt = oracle.block_index(300)
+    for qb in range(300):
+        assert cnt[qb] == min(qb + 1, 8)
+        row = list(idx[qb, :cnt[qb]])
+        assert row == sorted(set(row))
+        assert 0 in row and qb in row
+        assert all(x == -1 for x in idx[qb, cnt[qb]:])
+        assert max(row) == qb and (qb < 7 or min(r for r in row if r > 0) == qb - 6)
+
+
+def test_block_index_seq_matches_rows():
+    lens = np.array([1, 127, 128, 129, 1024, 1025, 65536, 131072])
+    idx, cnt = oracle.block_index_seq(lens)
+    ridx, rcnt = oracle.block_index(1024)
+    for b, n in enumerate(lens):
+        qb = (n - 1) // 128
+        assert list(idx[b]) == list(ridx[qb]) and cnt[b] == rcnt[qb]
+
+
+@pytest.mark.parametrize("L,expect", [(2048, 1508352), (32768, 31014912), (131072, 125435904),
+                                      (262144, 251330560), (1024, 524800)])
+def test_total_pairs_closed_form(L, expect):
+    """Pairs per head from the block index (blocks below the query block are
+    full, the own block is causal) equal the closed form; the window never
+    exceeds S = 1024 keys (QbitAI report: window fixed at 1024 tokens)."""
+    nqb = L // 128
+    idx, cnt = oracle.block_index(nqb)
+    total = 0
+    for qb in range(nqb):
+        full = cnt[qb] - 1
+        total += 128 * 128 * full + 128 * 129 // 2
+        assert 128 * cnt[qb] <= 1024
+    assert total == expect == pairs_closed(L)
+
+
+def test_zero_query_lse_counts_keys_and_onehot_blocks():
+    """q = 0 makes every allowed key weigh the same: lse = ln(#keys) and, with
+    one-hot values per block, o = (#keys of that block)/(#keys)."""
+    L, D = 1408 + 37, 4
+    nb = (L + 127) // 128
+    q = np.zeros((1, L, 1, D))
+    k = RNG.standard_normal((1, L, 1, D))
+    v = np.zeros((1, L, 1, nb))
+    for j in range(L):
+        v[0, j, 0, j // 128] = 1.0
+    o, lse = oracle.ssa_attention(q, k, v, 0.1)
+    for i in range(L):
+        n = nkeys_closed(i)
+        assert abs(lse[0, 0, i] - math.log(n)) < 1e-12
+        qb = i // 128
+        for t in range(nb):
+            if t == qb:
+                expect = (i % 128) + 1
+            elif t == 0 or qb - 6 <= t < qb:
+                expect = 128
+            else:
+                expect = 0
+            assert abs(o[0, i, 0, t] - expect / n) < 1e-13
+
+
+def test_constant_values_and_first_row():
+    L = 1300
+    q = RNG.standard_normal((1, L, 1, 8))
+    k = RNG.standard_normal((1, L, 1, 8))
+    v = np.broadcast_to(np.array([1.5, -2.0, 0.25]), (1, L, 1, 3)).copy()
+    o, _ = oracle.ssa_attention(q, k, v, 0.5)
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-14)  # softmax weights sum to 1
+    v2 = RNG.standard_normal((1, L, 1, 3))
+    o2, lse2 = oracle.ssa_attention(q, k, v2, 0.5)
+    np.testing.assert_allclose(o2[0, 0, 0], v2[0, 0, 0], rtol=0, atol=1e-15)
+    assert abs(lse2[0, 0, 0] - 0.5 * float(q[0, 0, 0] @ k[0, 0, 0])) < 1e-14
+
+
+# ---------------------------------------------------------------------------
+# decode == last prefill row
+# ---------------------------------------------------------------------------
+
+def _paged(k_seq, bs, rng, P_extra=5):
+    """Scatter one sequence [L, H, D] into pages [P, H, bs, D] via a random table."""
+    L, H, D = k_seq.shape
+    nblk = (L + bs - 1) // bs
+    P = nblk + P_extra
+    perm = rng.permutation(P)[:nblk]
+    pages = np.full((P, H, bs, D), np.nan)
+    for t in range(nblk):
+        rows = k_seq[t * bs:min((t + 1) * bs, L)]
+        pages[perm[t], :, :rows.shape[0]] = rows.transpose(1, 0, 2)
+    return pages, perm
+
+
+@pytest.mark.parametrize("n,Hq,Hkv", [(1, 2, 2), (200, 4, 2), (1024, 2, 1), (1025, 2, 2), (2000, 2, 2)])
+def test_decode_equals_prefill_last_row(n, Hq, Hkv):
+    rng = np.random.default_rng(n)
+    D, Dv = 8, 6
+    q = rng.standard_normal((1, n, Hq, D))
+    k = rng.standard_normal((1, n, Hkv, D))
+    v = rng.standard_normal((1, n, Hkv, Dv))
+    o_p, lse_p = oracle.ssa_attention(q, k, v, 0.3)
+    kp, perm = _paged(k[0], 128, rng)
+    vp = np.full((kp.shape[0], Hkv, 128, Dv), np.nan)
+    for t in range((n + 127) // 128):
+        rows = v[0, t * 128:min((t + 1) * 128, n)]
+        vp[perm[t], :, :rows.shape[0]] = rows.transpose(1, 0, 2)
+    bt = np.full((1, 16), -1, np.int32)
+    bt[0, :len(perm)] = perm
+    o_d, lse_d = oracle.decode(q[:, n - 1], kp, vp, bt, np.array([n]), 0.3)
+    np.testing.assert_allclose(o_d[0], o_p[0, n - 1], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse_d[0], lse_p[0, :, n - 1], rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# page selection
+# ---------------------------------------------------------------------------
+
+def test_page_select_short_is_dense():
+    """With at most top_m candidates every earlier page is kept: L <= 2048 is dense."""
+    L = 2048 + 50
+    q = RNG.standard_normal((1, L, 2, 8))
+    k = RNG.standard_normal((1, L, 1, 8))
+    idx, cnt, near = oracle.page_select(q, k, top_m=8)
+    for qb in range(16):
+        for h in range(2):
+            assert list(idx[0, h, qb, :cnt[0, h, qb]]) == list(range(qb + 1))
+    assert cnt[0, 0, 16] == 16 and not near.any()
+
+
+def test_page_select_bruteforce_exact_tiny():
+    """Tiny geometry (block 4, 1 global, 2 local, top 2): every row re-decided by
+    enumerating the candidates with exact rational scores."""
+    bs, ng, nl, M = 4, 1, 2, 2
+    win = Window(bs, ng, nl)
+    L, D = 53, 3
+    q = np.round(RNG.standard_normal((1, L, 2, D)) * 8) / 8
+    k = np.round(RNG.standard_normal((1, L, 1, D)) * 8) / 8
+    idx, cnt, _ = oracle.page_select(q, k, win, top_m=M)
+    for h in range(2):
+        for qb in range((L + bs - 1) // bs):
+            rows = range(qb * bs, min((qb + 1) * bs, L))
+            qsum = [sum(Fraction(float(q[0, i, h, c])) for i in rows) for c in range(D)]
+            base = set(range(max(0, qb - nl + 1), qb + 1)) | ({0} if qb >= 0 else set())
+            cands = [c for c in range(1, qb + 1) if c not in base]
+            score = {c: sum(qsum[d] * sum(Fraction(float(k[0, j, 0, d])) for j in range(c * bs, (c + 1) * bs))
+                            for d in range(D)) for c in cands}
+            best = sorted(cands, key=lambda c: (-score[c], c))[:M]
+            want = sorted(base | set(best))
+            assert list(idx[0, h, qb, :cnt[0, h, qb]]) == want
+
+
+def test_page_select_planted_and_ties():
+    """A page whose keys share a direction with the query block is selected; an
+    exact duplicate of the best page loses the tie to the lower index."""
+    rng = np.random.default_rng(7)
+    L, D = 128 * 40, 16
+    q = rng.standard_normal((1, L, 1, D))
+    k = rng.standard_normal((1, L, 1, D))
+    u = rng.standard_normal(D)
+    qb = 39
+    q[0, qb * 128:(qb + 1) * 128, 0] += u
+    k[0, 5 * 128:6 * 128, 0] += u            # planted page 5
+    k[0, 20 * 128:21 * 128, 0] = k[0, 5 * 128:6 * 128, 0]   # exact duplicate at 20
+    idx, cnt, near = oracle.page_select(q, k, top_m=1)
+    row = list(idx[0, 0, qb, :cnt[0, 0, qb]])
+    assert 5 in row and 20 not in row
+    idx2, cnt2, _ = oracle.page_select(q, k, top_m=2)
+    row2 = list(idx2[0, 0, qb, :cnt2[0, 0, qb]])
+    assert 5 in row2 and 20 in row2
+
+
+def test_block_list_attention_with_window_lists_is_ssa():
+    L = 1600
+    q = RNG.standard_normal((1, L, 2, 8))
+    k = RNG.standard_normal((1, L, 2, 8))
+    v = RNG.standard_normal((1, L, 2, 8))
+    idx, cnt = oracle.block_index((L + 127) // 128)
+    nqb = idx.shape[0]
+    idx4 = np.broadcast_to(idx[None, None], (1, 2, nqb, 8))
+    cnt3 = np.broadcast_to(cnt[None, None], (1, 2, nqb))
+    o1, l1 = oracle.block_list_attention(q, k, v, 0.2, idx4, cnt3)
+    o2, l2 = oracle.ssa_attention(q, k, v, 0.2)
+    np.testing.assert_allclose(o1, o2, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must be caught by one of the pins above
+# ---------------------------------------------------------------------------
+
+def _ssa_vs_brute(win=Window(4, 1, 3)):
+    L = 33
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, L, 2, 3))
+    k = rng.standard_normal((1, L, 1, 3))
+    v = rng.standard_normal((1, L, 1, 2))
+    o, lse = oracle.ssa_attention(q, k, v, 0.7, win)
+    ref = brute_rows(q, k, v, 0.7, range(L),
+                     lambda i: brute_window_keys(i, win.block_size, win.n_global, win.n_local))
+    return max(max(np.abs(o[b, i, h] - ob).max(), abs(lse[b, h, i] - lb)) for (b, h, i), (ob, lb) in ref.items())
+
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    import oracle.ssa as S
+    assert _ssa_vs_brute() < 1e-12
+    good_wb = S.window_blocks
+    good_attend = S._attend
+
+    # one local block too many
+    monkeypatch.setattr(S, "window_blocks", lambda qb, win=S.DEFAULT_WINDOW:
+                        good_wb(qb, Window(win.block_size, win.n_global, win.n_local + 1)))
+    assert _ssa_vs_brute() > 1e-3
+    monkeypatch.setattr(S, "window_blocks", good_wb)
+
+    # global block dropped
+    monkeypatch.setattr(S, "window_blocks", lambda qb, win=S.DEFAULT_WINDOW:
+                        good_wb(qb, Window(win.block_size, 0, win.n_local)))
+    assert _ssa_vs_brute() > 1e-3
+    monkeypatch.setattr(S, "window_blocks", good_wb)
+
+    # sign of the scores flipped
+    monkeypatch.setattr(S, "_attend", lambda qr, kr, vr, al, sc: good_attend(qr, kr, vr, al, -sc))
+    assert _ssa_vs_brute() > 1e-3
+
+    # keys used in place of values (wrong operand)
+    monkeypatch.setattr(S, "_attend", lambda qr, kr, vr, al, sc: good_attend(qr, kr, kr[:, :vr.shape[1]], al, sc))
+    assert _ssa_vs_brute() > 1e-3
+
+    # scale applied twice
+    monkeypatch.setattr(S, "_attend", lambda qr, kr, vr, al, sc: good_attend(qr, kr, vr, al, sc * sc))
+    assert _ssa_vs_brute() > 1e-3
+
+    # the max dropped from lse
+    def no_max(qr, kr, vr, al, sc):
+        o, lse = good_attend(qr, kr, vr, al, sc)
+        s = np.where(al, sc * (qr @ kr.T), -np.inf)
+        return o, lse - s.max(axis=1)
+    monkeypatch.setattr(S, "_attend", no_max)
+    assert _ssa_vs_brute() > 1e-3
+    monkeypatch.setattr(S, "_attend", good_attend)
+    assert _ssa_vs_brute() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# the shared generator rounds like torch
+# ---------------------------------------------------------------------------
+
+def test_generator_rounding_matches_torch():
+    import synth
+    x = np.random.default_rng(0).standard_normal(100000, dtype=np.float32) * 3
+    bits = synth.f32_to_bf16_bits(x)
+    tb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits, tb)
+    back = synth.bf16_bits_to_f32(bits)
+    assert np.array_equal(back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
