@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Benchmark of the SSA hot path on one MI355X.
+
+One step = one pass over every row of the path on resident synthetic inputs:
+
+  a1  block index            (256 query blocks)
+  a2  SSA prefill            B=1, H=16, d=128, L=32768, bf16, layout [B, H, L, D]
+  a3  SSA decode             batch 64, H=16/16, d=128, context ~ U[65536, 131072]
+  a5  dense causal layer     same tensors as a2 (the comparison layer)
+  a6+a7 page selection       L=131072, H=16, d=128, M=8
+  a8  page-selected prefill  over those lists
+
+The headline value is the SSA prefill throughput (algorithmic TFLOP/s: 4*d per
+(query, key) pair the window admits) at the L=32768 workload; the decode GB/s
+(algorithmic bytes: every admitted key and value row once, plus q and o) at
+the ~128K-context decode workload is reported beside it, each with its
+fraction of the MI355X peak (bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s).  Kernel
+times come from HIP events recorded on the stream the kernels run on.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import multiprocessing as mp
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+# ----------------------------------------------------------------------------
+# workload sizes and algorithmic work (closed forms of the window)
+# ----------------------------------------------------------------------------
+
+W2 = dict(B=1, L=32768, H=16, D=128, seed=2)
+W3 = dict(B=64, H=16, D=128, lo=65536, hi=131072, seed=3)
+W5 = dict(B=1, L=131072, H=16, D=128, M=8, seed=5)
+
+
+def keys_ssa(i: int) -> int:
+    """Keys a query at position i reads: 1 global + 7 local blocks of 128."""
+    return i + 1 if i < 1024 else 128 + 6 * 128 + (i % 128) + 1
+
+
+def keys_page(i: int, M: int = 8) -> int:
+    w = 128 * (8 + M)
+    return i + 1 if i < w else w - 128 + (i % 128) + 1
+
+
+def pairs(L: int, keys) -> int:
+    # per 128-row block the count is an arithmetic series; sum exactly
+    return sum(keys(i) for i in range(L))
+
+
+def ssa_flops(L, H, D, B=1):
+    return 4 * D * pairs(L, keys_ssa) * H * B
+
+
+def dense_flops(L, H, D, B=1):
+    return 4 * D * (L * (L + 1) // 2) * H * B
+
+
+def page_flops(L, H, D, M, B=1):
+    return 4 * D * pairs(L, lambda i: keys_page(i, M)) * H * B
+
+
+def decode_bytes(lens, Hq, Hkv, Dqk, Dv):
+    kv = sum(keys_ssa(int(n) - 1) for n in lens) * Hkv * (Dqk + Dv) * 2
+    return kv + len(lens) * Hq * (Dqk + Dv) * 2
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on the host cores (runs before any GPU use,
+# so the worker pool is forked from a process that holds no HIP state)
+# ----------------------------------------------------------------------------
+
+_CPU = {}
+
+
+def _cpu_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _cpu_task(qb):
+    import oracle
+    q, k, v = _CPU["q"], _CPU["k"], _CPU["v"]
+    H = q.shape[2]
+    rows = slice(qb * 128, (qb + 1) * 128)
+    oracle.ssa_rows(q[0, rows], qb * 128, k[0], v[0], 1 / math.sqrt(q.shape[3]), list(range(H)), H)
+    return qb
+
+
+def cpu_baseline(budget_s: float = 25.0):
+    L, H, D, seed = W2["L"], W2["H"], W2["D"], W2["seed"]
+    _CPU["q"] = synth.bf16_bits_to_f32(synth.seq_tensor(seed, synth.Q, 1, L, H, D))
+    _CPU["k"] = synth.bf16_bits_to_f32(synth.seq_tensor(seed, synth.K, 1, L, H, D))
+    _CPU["v"] = synth.bf16_bits_to_f32(synth.seq_tensor(seed, synth.V, 1, L, H, D))
+    cores = min(16, len(os.sched_getaffinity(0)))
+    ctx = mp.get_context("fork")
+    nqb = L // 128
+    order = list(range(nqb - 1, -1, -1))  # bench order: last query blocks first
+    done = []
+    with ctx.Pool(cores, initializer=_cpu_init) as pool:
+        pool.map(_cpu_task, order[:cores])  # start the workers
+        t0 = time.perf_counter()
+        for qb in pool.imap_unordered(_cpu_task, order, chunksize=1):
+            done.append(qb)
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        pool.terminate()
+    flops = sum(4 * D * sum(keys_ssa(i) for i in range(qb * 128, (qb + 1) * 128)) * H for qb in done)
+    _CPU.clear()
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"float64 numpy oracle, SSA prefill of {len(done)} of {nqb} query blocks x {H} heads of the "
+                  f"L={L} d={D} workload ({len(done) / nqb:.0%}), {dt:.1f} s wall on {cores} processes",
+        "seconds": dt,
+    }
+
+
+# ----------------------------------------------------------------------------
+# GPU part
+# ----------------------------------------------------------------------------
+
+def traffic_for(kernel_file: str, key: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current source of the kernel; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "long_context_block_ssa_amd", "csrc", kernel_file)
+    try:
+        with open(path) as f:
+            data = json.load(f)
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        ent = data.get(key)
+        if ent and ent.get("source_sha") == h:
+            return ent["bytes_per_launch"]
+    except Exception:
+        pass
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rotations", type=int, default=2, help="independent decode page sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=25.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(every row of the path fits one MI355X; sharding is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_budget)
+    if cpu:
+        print(f"[bench] cpu baseline: {cpu['value']:.4f} TFLOP/s ({cpu['sample']})", flush=True)
+
+    import torch
+    import long_context_block_ssa_amd as ssa
+
+    ssa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(bits, head_major=True):
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+        if head_major:  # [B, H, L, D] in memory, logical [B, L, H, D] view
+            return t.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3)
+        return t.to(dev)
+
+    print("[bench] generating inputs", flush=True)
+    # a2 / a5 inputs
+    L2, H2, D2, s2 = W2["L"], W2["H"], W2["D"], W2["seed"]
+    q2, k2, v2 = (up(synth.seq_tensor(s2, t, 1, L2, H2, D2)) for t in (synth.Q, synth.K, synth.V))
+    o2 = torch.empty((1, H2, L2, D2), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
+    od = torch.empty_like(o2)
+    nqb2 = L2 // 128
+    # a3 inputs: one paged pool, several independent (q, table) sets
+    B3, H3, D3, s3 = W3["B"], W3["H"], W3["D"], W3["seed"]
+    lens = synth.decode_seq_lens(s3, B3, W3["lo"], W3["hi"])
+    tables = []
+    P = None
+    for r in range(args.rotations):
+        bt, P = synth.decode_block_table(s3, lens, 128, rotation=r)
+        tables.append(bt)
+    kp = torch.full((P, H3, 128, D3), float("nan"), dtype=torch.bfloat16, device=dev)
+    vp = torch.full((P, H3, 128, D3), float("nan"), dtype=torch.bfloat16, device=dev)
+    fill = synth.decode_fill_blocks(lens, 128, 1, 7)
+    for r, bt in enumerate(tables):
+        ids, kh, vh = [], [], []
+        for b, blocks in enumerate(fill):
+            for t in blocks:
+                ids.append(int(bt[b, t]))
+                kh.append(synth.page_chunk(s3 + 100 * r, synth.K, b, t, H3, D3))
+                vh.append(synth.page_chunk(s3 + 100 * r, synth.V, b, t, H3, D3))
+        idx_t = torch.tensor(ids, dtype=torch.long, device=dev)
+        kp[idx_t] = up(np.stack(kh), head_major=False)
+        vp[idx_t] = up(np.stack(vh), head_major=False)
+    q3 = [up(synth.decode_query(s3, B3, H3, D3, rotation=r)[None], head_major=False)[0]
+          for r in range(args.rotations)]
+    bts = [torch.from_numpy(bt).to(dev) for bt in tables]
+    sl3 = torch.from_numpy(lens).to(dev)
+    o3 = torch.empty((B3, H3, D3), dtype=torch.bfloat16, device=dev)
+    # a6-a8 inputs
+    L5, H5, D5, M5, s5 = W5["L"], W5["H"], W5["D"], W5["M"], W5["seed"]
+    q5, k5, v5 = (up(synth.seq_tensor(s5, t, 1, L5, H5, D5)) for t in (synth.Q, synth.K, synth.V))
+    o5 = torch.empty((1, H5, L5, D5), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
+    nqb5 = L5 // 128
+    idx5 = torch.empty((1, H5, nqb5, 8 + M5), dtype=torch.int32, device=dev)
+    cnt5 = torch.empty((1, H5, nqb5), dtype=torch.int32, device=dev)
+    ws5 = torch.empty((ssa.page_select_workspace_size(q5, k5) + 256,), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    rows = ["a1 block_index", "a2 ssa_prefill", "a3 ssa_decode", "a5 dense_causal", "a6-a7 page_select",
+            "a8 page_prefill"]
+    nev = len(rows) + 1
+
+    def step(s, ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        idx2, cnt2 = ssa.block_index(nqb2, device=dev)
+        mark(1)
+        ssa.prefill(q2, k2, v2, ssa.lists_from_index(idx2, cnt2), out=o2)
+        mark(2)
+        r = s % args.rotations
+        ssa.decode(q3[r], kp, vp, bts[r], sl3, out=o3)
+        mark(3)
+        ssa.dense_causal(q2, k2, v2, out=od)
+        mark(4)
+        i5, c5 = ssa.page_select(q5, k5, top_m=M5, workspace=ws5)
+        mark(5)
+        ssa.prefill(q5, k5, v5, ssa.lists_per_head(i5, c5), out=o5)
+        mark(6)
+
+    print("[bench] warmup", flush=True)
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    print("[bench] timing", flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(s, evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_row = [float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)])) for i in range(len(rows))]
+    ms_step = wall * 1e3 / args.steps
+    for name, ms in zip(rows, per_row):
+        print(f"[bench] {name:22s} {ms * 1e3:10.1f} us", flush=True)
+
+    for t, name in ((o2, "ssa"), (o3, "decode"), (od, "dense"), (o5, "page")):
+        if not torch.isfinite(t.float()).all():
+            raise RuntimeError(f"non-finite {name} output")
+
+    f2 = ssa_flops(L2, H2, D2)
+    t2 = per_row[1] * 1e-3
+    tf2 = f2 / t2 / 1e12
+    b3 = decode_bytes(lens, H3, H3, D3, D3)
+    t3 = per_row[2] * 1e-3
+    gb3 = b3 / t3 / 1e9
+    fd = dense_flops(L2, H2, D2)
+    f5 = page_flops(L5, H5, D5, M5)
+    b5 = 2 * L5 * H5 * D5 * 2
+    kernels = {
+        "ssa_prefill": {"bound": "mfma", "achieved": tf2, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": tf2 / PEAK_BF16_TFLOPS, "traffic": traffic_for("prefill.hip", "ssa_prefill"),
+                        "us": per_row[1] * 1e3, "work": f2},
+        "ssa_decode": {"bound": "hbm", "achieved": gb3, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                       "frac": gb3 / PEAK_HBM_GBS, "traffic": traffic_for("decode.hip", "ssa_decode"),
+                       "us": per_row[2] * 1e3, "work": b3},
+        "dense_causal": {"bound": "mfma", "achieved": fd / (per_row[3] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": fd / (per_row[3] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         "us": per_row[3] * 1e3, "work": fd},
+        "page_select": {"bound": "hbm", "achieved": b5 / (per_row[4] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": b5 / (per_row[4] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "us": per_row[4] * 1e3, "work": b5},
+        "page_prefill": {"bound": "mfma", "achieved": f5 / (per_row[5] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": f5 / (per_row[5] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         "us": per_row[5] * 1e3, "work": f5},
+        "block_index": {"us": per_row[0] * 1e3},
+    }
+    out = {
+        "metric": "SSA prefill TFLOP/s (frac MFMA peak) + decode GB/s (frac HBM) at 128K ctx",
+        "value": tf2,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "SSA prefill B=1 H=16 d=128 L=32768 bf16 (value) + SSA decode batch 64 H=16/16 d=128 "
+                        "ctx U[65536,131072] bf16 (decode) + dense causal (same shape) + page selection "
+                        "L=131072 H=16 d=128 M=8",
+            "prefill_tokens_per_s": L2 / t2,
+            "decode_gbps": gb3,
+            "decode_frac_hbm": gb3 / PEAK_HBM_GBS,
+            "decode_tokens_per_s": B3 / t3,
+            "page_select_index_share": per_row[4] / (per_row[4] + per_row[5]),
+        },
+        "roofline": kernels["ssa_prefill"],
+        "roofline_decode": kernels["ssa_decode"],
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,212 @@
+/*
+ * ssa.h -- C ABI of libssa, block-sparse streaming attention (SSA) on MI355X (gfx950).
+ *
+ * SSA is the sparse attention of LongCat's LoZA: every query reads a fixed
+ * window of 128-token key blocks -- one global block (block 0) and the seven
+ * most recent blocks, its own block included and causally masked -- so the
+ * cost per query is bounded by S = 1024 keys (QbitAI report on LongCat LoZA,
+ * the paragraphs on the O(L*S) cost and on the 1024-token sparse window).
+ * Within the window it is ordinary softmax attention restricted by a 0/1 mask
+ * ("LoZA: ZigZag sparse attention" page, section 2.1, equations (1)-(2)).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All tensor pointers are DEVICE pointers on the caller's current HIP
+ *    device; every size is in elements unless it says bytes.
+ *  - The caller allocates and owns every buffer.  The library allocates no
+ *    device memory and keeps no state besides a thread-local error string.
+ *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL is the null stream) and never synchronises the host.
+ *  - Arguments are validated on the host before anything is enqueued; on a
+ *    validation failure nothing is launched.  Device-side contents (block
+ *    lists, page tables, sequence lengths) cannot be checked on the host; the
+ *    kernels treat out-of-range entries as documented per call and never read
+ *    or write outside the buffers described here.
+ *  - Return value: an ssa_status.  ssa_last_error() describes the last failure
+ *    of the calling thread.  The library never aborts, throws or prints.
+ *  - Results are bitwise deterministic for identical inputs and launch
+ *    arguments: no floating-point atomics are used.
+ */
+#ifndef SSA_H_
+#define SSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSA_VERSION 10000 /* 1.0.0 */
+
+typedef enum ssa_status {
+  SSA_OK = 0,
+  SSA_ERR_INVALID = 1,     /* a null pointer, a bad size, stride or alignment */
+  SSA_ERR_UNSUPPORTED = 2, /* a valid request this build has no kernel for   */
+  SSA_ERR_DEVICE = 3,      /* the HIP runtime refused a launch               */
+  SSA_ERR_WORKSPACE = 4    /* workspace missing or too small                 */
+} ssa_status;
+
+typedef enum ssa_dtype { SSA_DTYPE_F32 = 0, SSA_DTYPE_BF16 = 1 } ssa_dtype;
+
+/* Window geometry.  The defaults {128, 1, 7} are the ones of the QbitAI report
+ * on LoZA (1 global + 7 local blocks of 128 tokens).  Global blocks are
+ * [0, n_global); local blocks are [qb - n_local + 1, qb], the query's own
+ * block qb included; the union is clipped to [0, qb] and counted once. */
+typedef struct ssa_window {
+  int32_t block_size; /* tokens per block; the attention kernels need 128     */
+  int32_t n_global;   /* >= 0                                                */
+  int32_t n_local;    /* >= 1 (the own block is always local)                 */
+} ssa_window;
+
+/* Dense attention operands, logical shapes
+ *   q [B, L, Hq, Dqk], k [B, L, Hkv, Dqk], v [B, L, Hkv, Dv] -> o [B, L, Hq, Dv]
+ * stored with arbitrary element strides for (batch, position, head) and a
+ * contiguous channel dimension.  Query head h reads kv head h / (Hq / Hkv).
+ * Requirements: base pointers 16-byte aligned; every stride times the element
+ * size a multiple of 16 bytes.  v may alias k (the latent-shared layout uses
+ * v = the first Dv channels of k); o must not overlap any input.
+ * lse, when not NULL, receives the natural-log sum of exponentials of the
+ * scaled scores, fp32, contiguous [B, Hq, L].
+ * Supported (dtype, Dqk, Dv): (F32, 64, 64), (BF16, 64, 64), (BF16, 128, 128),
+ * (BF16, 576, 512).  out_dtype is BF16 or F32 for BF16 inputs, F32 for F32.
+ * scale multiplies q.k before the softmax; it must be finite and > 0
+ * (1/sqrt(Dqk) is the usual choice, section 2.1 of the ZigZag page). */
+typedef struct ssa_attn_args {
+  int32_t dtype;     /* ssa_dtype of q, k, v */
+  int32_t out_dtype; /* ssa_dtype of o       */
+  int32_t B, L, Hq, Hkv, Dqk, Dv;
+  float scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_stride[3]; /* (b, l, h) element strides */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+} ssa_attn_args;
+
+/* Per-query-block lists of readable key blocks, as written by
+ * ssa_block_index (one list shared by every batch and head: strides 0) or by
+ * ssa_page_select (one list per batch and query head).
+ *   row (b, h, qb):  idx[b*idx_sb + h*idx_sh + qb*W + s], s < cnt[b*cnt_sb + h*cnt_sh + qb]
+ * Entries must be distinct.  An entry < 0, > qb or >= ceil(L/128) is skipped;
+ * the own block qb is causally masked (key j <= query i).  A row whose list
+ * admits no key produces o = 0 and lse = -inf. */
+typedef struct ssa_block_lists {
+  const int32_t* idx;
+  const int32_t* cnt;
+  int32_t W;         /* list capacity, 1 .. 64        */
+  int32_t n_qblocks; /* rows per (b, h); >= ceil(L/128) */
+  int64_t idx_sb, idx_sh;
+  int64_t cnt_sb, cnt_sh;
+} ssa_block_lists;
+
+/* Paged decode operands.  One new query per sequence:
+ *   q [B, Hq, Dqk]  -> o [B, Hq, Dv]   (strides for (b, h); channels contiguous)
+ *   k_pages [num_pages, Hkv, page_size, Dqk], v_pages [num_pages, Hkv, page_size, Dv]
+ *     (strides for (page, head, slot); channels contiguous; v may alias k)
+ *   block_table [B, max_blocks] int32: logical block t of sequence b lives in
+ *     page block_table[b*bt_stride + t]
+ *   seq_lens [B] int32: context length INCLUDING the new token, whose key and
+ *     value are already in the cache; the query sits at position n - 1.
+ * A sequence whose length is outside [1, max_blocks*page_size], or whose
+ * window names a page outside [0, num_pages), gets an all-NaN output row (and
+ * lse = NaN) and nothing out of range is read.
+ * Supported (dtype, Dqk, Dv): (BF16, 64, 64), (BF16, 128, 128) with
+ * Hq/Hkv <= 16, and (BF16, 576, 512) with Hkv == 1. */
+typedef struct ssa_decode_args {
+  int32_t dtype; /* of q, k_pages, v_pages and o: BF16 */
+  int32_t B, Hq, Hkv, Dqk, Dv;
+  int32_t page_size; /* == the window's block_size == 128 */
+  int32_t num_pages, max_blocks;
+  float scale;
+  const void* q;
+  const void* k_pages;
+  const void* v_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* o;
+  float* lse; /* optional, contiguous [B, Hq] */
+  int64_t q_stride[2];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[2];
+  int64_t bt_stride;
+} ssa_decode_args;
+
+/* ---------------------------------------------------------------------------
+ * ssa_block_index -- the window of every query block (QbitAI report on LoZA,
+ * sparse-window paragraph).  Writes idx [n_qblocks, W] with W = n_global +
+ * n_local: the readable block ids of row qb in ascending order, padded with
+ * -1; and cnt [n_qblocks] = their number (min(qb + 1, W) for the defaults).
+ * Exact integer output.  n_qblocks >= 1; W <= 64.
+ * ------------------------------------------------------------------------- */
+int ssa_block_index(const ssa_window* win, int32_t n_qblocks, int32_t* idx, int32_t* cnt,
+                    void* stream);
+
+/* Same rule for decode rows: row b uses qb = (seq_lens[b] - 1) / block_size.
+ * A length < 1 yields cnt = 0 and a row of -1. */
+int ssa_block_index_seq(const ssa_window* win, const int32_t* seq_lens, int32_t B, int32_t* idx,
+                        int32_t* cnt, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ssa_prefill -- block-sparse causal attention of every query over the key
+ * blocks its row lists (SSA: the lists of ssa_block_index; the page-selected
+ * variant: the lists of ssa_page_select).  Within the listed blocks the
+ * result is the masked softmax of equation (2) of the ZigZag page, section
+ * 2.1.  bf16 inputs are multiplied on the matrix cores with fp32
+ * accumulation; the softmax runs in fp32.
+ * ------------------------------------------------------------------------- */
+int ssa_prefill(const ssa_attn_args* a, const ssa_block_lists* lists, void* stream);
+
+/* ssa_dense_causal -- the comparison layer: plain causal attention, key j <=
+ * query i (equation (1) of the ZigZag page with the causal rule of its
+ * section 2.2.1), same kernel family as ssa_prefill. */
+int ssa_dense_causal(const ssa_attn_args* a, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ssa_decode -- one decode step of SSA over a paged cache: the query at
+ * position n - 1 reads the window of its block (block 0 and the 7 most recent
+ * blocks, the last one holding (n - 1) mod 128 + 1 valid keys).  The window is
+ * split over its blocks and the per-block softmax partials are merged inside
+ * the kernel.  No workspace.
+ * ------------------------------------------------------------------------- */
+int ssa_decode(const ssa_decode_args* a, const ssa_window* win, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ssa_page_select -- block lists for the page-selected variant (LongCat
+ * sparse attention article, section 3: streaming-aware indexing keeps the
+ * sink and the local window; hierarchical indexing scores 128-token pages
+ * coarsely and keeps the top M).  For batch b, query head h and query block
+ * qb the list is the window of qb plus the top_m pages c in
+ * [n_global, qb - n_local] with the highest score
+ *      < sum of q over block qb , sum of k over page c >      (kv head of h)
+ * ranked in fp64 from exact fp64 block sums; equal scores prefer the lower
+ * page; with at most top_m candidates all are kept.  Output lists are
+ * ascending, padded with -1:
+ *   idx [B, Hq, nqb, W] with W = n_global + n_local + top_m,  cnt [B, Hq, nqb]
+ * (contiguous), ready for ssa_prefill with idx_sb = Hq*nqb*W, idx_sh = nqb*W,
+ * cnt_sb = Hq*nqb, cnt_sh = nqb.  Uses a.q, a.k, their strides, a.dtype
+ * (BF16), B, L, Hq, Hkv, Dqk (64 or 128).  0 <= top_m <= 32.  The workspace
+ * holds the fp64 block sums; its size comes from
+ * ssa_page_select_workspace_size and it needs 256-byte alignment.
+ * ------------------------------------------------------------------------- */
+size_t ssa_page_select_workspace_size(const ssa_attn_args* a, const ssa_window* win);
+int ssa_page_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_m, int32_t* idx,
+                    int32_t* cnt, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Text of the calling thread's last error ("" if none).  Valid until the
+ * thread's next failing call. */
+const char* ssa_last_error(void);
+
+/* SSA_VERSION of the library. */
+int ssa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSA_H_ */

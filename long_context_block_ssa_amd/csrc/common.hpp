@@ -1,0 +1,103 @@
+// Internal declarations shared by the C-ABI layer and the gfx950 kernels.
+// Nothing here is part of the public interface (include/ssa.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+namespace ssa {
+
+// Launch through hipLaunchKernel so that the launch's own status is returned
+// (hipGetLastError would also report errors left over by unrelated calls).
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+                         Args&&... args) {
+  std::tuple<KArgs...> held(std::forward<Args>(args)...);
+  return std::apply(
+      [&](auto&... a) {
+        void* ptrs[] = {static_cast<void*>(&a)...};
+        return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, shmem, stream);
+      },
+      held);
+}
+
+// ---------------------------------------------------------------------------
+// launch parameter blocks (plain structs passed by value to kernels)
+// ---------------------------------------------------------------------------
+
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t qs_b, qs_l, qs_h;
+  int64_t ks_b, ks_l, ks_h;
+  int64_t vs_b, vs_l, vs_h;
+  int64_t os_b, os_l, os_h;
+  int32_t B, L, Hq, Hkv, group;  // group = Hq / Hkv
+  int32_t nqb;                   // ceil(L / 128)
+  float c1;                      // scale * log2(e): exp(scale*s) == exp2(c1*s)
+  float scale;
+  // block lists; dense != 0 means "every block 0 .. qb" and the list is unused
+  const int32_t* idx;
+  const int32_t* cnt;
+  int32_t W;
+  int32_t dense;
+  int64_t idx_sb, idx_sh, cnt_sb, cnt_sh;
+};
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int64_t qs_b, qs_h;
+  int64_t ks_p, ks_h, ks_s;
+  int64_t vs_p, vs_h, vs_s;
+  int64_t os_b, os_h;
+  int64_t bt_stride;
+  int32_t B, Hq, Hkv, group;
+  int32_t num_pages, max_blocks;
+  int32_t n_global, n_local;
+  float c1;
+  float scale;
+};
+
+struct PageSelectParams {
+  const void* q;
+  const void* k;
+  int64_t qs_b, qs_l, qs_h;
+  int64_t ks_b, ks_l, ks_h;
+  int32_t B, L, Hq, Hkv, group, D;
+  int32_t nqb;
+  int32_t n_global, n_local, top_m, W;
+  double* qsum;  // [B, Hq, nqb, D]
+  double* ksum;  // [B, Hkv, nqb, D]
+  int32_t* idx;  // [B, Hq, nqb, W]
+  int32_t* cnt;  // [B, Hq, nqb]
+};
+
+// ---------------------------------------------------------------------------
+// launchers (defined in the .hip files); each returns a hipError_t
+// ---------------------------------------------------------------------------
+
+hipError_t launch_block_index(int32_t block_size, int32_t n_global, int32_t n_local, int32_t rows,
+                              const int32_t* seq_lens, int32_t* idx, int32_t* cnt,
+                              hipStream_t stream);
+
+// dtype: 0 f32, 1 bf16; out_f32: output element type
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int dqk, int dv, bool out_f32,
+                          hipStream_t stream);
+
+hipError_t launch_decode(const DecodeParams& p, int dqk, int dv, hipStream_t stream);
+
+hipError_t launch_page_select(const PageSelectParams& p, hipStream_t stream);
+
+}  // namespace ssa

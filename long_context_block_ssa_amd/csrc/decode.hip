@@ -1,0 +1,218 @@
+// SSA decode over a paged KV cache, gfx950.
+//
+// A decode step reads, for the query at position n - 1, the window of its
+// block qb = (n - 1) / 128: block 0 and the blocks qb - 6 .. qb (QbitAI report
+// on LongCat LoZA, sparse-window paragraph); the last block holds
+// (n - 1) mod 128 + 1 valid keys.  Long-context decode is bound by reading the
+// cache (LongCat sparse attention article, section 1), and contiguous reads
+// coalesce (its section 3, mechanism 1), so the kernel is organised around
+// streaming whole 128-token pages with 16-byte loads:
+//
+//   - one workgroup per (sequence, kv head), one wave per window block;
+//   - a wave streams its page's K and V rows (each row = D/8 lanes x 16 B),
+//     computes the scores with a DPP row reduction, and keeps a partial
+//     softmax state (m, l, o[D]) -- an exact rewrite of the max-subtracted
+//     softmax of the CSA/HCA tutorial page, section 7.1;
+//   - the per-block partials are merged in LDS: M = max m_w,
+//     o = sum o_w e^(m_w - M) / sum l_w e^(m_w - M).
+#include "common.hpp"
+
+namespace ssa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the CPR lanes that hold one key row (CPR = 16: a DPP row; CPR = 8:
+// half a row).  Every lane of the group ends with the full sum.
+template <int CPR>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (CPR == 16) {
+    x += dpp<0x128>(x);  // row_ror:8
+    x += dpp<0x124>(x);  // row_ror:4
+  } else {
+    static_assert(CPR == 8, "8 or 16 lanes per key row");
+    x += dpp<0x141>(x);  // row_half_mirror
+  }
+  x += dpp<0x4E>(x);  // quad_perm [2,3,0,1]
+  x += dpp<0xB1>(x);  // quad_perm [1,0,3,2]
+  return x;
+}
+
+// Reduction over the key groups of a wave (lanes with equal lane % CPR).
+template <int CPR>
+__device__ __forceinline__ float across_keys_max(float x) {
+#pragma unroll
+  for (int s = CPR; s < 64; s <<= 1) x = fmaxf(x, __shfl_xor(x, s));
+  return x;
+}
+template <int CPR>
+__device__ __forceinline__ float across_keys_sum(float x) {
+#pragma unroll
+  for (int s = CPR; s < 64; s <<= 1) x += __shfl_xor(x, s);
+  return x;
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4 v, float* f) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    f[2 * w] = __builtin_bit_cast(float, v[w] << 16);
+    f[2 * w + 1] = __builtin_bit_cast(float, v[w] & 0xFFFF0000u);
+  }
+}
+
+constexpr int kMaxWaves = 16;
+
+template <int D>
+__global__ __launch_bounds__(1024) void decode_mha_kernel(DecodeParams p) {
+  constexpr int CPR = D / 8;      // lanes per key row (16 B each)
+  constexpr int KPI = 64 / CPR;   // keys per wave-wide load
+  constexpr int PASS = 64;        // keys per pass (2 passes per 128-key page)
+  constexpr int NI = PASS / KPI;  // loads per pass and operand
+  __shared__ float part[kMaxWaves][D + 2];
+  __shared__ int bad;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int kr = lane / CPR, cc = lane % CPR;
+  const int b = blockIdx.x / p.Hkv, hk = blockIdx.x % p.Hkv;
+  const int n = p.seq_lens[b];
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+
+  // window slot of this wave (same rule as the block-index builder)
+  int blk = -1;
+  const bool len_ok = n >= 1 && n <= p.max_blocks * 128;
+  if (len_ok) {
+    const int qb = (n - 1) / 128;
+    const int g_end = min(p.n_global, qb + 1);
+    const int l_begin = max(g_end, qb - p.n_local + 1);
+    const int cntw = g_end + (qb - l_begin + 1);
+    if (wave < cntw) blk = wave < g_end ? wave : l_begin + (wave - g_end);
+  } else if (threadIdx.x == 0) {
+    bad = 1;
+  }
+  int page = -1, valid = 0;
+  if (blk >= 0) {
+    page = p.block_table[b * p.bt_stride + blk];
+    if (page < 0 || page >= p.num_pages) {
+      if (lane == 0) bad = 1;
+      blk = -1;
+    } else {
+      valid = min(128, n - blk * 128);
+    }
+  }
+  __syncthreads();
+  const bool all_bad = bad != 0;
+
+  const __bf16* kp = static_cast<const __bf16*>(p.k) + static_cast<int64_t>(page) * p.ks_p + hk * p.ks_h + cc * 8;
+  const __bf16* vp = static_cast<const __bf16*>(p.v) + static_cast<int64_t>(page) * p.vs_p + hk * p.vs_h + cc * 8;
+
+  for (int hq = hk * p.group; hq < (hk + 1) * p.group; ++hq) {
+    float m = kNegInf, l = 0.f;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    if (!all_bad && blk >= 0) {
+      float qv[8];
+      bf16x8_to_f32(*reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.q) + b * p.qs_b + hq * p.qs_h + cc * 8),
+                    qv);
+#pragma unroll
+      for (int ps = 0; ps < 128 / PASS; ++ps) {
+        u32x4 kv[NI], vv[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int key = ps * PASS + i * KPI + kr;
+          kv[i] = u32x4{0, 0, 0, 0};
+          vv[i] = u32x4{0, 0, 0, 0};
+          if (key < valid) {
+            kv[i] = *reinterpret_cast<const u32x4*>(kp + key * p.ks_s);
+            vv[i] = *reinterpret_cast<const u32x4*>(vp + key * p.vs_s);
+          }
+        }
+        float s[NI];
+        float mx = kNegInf;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          float kf[8];
+          bf16x8_to_f32(kv[i], kf);
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) d = __builtin_fmaf(qv[e], kf[e], d);
+          d = group_sum<CPR>(d);
+          const int key = ps * PASS + i * KPI + kr;
+          s[i] = key < valid ? d : kNegInf;
+          mx = fmaxf(mx, s[i]);
+        }
+        mx = across_keys_max<CPR>(mx);
+        const float m_new = fmaxf(m, mx);
+        if (m_new == kNegInf) continue;  // whole pass past the valid keys
+        const float alpha = __builtin_amdgcn_exp2f((m - m_new) * p.c1);
+        const float mc = m_new * p.c1;
+        l *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= alpha;
+        float ps_sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c1, -mc));
+          ps_sum += pe;
+          float vf[8];
+          bf16x8_to_f32(vv[i], vf);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(pe, vf[e], o[e]);
+        }
+        // every lane of a key group holds the same pe: count each key once
+        l += across_keys_sum<CPR>(ps_sum);
+        m = m_new;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = across_keys_sum<CPR>(o[e]);
+    }
+    if (kr == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[wave][cc * 8 + e] = o[e];
+    }
+    if (lane == 0) {
+      part[wave][D] = m;
+      part[wave][D + 1] = l;
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+      float M = kNegInf;
+      for (int w = 0; w < nwaves; ++w) M = fmaxf(M, part[w][D]);
+      float acc = 0.f, lsum = 0.f;
+      for (int w = 0; w < nwaves; ++w) {
+        const float sc = part[w][D] == kNegInf ? 0.f : __builtin_amdgcn_exp2f((part[w][D] - M) * p.c1);
+        acc = __builtin_fmaf(part[w][d], sc, acc);
+        lsum = __builtin_fmaf(part[w][D + 1], sc, lsum);
+      }
+      const float nan = __builtin_nanf("");
+      const float out = all_bad ? nan : acc / lsum;
+      __bf16* op = static_cast<__bf16*>(p.o) + b * p.os_b + hq * p.os_h;
+      op[d] = static_cast<__bf16>(out);
+      if (d == 0 && p.lse)
+        p.lse[static_cast<int64_t>(b) * p.Hq + hq] = all_bad ? nan : M * p.scale + __builtin_amdgcn_logf(lsum) * kLn2;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, int dqk, int dv, hipStream_t stream) {
+  const int waves = p.n_global + p.n_local;  // validated <= 16
+  const dim3 grid(static_cast<unsigned>(p.B) * p.Hkv);
+  const dim3 block(64 * waves);
+  if (dqk == 128 && dv == 128) return launch_kernel(decode_mha_kernel<128>, grid, block, 0, stream, p);
+  if (dqk == 64 && dv == 64) return launch_kernel(decode_mha_kernel<64>, grid, block, 0, stream, p);
+  return hipErrorNotSupported;
+}
+
+}  // namespace ssa

@@ -238,7 +238,7 @@ def _exact_scores(qsum_exact, ksum_exact, cands):
     return [sum(a * b for a, b in zip(qsum_exact, ksum_exact[c])) for c in cands]
 
 
-def page_select(q, k, win: Window = DEFAULT_WINDOW, top_m: int = 8):
+def page_select(q, k, win: Window = DEFAULT_WINDOW, top_m: int = 8, heads=None):
     """Block lists for page-selected attention (LongCat sparse attention article,
     section 3: sink + sliding window kept, top-M pages by a coarse page score).
 
@@ -248,6 +248,8 @@ def page_select(q, k, win: Window = DEFAULT_WINDOW, top_m: int = 8):
     scores prefer the lower page.  When there are at most ``top_m`` candidates
     all are taken.  Lists are ascending and padded with -1 to
     W = n_global + n_local + top_m.
+
+    ``heads`` restricts the work to some query heads (other rows stay -1 / 0).
 
     Returns idx int32 [B, Hq, nqb, W], cnt int32 [B, Hq, nqb] and
     near bool [B, Hq, nqb]: rows whose float64 scores left the top-M boundary
@@ -267,22 +269,24 @@ def page_select(q, k, win: Window = DEFAULT_WINDOW, top_m: int = 8):
     cnt = np.zeros((B, Hq, nqb), np.int32)
     near = np.zeros((B, Hq, nqb), bool)
     for b in range(B):
-        for h in range(Hq):
+        for h in (range(Hq) if heads is None else heads):
             g = _kv_head(h, Hq, Hkv)
             for qb in range(nqb):
                 base = window_blocks(qb, win)
-                cands = list(range(win.n_global, qb - win.n_local + 1))
+                c0, c1 = win.n_global, qb - win.n_local + 1   # candidates c0 .. c1-1
+                cands = list(range(c0, c1))
                 if len(cands) <= top_m:
                     chosen = cands
                 else:
                     a = qs[b, qb, h]
-                    kc = ks[b, cands, g]
+                    kc = ks[b, c0:c1, g]
                     sc = kc @ a
                     err = 1e-9 * (np.abs(kc) @ np.abs(a))
-                    order = sorted(range(len(cands)), key=lambda n: (-sc[n], cands[n]))
+                    # descending score, then ascending page id
+                    order = np.lexsort((np.arange(c0, c1), -sc))
                     sm, sn = sc[order[top_m - 1]], sc[order[top_m]]
                     if sm - sn > 2.0 * err.max():
-                        chosen = [cands[n] for n in order[:top_m]]
+                        chosen = [c0 + int(n) for n in order[:top_m]]
                     else:
                         near[b, h, qb] = True
                         rq = q[b, qb * bs:min((qb + 1) * bs, L), h]

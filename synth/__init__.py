@@ -19,6 +19,8 @@ values widened to float64.
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 CHUNK = 128
@@ -61,13 +63,26 @@ def rows_chunk(seed: int, tensor_id: int, b: int, t: int, H: int, D: int,
 
 
 def seq_tensor(seed: int, tensor_id: int, B: int, L: int, H: int, D: int,
-               dtype: str = "bf16", mul: float = 1.0) -> np.ndarray:
-    """Whole logical [B, L, H, D] tensor (bf16 bits or float32), chunk by chunk."""
+               dtype: str = "bf16", mul: float = 1.0, workers: int = 8) -> np.ndarray:
+    """Whole logical [B, L, H, D] tensor (bf16 bits or float32), chunk by chunk.
+
+    Chunks are independent draws, so they are filled by a thread pool; the
+    result does not depend on ``workers``.
+    """
     nt = (L + CHUNK - 1) // CHUNK
     out = np.empty((B, nt * CHUNK, H, D), np.uint16 if dtype == "bf16" else np.float32)
-    for b in range(B):
-        for t in range(nt):
-            out[b, t * CHUNK:(t + 1) * CHUNK] = rows_chunk(seed, tensor_id, b, t, H, D, dtype, mul)
+
+    def fill(bt):
+        b, t = bt
+        out[b, t * CHUNK:(t + 1) * CHUNK] = rows_chunk(seed, tensor_id, b, t, H, D, dtype, mul)
+
+    jobs = [(b, t) for b in range(B) for t in range(nt)]
+    if workers > 1 and len(jobs) > 8:
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fill, jobs))
+    else:
+        for j in jobs:
+            fill(j)
     return out[:, :L]
 
 

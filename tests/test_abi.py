@@ -1,0 +1,197 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects invalid
+arguments on the host before any HIP call (so these run without a GPU).
+
+No test here makes a call that would pass validation: the device pointers used
+are fake, so a valid call would launch a kernel on them.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_block_ssa_amd as ssa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssa.LIB_PATH):
+        from long_context_block_ssa_amd import _build
+        _build.build(verbose=False)
+    return ssa.load()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "ssa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    assert set(names) == set(ssa.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version(lib):
+    assert lib.ssa_version() == 10000
+
+
+def good_args(**over):
+    a = ssa.CAttnArgs()
+    a.dtype = a.out_dtype = ssa.DTYPE_BF16
+    a.B, a.L, a.Hq, a.Hkv, a.Dqk, a.Dv = 1, 256, 2, 2, 128, 128
+    a.scale = 0.088
+    a.q = a.k = a.v = FAKE
+    a.o = FAKE + 4096
+    a.lse = None
+    for s in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        setattr(a, s, (ctypes.c_int64 * 3)(256 * 2 * 128, 2 * 128, 128))
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a
+
+
+def lists(**over):
+    li = ssa.CBlockLists()
+    li.idx, li.cnt, li.W, li.n_qblocks = FAKE, FAKE, 8, 2
+    for key, val in over.items():
+        setattr(li, key, val)
+    return li
+
+
+@pytest.mark.parametrize("over,code,needle", [
+    (dict(q=None), ssa.SSA_ERR_INVALID, "non-NULL"),
+    (dict(o=FAKE + 2), ssa.SSA_ERR_INVALID, "aligned"),
+    (dict(B=0), ssa.SSA_ERR_INVALID, "sizes"),
+    (dict(L=-5), ssa.SSA_ERR_INVALID, "sizes"),
+    (dict(Hq=3), ssa.SSA_ERR_INVALID, "multiple"),
+    (dict(scale=0.0), ssa.SSA_ERR_INVALID, "scale"),
+    (dict(scale=float("nan")), ssa.SSA_ERR_INVALID, "scale"),
+    (dict(dtype=7), ssa.SSA_ERR_INVALID, "dtype"),
+    (dict(Dqk=96, Dv=96), ssa.SSA_ERR_UNSUPPORTED, "no kernel"),
+    (dict(dtype=ssa.DTYPE_F32, out_dtype=ssa.DTYPE_BF16, Dqk=64, Dv=64), ssa.SSA_ERR_UNSUPPORTED, "no kernel"),
+    (dict(q_stride=(ctypes.c_int64 * 3)(1000, 3, 128)), ssa.SSA_ERR_INVALID, "stride"),
+    (dict(k_stride=(ctypes.c_int64 * 3)(-256, 256, 128)), ssa.SSA_ERR_INVALID, "stride"),
+])
+def test_prefill_and_dense_reject(lib, over, code, needle):
+    a = good_args(**over)
+    li = lists()
+    assert lib.ssa_prefill(ctypes.byref(a), ctypes.byref(li), None) == code
+    assert needle in lib.ssa_last_error().decode()
+    assert lib.ssa_dense_causal(ctypes.byref(a), None) == code
+
+
+@pytest.mark.parametrize("over,needle", [
+    (dict(idx=None), "non-NULL"),
+    (dict(W=0), "W="),
+    (dict(W=65), "W="),
+    (dict(n_qblocks=1), "rows per head"),
+    (dict(idx_sh=-1), "strides"),
+])
+def test_prefill_rejects_bad_lists(lib, over, needle):
+    a = good_args()
+    li = lists(**over)
+    assert lib.ssa_prefill(ctypes.byref(a), ctypes.byref(li), None) == ssa.SSA_ERR_INVALID
+    assert needle in lib.ssa_last_error().decode()
+    assert lib.ssa_prefill(ctypes.byref(a), None, None) == ssa.SSA_ERR_INVALID
+
+
+def test_block_index_rejects(lib):
+    w = ssa.CWindow(128, 1, 7)
+    assert lib.ssa_block_index(None, 4, FAKE, FAKE, None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_block_index(ctypes.byref(w), 0, FAKE, FAKE, None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_block_index(ctypes.byref(w), 4, None, FAKE, None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_block_index(ctypes.byref(w), 4, FAKE + 2, FAKE, None) == ssa.SSA_ERR_INVALID
+    bad = ssa.CWindow(128, 1, 0)
+    assert lib.ssa_block_index(ctypes.byref(bad), 4, FAKE, FAKE, None) == ssa.SSA_ERR_INVALID
+    wide = ssa.CWindow(128, 30, 40)
+    assert lib.ssa_block_index(ctypes.byref(wide), 4, FAKE, FAKE, None) == ssa.SSA_ERR_INVALID
+    assert "width" in lib.ssa_last_error().decode()
+    assert lib.ssa_block_index_seq(ctypes.byref(w), None, 4, FAKE, FAKE, None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_block_index_seq(ctypes.byref(w), FAKE, 0, FAKE, FAKE, None) == ssa.SSA_ERR_INVALID
+
+
+def decode_args(**over):
+    a = ssa.CDecodeArgs()
+    a.dtype = ssa.DTYPE_BF16
+    a.B, a.Hq, a.Hkv, a.Dqk, a.Dv = 2, 4, 4, 128, 128
+    a.page_size, a.num_pages, a.max_blocks = 128, 10, 5
+    a.scale = 0.088
+    a.q = a.k_pages = a.v_pages = a.o = FAKE
+    a.block_table = a.seq_lens = FAKE
+    a.q_stride = (ctypes.c_int64 * 2)(512, 128)
+    a.k_stride = (ctypes.c_int64 * 3)(4 * 128 * 128, 128 * 128, 128)
+    a.v_stride = (ctypes.c_int64 * 3)(4 * 128 * 128, 128 * 128, 128)
+    a.o_stride = (ctypes.c_int64 * 2)(512, 128)
+    a.bt_stride = 5
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(block_table=None), ssa.SSA_ERR_INVALID),
+    (dict(seq_lens=None), ssa.SSA_ERR_INVALID),
+    (dict(page_size=64), ssa.SSA_ERR_INVALID),
+    (dict(Hq=6), ssa.SSA_ERR_INVALID),
+    (dict(num_pages=0), ssa.SSA_ERR_INVALID),
+    (dict(bt_stride=4), ssa.SSA_ERR_INVALID),
+    (dict(scale=-1.0), ssa.SSA_ERR_INVALID),
+    (dict(dtype=ssa.DTYPE_F32), ssa.SSA_ERR_UNSUPPORTED),
+    (dict(Dqk=576, Dv=512, Hkv=2), ssa.SSA_ERR_UNSUPPORTED),
+    (dict(Hq=64, Hkv=2), ssa.SSA_ERR_UNSUPPORTED),
+    (dict(k_stride=(ctypes.c_int64 * 3)(4 * 128 * 128, 128 * 128, 100)), ssa.SSA_ERR_INVALID),
+])
+def test_decode_rejects(lib, over, code):
+    a = decode_args(**over)
+    w = ssa.CWindow(128, 1, 7)
+    assert lib.ssa_decode(ctypes.byref(a), ctypes.byref(w), None) == code
+    assert lib.ssa_last_error().decode() != ""
+
+
+def test_decode_rejects_window(lib):
+    a = decode_args()
+    assert lib.ssa_decode(ctypes.byref(a), None, None) == ssa.SSA_ERR_INVALID
+    w = ssa.CWindow(128, 9, 9)  # 18 waves > 16
+    assert lib.ssa_decode(ctypes.byref(a), ctypes.byref(w), None) == ssa.SSA_ERR_INVALID
+
+
+def test_page_select_rejects(lib):
+    a = good_args()
+    w = ssa.CWindow(128, 1, 7)
+    need = lib.ssa_page_select_workspace_size(ctypes.byref(a), ctypes.byref(w))
+    nqb = 2
+    assert need == (8 * 1 * 2 * nqb * 128 + 255) // 256 * 256 * 2
+    assert lib.ssa_page_select(ctypes.byref(a), ctypes.byref(w), 8, FAKE, FAKE, FAKE, need - 1, None) \
+        == ssa.SSA_ERR_WORKSPACE
+    assert lib.ssa_page_select(ctypes.byref(a), ctypes.byref(w), 8, FAKE, FAKE, None, need, None) \
+        == ssa.SSA_ERR_WORKSPACE
+    assert lib.ssa_page_select(ctypes.byref(a), ctypes.byref(w), 33, FAKE, FAKE, FAKE, need, None) \
+        == ssa.SSA_ERR_INVALID
+    assert lib.ssa_page_select(ctypes.byref(a), ctypes.byref(w), 8, FAKE, FAKE, FAKE + 16, need, None) \
+        == ssa.SSA_ERR_INVALID  # workspace alignment
+    a2 = good_args(Dqk=576, Dv=512)
+    assert lib.ssa_page_select(ctypes.byref(a2), ctypes.byref(w), 8, FAKE, FAKE, FAKE, 1 << 30, None) \
+        == ssa.SSA_ERR_UNSUPPORTED
+
+
+def test_error_is_thread_local(lib):
+    import threading
+    a = good_args(B=0)
+    li = lists()
+    assert lib.ssa_prefill(ctypes.byref(a), ctypes.byref(li), None) == ssa.SSA_ERR_INVALID
+    seen = {}
+
+    def other():
+        seen["msg"] = lib.ssa_last_error().decode()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "sizes" in lib.ssa_last_error().decode()

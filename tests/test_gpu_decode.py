@@ -1,0 +1,163 @@
+"""GPU parity: SSA decode over a paged cache against the float64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import bits_to_dev, check_close, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def build_case(seed, B, Hq, Hkv, D, seq_lens, head=1, tail=7, mul=1.0, Dv=None, share_kv=False):
+    """Paged cache with finite values only in the first `head` and last `tail`
+    logical blocks of every sequence, and only in slots < n; NaN elsewhere.
+
+    Returns device tensors and a compact host copy (only the filled pages) for
+    the oracle.
+    """
+    Dv = D if Dv is None else Dv
+    seq_lens = np.asarray(seq_lens, np.int32)
+    bt, P = synth.decode_block_table(seed, seq_lens, 128)
+    fill = synth.decode_fill_blocks(seq_lens, 128, head, tail)
+    kp = torch.full((P, Hkv, 128, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vp = kp if share_kv else torch.full((P, Hkv, 128, Dv), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ids, kh, vh = [], [], []
+    for b, blocks in enumerate(fill):
+        n = int(seq_lens[b])
+        for t in blocks:
+            kb = synth.page_chunk(seed, synth.K, b, t, Hkv, D, "bf16", mul)
+            vb = kb[..., :Dv] if share_kv else synth.page_chunk(seed, synth.V, b, t, Hkv, Dv, "bf16", mul)
+            valid = min(128, n - t * 128)
+            kb = kb.copy()
+            vb = vb.copy()
+            kb[:, valid:] = 0x7FC0  # bf16 NaN past the sequence end
+            vb[:, valid:] = 0x7FC0
+            ids.append(int(bt[b, t]))
+            kh.append(kb)
+            vh.append(vb)
+    idx = torch.tensor(ids, dtype=torch.long, device="cuda")
+    kp[idx] = bits_to_dev(np.stack(kh)[:, None]).reshape(len(ids), Hkv, 128, D)
+    if not share_kv:
+        vp[idx] = bits_to_dev(np.stack(vh)[:, None]).reshape(len(ids), Hkv, 128, Dv)
+    # compact host pool for the oracle: remap physical ids to 0..len(ids)-1
+    remap = {p: i for i, p in enumerate(ids)}
+    bt_c = np.full_like(bt, -1)
+    for b in range(len(seq_lens)):
+        for t in range(bt.shape[1]):
+            if bt[b, t] in remap:
+                bt_c[b, t] = remap[bt[b, t]]
+    k_host = synth.bf16_bits_to_f32(np.stack(kh))
+    v_host = synth.bf16_bits_to_f32(np.stack(vh))
+    q_bits = synth.decode_query(seed, len(seq_lens), Hq, D, "bf16", mul)
+    q = bits_to_dev(q_bits[None]).reshape(len(seq_lens), Hq, D)
+    dev = dict(q=q, k=kp, v=vp, bt=torch.from_numpy(bt).cuda(), sl=torch.from_numpy(seq_lens).cuda())
+    host = dict(q=synth.bf16_bits_to_f32(q_bits), k=k_host, v=v_host, bt=bt_c, sl=seq_lens)
+    return dev, host
+
+
+def run_and_check(lib, dev, host, scale, name, rel=False, v_view=None):
+    say(f"ssa_decode {name}")
+    v = dev["v"] if v_view is None else v_view
+    o, lse = lib.decode(dev["q"], dev["k"], v, dev["bt"], dev["sl"], scale=scale, with_lse=True)
+    torch.cuda.synchronize()
+    vh = host["v"] if v_view is None else host["k"][..., :v.shape[3]]
+    ro, rl = oracle.decode(host["q"], host["k"], vh, host["bt"], host["sl"], scale)
+    check_close(to_f64(o), ro, f"{name} o", rel=rel)
+    check_close(to_f64(lse), rl, f"{name} lse")
+    return o
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 4, 2), (128, 2, 2), (64, 3, 1), (128, 16, 1)])
+def test_decode_small_nan_poisoned(lib, D, Hq, Hkv):
+    lens = [1, 2, 127, 128, 129, 1000, 1024, 1025, 5000, 7777]
+    dev, host = build_case(21, len(lens), Hq, Hkv, D, lens)
+    run_and_check(lib, dev, host, 1 / math.sqrt(D), f"small D={D} Hq={Hq} Hkv={Hkv}")
+
+
+def test_decode_cfg3_full(lib):
+    """Batch 64, 16/16 heads, d = 128, lengths uniform in [65536, 131072]."""
+    lens = synth.decode_seq_lens(3, 64, 65536, 131072)
+    dev, host = build_case(3, 64, 16, 16, 128, lens)
+    run_and_check(lib, dev, host, 1 / math.sqrt(128), "cfg3 full")
+
+
+def test_decode_equals_prefill_last_row(lib):
+    """The decode of a sequence of length n equals row n - 1 of the prefill."""
+    D, H = 128, 2
+    for n in [1, 300, 1024, 1153, 4000]:
+        qh = synth.seq_tensor(31, synth.Q, 1, n, H, D)
+        kh = synth.seq_tensor(31, synth.K, 1, n, H, D)
+        vh = synth.seq_tensor(31, synth.V, 1, n, H, D)
+        q, k, v = bits_to_dev(qh), bits_to_dev(kh), bits_to_dev(vh)
+        say(f"decode==prefill n={n}")
+        o_p, l_p = lib.ssa(q, k, v, with_lse=True)
+        nb = (n + 127) // 128
+        perm = np.random.default_rng(n).permutation(nb + 3)[:nb].astype(np.int32)
+        kp = torch.full((nb + 3, H, 128, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        vp = torch.full((nb + 3, H, 128, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        for t in range(nb):
+            r = slice(t * 128, min((t + 1) * 128, n))
+            cnt = r.stop - r.start
+            kp[int(perm[t]), :, :cnt] = k[0, r].transpose(0, 1)
+            vp[int(perm[t]), :, :cnt] = v[0, r].transpose(0, 1)
+        bt = torch.from_numpy(perm[None]).cuda()
+        sl = torch.tensor([n], dtype=torch.int32, device="cuda")
+        o_d, l_d = lib.decode(q[:, n - 1], kp, vp, bt, sl, with_lse=True)
+        torch.cuda.synchronize()
+        ro, rl = oracle.ssa_rows(synth.bf16_bits_to_f32(qh[0, n - 1:n]).astype(np.float64), n - 1,
+                                 synth.bf16_bits_to_f32(kh[0]), synth.bf16_bits_to_f32(vh[0]),
+                                 1 / math.sqrt(D), [0, 1], H)
+        check_close(to_f64(o_d), ro, f"decode n={n}")
+        check_close(to_f64(o_p[0, n - 1:n]), ro, f"prefill row n-1 n={n}")
+        assert (o_d.float() - o_p[0, n - 1].float()).abs().max().item() <= 1e-2
+        assert (l_d - l_p[0, :, n - 1]).abs().max().item() <= 1e-3
+
+
+def test_decode_invalid_rows_are_nan(lib):
+    """Lengths outside [1, max_blocks*128] and page ids outside [0, num_pages)
+    give NaN rows; the other rows are unaffected."""
+    lens = [500, 1300, 900, 700]
+    dev, host = build_case(41, 4, 2, 2, 128, lens)
+    sl = dev["sl"].clone()
+    bt = dev["bt"].clone()
+    sl[1] = 0
+    bt[2, (900 - 1) // 128] = 10 ** 6   # own block of sequence 2 points outside the pool
+    sl[3] = bt.shape[1] * 128 + 1
+    say("decode invalid rows")
+    o, lse = lib.decode(dev["q"], dev["k"], dev["v"], bt, sl, with_lse=True)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    assert np.isnan(o[1:]).all() and np.isnan(lse.cpu().numpy()[1:]).all()
+    ro, _ = oracle.decode(host["q"], host["k"], host["v"], host["bt"], host["sl"], 1 / math.sqrt(128), batches=[0])
+    check_close(o[0:1], ro[0:1], "valid row beside invalid ones")
+
+
+def test_decode_structural_onehot(lib):
+    """q = 0 and V = one-hot(logical block id): o = (#keys in block)/(#keys)."""
+    D, H = 128, 1
+    lens = np.array([1, 129, 1024, 1025, 3000, 70000], np.int32)
+    bt, P = synth.decode_block_table(5, lens, 128)
+    kp = torch.zeros((P, H, 128, D), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros((P, H, 128, D), dtype=torch.bfloat16, device="cuda")
+    for b, n in enumerate(lens):
+        for t in range((int(n) + 127) // 128):
+            vp[int(bt[b, t]), :, :, t % D] = 1.0
+    q = torch.zeros((len(lens), H, D), dtype=torch.bfloat16, device="cuda")
+    say("decode structural")
+    o, lse = lib.decode(q, kp, vp, torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda(), with_lse=True)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    for b, n in enumerate(lens):
+        i = int(n) - 1
+        qb = i // 128
+        nk = i + 1 if i < 1024 else 897 + (i % 128)
+        assert abs(float(lse[b, 0]) - math.log(nk)) < 1e-5
+        want = np.zeros(D)
+        for t in range(qb + 1):
+            c = (i % 128 + 1) if t == qb else (128 if (t == 0 or t >= qb - 6) else 0)
+            want[t % D] += c / nk
+        assert np.abs(o[b, 0] - want).max() <= 2 ** -8, b
