@@ -109,7 +109,7 @@ typedef struct ssa_block_lists {
  *   k_pages [num_pages, Hkv, page_size, Dqk], v_pages [num_pages, Hkv, page_size, Dv]
  *     (strides for (page, head, slot); channels contiguous; v may alias k)
  *   block_table [B, max_blocks] int32: logical block t of sequence b lives in
- *     page block_table[b*bt_stride + t]
+ *     page block_table[b*bt_stride + t]  (bt_stride >= max_blocks when B > 1)
  *   seq_lens [B] int32: context length INCLUDING the new token, whose key and
  *     value are already in the cache; the query sits at position n - 1.
  * A sequence whose length is outside [1, max_blocks*page_size], or whose

@@ -229,7 +229,7 @@ int ssa_decode(const ssa_decode_args* a, const ssa_window* win, void* stream) {
       if (ss[t][i] < 0 || (ss[t][i] * 2) % 16 != 0)
         return fail(SSA_ERR_INVALID, "%s: stride %lld of operand %d must be >= 0 and a multiple of 16 bytes", who,
                     static_cast<long long>(ss[t][i]), t);
-  if (a->bt_stride < a->max_blocks)
+  if (a->B > 1 && a->bt_stride < a->max_blocks)
     return fail(SSA_ERR_INVALID, "%s: bt_stride=%lld < max_blocks=%d", who, static_cast<long long>(a->bt_stride),
                 a->max_blocks);
   const bool mha = (a->Dqk == 64 && a->Dv == 64) || (a->Dqk == 128 && a->Dv == 128);
