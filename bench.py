@@ -175,6 +175,8 @@ def main():
     ap.add_argument("--rotations", type=int, default=2, help="independent decode page sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=25.0)
+    ap.add_argument("--only", default="", help="comma list of rows to run (prefill,decode,dense,page); "
+                    "for profiling one kernel -- the JSON line is printed only for a full run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -245,6 +247,9 @@ def main():
             "a8 page_prefill"]
     nev = len(rows) + 1
 
+    only = set(x for x in args.only.split(",") if x)
+    run = {name: (not only) or (name in only) for name in ("prefill", "decode", "dense", "page")}
+
     def step(s, ev=None):
         def mark(i):
             if ev is not None:
@@ -252,16 +257,21 @@ def main():
         mark(0)
         idx2, cnt2 = ssa.block_index(nqb2, device=dev)
         mark(1)
-        ssa.prefill(q2, k2, v2, ssa.lists_from_index(idx2, cnt2), out=o2)
+        if run["prefill"]:
+            ssa.prefill(q2, k2, v2, ssa.lists_from_index(idx2, cnt2), out=o2)
         mark(2)
         r = s % args.rotations
-        ssa.decode(q3[r], kp, vp, bts[r], sl3, out=o3)
+        if run["decode"]:
+            ssa.decode(q3[r], kp, vp, bts[r], sl3, out=o3)
         mark(3)
-        ssa.dense_causal(q2, k2, v2, out=od)
+        if run["dense"]:
+            ssa.dense_causal(q2, k2, v2, out=od)
         mark(4)
-        i5, c5 = ssa.page_select(q5, k5, top_m=M5, workspace=ws5)
+        if run["page"]:
+            i5, c5 = ssa.page_select(q5, k5, top_m=M5, workspace=ws5)
         mark(5)
-        ssa.prefill(q5, k5, v5, ssa.lists_per_head(i5, c5), out=o5)
+        if run["page"]:
+            ssa.prefill(q5, k5, v5, ssa.lists_per_head(i5, c5), out=o5)
         mark(6)
 
     print("[bench] warmup", flush=True)
@@ -281,6 +291,8 @@ def main():
     for name, ms in zip(rows, per_row):
         print(f"[bench] {name:22s} {ms * 1e3:10.1f} us", flush=True)
 
+    if only:
+        return
     for t, name in ((o2, "ssa"), (o3, "decode"), (od, "dense"), (o5, "page")):
         if not torch.isfinite(t.float()).all():
             raise RuntimeError(f"non-finite {name} output")
