@@ -69,13 +69,26 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4 v, float* f) {
 }
 
 constexpr int kMaxWaves = 16;
+constexpr int kSub = 32;  // keys per sub-pass
 
+__device__ __forceinline__ float dot8_bf16(const float* q, const u32x4 k) {
+  float kf[8];
+  bf16x8_to_f32(k, kf);
+  float d = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) d = __builtin_fmaf(q[e], kf[e], d);
+  return d;
+}
+
+// One workgroup per (sequence, kv head).  The window's blocks are split over
+// the waves: `split` waves per block (128 / split keys each), streamed in
+// sub-passes of 32 keys -- 16-byte loads, D/8 lanes per key row, so a wave
+// reads 4 (D = 128) or 8 (D = 64) whole rows per instruction.
 template <int D>
-__global__ __launch_bounds__(1024) void decode_mha_kernel(DecodeParams p) {
-  constexpr int CPR = D / 8;      // lanes per key row (16 B each)
-  constexpr int KPI = 64 / CPR;   // keys per wave-wide load
-  constexpr int PASS = 64;        // keys per pass (2 passes per 128-key page)
-  constexpr int NI = PASS / KPI;  // loads per pass and operand
+__global__ __launch_bounds__(1024) void decode_mha_kernel(DecodeParams p, int split) {
+  constexpr int CPR = D / 8;     // lanes per key row (16 B each)
+  constexpr int KPI = 64 / CPR;  // keys per wave-wide load
+  constexpr int NI = kSub / KPI; // loads per sub-pass and operand
   __shared__ float part[kMaxWaves][D + 2];
   __shared__ int bad;
 
@@ -87,6 +100,8 @@ __global__ __launch_bounds__(1024) void decode_mha_kernel(DecodeParams p) {
   __syncthreads();
 
   // window slot of this wave (same rule as the block-index builder)
+  const int slot = wave / split, part_i = wave % split;
+  const int keys_per_wave = 128 / split;
   int blk = -1;
   const bool len_ok = n >= 1 && n <= p.max_blocks * 128;
   if (len_ok) {
@@ -94,18 +109,20 @@ __global__ __launch_bounds__(1024) void decode_mha_kernel(DecodeParams p) {
     const int g_end = min(p.n_global, qb + 1);
     const int l_begin = max(g_end, qb - p.n_local + 1);
     const int cntw = g_end + (qb - l_begin + 1);
-    if (wave < cntw) blk = wave < g_end ? wave : l_begin + (wave - g_end);
+    if (slot < cntw) blk = slot < g_end ? slot : l_begin + (slot - g_end);
   } else if (threadIdx.x == 0) {
     bad = 1;
   }
-  int page = -1, valid = 0;
+  int page = -1, k_lo = 0, k_hi = 0;  // this wave's keys [k_lo, k_hi) within the page
   if (blk >= 0) {
     page = p.block_table[b * p.bt_stride + blk];
     if (page < 0 || page >= p.num_pages) {
       if (lane == 0) bad = 1;
       blk = -1;
     } else {
-      valid = min(128, n - blk * 128);
+      const int valid = min(128, n - blk * 128);
+      k_lo = part_i * keys_per_wave;
+      k_hi = min(k_lo + keys_per_wave, valid);
     }
   }
   __syncthreads();
@@ -123,15 +140,14 @@ __global__ __launch_bounds__(1024) void decode_mha_kernel(DecodeParams p) {
       float qv[8];
       bf16x8_to_f32(*reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.q) + b * p.qs_b + hq * p.qs_h + cc * 8),
                     qv);
-#pragma unroll
-      for (int ps = 0; ps < 128 / PASS; ++ps) {
+      for (int k0 = k_lo; k0 < k_hi; k0 += kSub) {
         u32x4 kv[NI], vv[NI];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-          const int key = ps * PASS + i * KPI + kr;
+          const int key = k0 + i * KPI + kr;
           kv[i] = u32x4{0, 0, 0, 0};
           vv[i] = u32x4{0, 0, 0, 0};
-          if (key < valid) {
+          if (key < k_hi) {
             kv[i] = *reinterpret_cast<const u32x4*>(kp + key * p.ks_s);
             vv[i] = *reinterpret_cast<const u32x4*>(vp + key * p.vs_s);
           }
@@ -140,19 +156,12 @@ __global__ __launch_bounds__(1024) void decode_mha_kernel(DecodeParams p) {
         float mx = kNegInf;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-          float kf[8];
-          bf16x8_to_f32(kv[i], kf);
-          float d = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) d = __builtin_fmaf(qv[e], kf[e], d);
-          d = group_sum<CPR>(d);
-          const int key = ps * PASS + i * KPI + kr;
-          s[i] = key < valid ? d : kNegInf;
+          const float d = group_sum<CPR>(dot8_bf16(qv, kv[i]));
+          s[i] = (k0 + i * KPI + kr < k_hi) ? d : kNegInf;
           mx = fmaxf(mx, s[i]);
         }
         mx = across_keys_max<CPR>(mx);
         const float m_new = fmaxf(m, mx);
-        if (m_new == kNegInf) continue;  // whole pass past the valid keys
         const float alpha = __builtin_amdgcn_exp2f((m - m_new) * p.c1);
         const float mc = m_new * p.c1;
         l *= alpha;
@@ -207,11 +216,12 @@ __global__ __launch_bounds__(1024) void decode_mha_kernel(DecodeParams p) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, int dqk, int dv, hipStream_t stream) {
-  const int waves = p.n_global + p.n_local;  // validated <= 16
+  const int width = p.n_global + p.n_local;  // validated <= 16
+  const int split = width <= 8 ? 2 : 1;      // waves per window block
   const dim3 grid(static_cast<unsigned>(p.B) * p.Hkv);
-  const dim3 block(64 * waves);
-  if (dqk == 128 && dv == 128) return launch_kernel(decode_mha_kernel<128>, grid, block, 0, stream, p);
-  if (dqk == 64 && dv == 64) return launch_kernel(decode_mha_kernel<64>, grid, block, 0, stream, p);
+  const dim3 block(64 * width * split);
+  if (dqk == 128 && dv == 128) return launch_kernel(decode_mha_kernel<128>, grid, block, 0, stream, p, split);
+  if (dqk == 64 && dv == 64) return launch_kernel(decode_mha_kernel<64>, grid, block, 0, stream, p, split);
   return hipErrorNotSupported;
 }
 
