@@ -96,7 +96,13 @@ hipError_t launch_block_index(int32_t block_size, int32_t n_global, int32_t n_lo
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int dqk, int dv, bool out_f32,
                           hipStream_t stream);
 
+// Dqk = 576, Dv = 512 (latent-shared heads); called by launch_prefill
+hipError_t launch_prefill_wide(const PrefillParams& p, int dqk, int dv, bool out_f32, hipStream_t stream);
+
 hipError_t launch_decode(const DecodeParams& p, int dqk, int dv, hipStream_t stream);
+
+// Dqk = 576, Dv = 512 with one kv head; called by launch_decode
+hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t stream);
 
 hipError_t launch_page_select(const PageSelectParams& p, hipStream_t stream);
 

@@ -69,7 +69,16 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4 v, float* f) {
 }
 
 constexpr int kMaxWaves = 16;
-constexpr int kSub = 32;  // keys per sub-pass
+#ifndef SSA_DECODE_SUB
+#define SSA_DECODE_SUB 32
+#endif
+#ifndef SSA_DECODE_PIPE
+#define SSA_DECODE_PIPE 0
+#endif
+#ifndef SSA_DECODE_SPLIT8
+#define SSA_DECODE_SPLIT8 1
+#endif
+constexpr int kSub = SSA_DECODE_SUB;  // keys per sub-pass
 
 __device__ __forceinline__ float dot8_bf16(const float* q, const u32x4 k) {
   float kf[8];
@@ -140,17 +149,26 @@ __global__ __launch_bounds__(1024) void decode_mha_kernel(DecodeParams p, int sp
       float qv[8];
       bf16x8_to_f32(*reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.q) + b * p.qs_b + hq * p.qs_h + cc * 8),
                     qv);
-      for (int k0 = k_lo; k0 < k_hi; k0 += kSub) {
-        u32x4 kv[NI], vv[NI];
+      u32x4 kv[NI], vv[NI];
+      auto load_sub = [&](int k0, u32x4* kd, u32x4* vd) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
           const int key = k0 + i * KPI + kr;
-          kv[i] = u32x4{0, 0, 0, 0};
-          vv[i] = u32x4{0, 0, 0, 0};
+          kd[i] = u32x4{0, 0, 0, 0};
+          vd[i] = u32x4{0, 0, 0, 0};
           if (key < k_hi) {
-            kv[i] = *reinterpret_cast<const u32x4*>(kp + key * p.ks_s);
-            vv[i] = *reinterpret_cast<const u32x4*>(vp + key * p.vs_s);
+            kd[i] = *reinterpret_cast<const u32x4*>(kp + key * p.ks_s);
+            vd[i] = *reinterpret_cast<const u32x4*>(vp + key * p.vs_s);
           }
+        }
+      };
+      if (SSA_DECODE_PIPE) load_sub(k_lo, kv, vv);
+      for (int k0 = k_lo; k0 < k_hi; k0 += kSub) {
+        u32x4 kn[NI], vn[NI];
+        if (SSA_DECODE_PIPE) {
+          if (k0 + kSub < k_hi) load_sub(k0 + kSub, kn, vn);
+        } else {
+          load_sub(k0, kv, vv);
         }
         float s[NI];
         float mx = kNegInf;
@@ -180,6 +198,13 @@ __global__ __launch_bounds__(1024) void decode_mha_kernel(DecodeParams p, int sp
         // every lane of a key group holds the same pe: count each key once
         l += across_keys_sum<CPR>(ps_sum);
         m = m_new;
+        if (SSA_DECODE_PIPE) {
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            kv[i] = kn[i];
+            vv[i] = vn[i];
+          }
+        }
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = across_keys_sum<CPR>(o[e]);
@@ -216,8 +241,9 @@ __global__ __launch_bounds__(1024) void decode_mha_kernel(DecodeParams p, int sp
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, int dqk, int dv, hipStream_t stream) {
+  if (dqk == 576 && dv == 512) return launch_decode_mla(p, stream);
   const int width = p.n_global + p.n_local;  // validated <= 16
-  const int split = width <= 8 ? 2 : 1;      // waves per window block
+  const int split = width <= 8 ? SSA_DECODE_SPLIT8 : 1;  // waves per window block
   const dim3 grid(static_cast<unsigned>(p.B) * p.Hkv);
   const dim3 block(64 * width * split);
   if (dqk == 128 && dv == 128) return launch_kernel(decode_mha_kernel<128>, grid, block, 0, stream, p, split);

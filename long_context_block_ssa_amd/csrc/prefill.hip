@@ -625,6 +625,7 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, int dqk, int dv, bo
     if (dqk == 64 && dv == 64) return launch_kernel(prefill_f32_kernel<64>, grid, block, 0, stream, p);
     return hipErrorNotSupported;
   }
+  if (dqk == 576 && dv == 512) return launch_prefill_wide(p, dqk, dv, out_f32, stream);
   const dim3 pgrid(static_cast<unsigned>((p.nqb + 1) / 2) * p.B * p.Hq);
   const dim3 pblock(kPairThreads);
   if (dqk == 128 && dv == 128)

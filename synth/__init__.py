@@ -155,3 +155,24 @@ def decode_query(seed: int, B: int, H: int, D: int, dtype: str = "bf16", mul: fl
     if mul != 1.0:
         x = x * np.float32(mul)
     return f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def torch_normal_bf16(seed: int, shape, mul: float = 1.0, device="cuda"):
+    """Seeded N(0,1) * mul draws rounded to bf16, generated on the device by
+    torch's own (Philox) generator -- for tensors too large to draw on the host
+    (the 38 GB query of the 576-wide latent workload).  Checks copy the rows
+    they need back to the host, so both sides read identical values."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    flat = out.view(-1)
+    step = 1 << 28
+    for s0 in range(0, flat.numel(), step):
+        n = min(step, flat.numel() - s0)
+        x = torch.randn(n, generator=gen, device=device, dtype=torch.float32)
+        if mul != 1.0:
+            x.mul_(mul)
+        flat[s0:s0 + n].copy_(x)
+        del x
+    return out

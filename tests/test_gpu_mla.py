@@ -1,0 +1,93 @@
+"""GPU parity at the latent-shared (MLA-like) shape: 576-wide keys shared by
+all query heads, values = the first 512 channels.  Inputs are N(0,1)/24
+(1/sqrt(576)), so outputs are ~1e-3 and the absolute 1e-2 bound is weak; each
+check also requires max error / max |reference| <= 1e-2."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import bits_to_dev, check_close, say, to_f64
+from tests.test_gpu_decode import build_case, run_and_check
+
+pytestmark = pytest.mark.gpu
+
+DQK, DV = 576, 512
+MUL = 1.0 / 24.0
+SCALE = 1.0 / 24.0
+
+
+def mla_inputs(seed, B, L, Hq, shared=True):
+    qb = synth.seq_tensor(seed, synth.Q, B, L, Hq, DQK, "bf16", MUL)
+    cb = synth.seq_tensor(seed, synth.LATENT, B, L, 1, DQK, "bf16", MUL)
+    q, c = bits_to_dev(qb), bits_to_dev(cb)
+    qh, ch = synth.bf16_bits_to_f32(qb), synth.bf16_bits_to_f32(cb)
+    if shared:
+        return qh, ch, ch[..., :DV], q, c, c[..., :DV]
+    vb = synth.seq_tensor(seed, synth.V, B, L, 1, DV, "bf16", MUL)
+    return qh, ch, synth.bf16_bits_to_f32(vb), q, c, bits_to_dev(vb)
+
+
+@pytest.mark.parametrize("L,Hq,shared,out", [(1300, 16, True, None), (129, 16, True, torch.float32),
+                                             (1000, 32, False, None), (2304, 16, True, None)])
+def test_mla_prefill_small(lib, L, Hq, shared, out):
+    qh, kh, vh, q, k, v = mla_inputs(71, 1, L, Hq, shared)
+    say(f"mla prefill L={L} Hq={Hq} shared={shared}")
+    o, lse = lib.ssa(q, k, v, scale=SCALE, out_dtype=out, with_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.ssa_attention(qh.astype(np.float64), kh, vh, SCALE)
+    check_close(to_f64(o), ro, f"mla L={L} o", rel=True)
+    check_close(to_f64(lse), rl, f"mla L={L} lse")
+
+
+def test_mla_dense_small(lib):
+    qh, kh, vh, q, k, v = mla_inputs(72, 1, 700, 16)
+    say("mla dense")
+    o, _ = lib.dense_causal(q, k, v, scale=SCALE)
+    torch.cuda.synchronize()
+    ro, _ = oracle.dense_causal(qh.astype(np.float64), kh, vh, SCALE)
+    check_close(to_f64(o), ro, "mla dense o", rel=True)
+
+
+def test_mla_prefill_full_size_sampled(lib):
+    """B=1, L=262144, 128 heads x 576/512 (the launch the benchmark times);
+    query blocks 0-8, 2047 and 8 seeded random ones, all heads."""
+    B, L, H = 1, 262144, 128
+    say("mla full-size inputs")
+    q = synth.torch_normal_bf16(404, (B, L, H, DQK), MUL)
+    c = synth.torch_normal_bf16(405, (B, L, 1, DQK), MUL)
+    say("mla full-size prefill")
+    o, lse = lib.ssa(q, c, c[..., :DV], scale=SCALE, with_lse=True)
+    torch.cuda.synchronize()
+    ch = c[0].float().cpu().numpy()
+    rng = np.random.default_rng(4)
+    qbs = list(range(9)) + [2047] + sorted(rng.choice(np.arange(9, 2047), 8, replace=False).tolist())
+    for qb in qbs:
+        rows = slice(qb * 128, (qb + 1) * 128)
+        qr = q[0, rows].float().cpu().numpy().astype(np.float64)
+        ro, rl = oracle.ssa_rows(qr, qb * 128, ch, ch[..., :DV], SCALE, list(range(H)), H)
+        check_close(to_f64(o[0, rows]), ro, f"mla full qb={qb}", rel=True)
+        check_close(to_f64(lse[0, :, rows]).T, rl, f"mla full lse qb={qb}")
+    del q, o, c
+
+
+@pytest.mark.parametrize("lens,Hq", [([1, 5, 129, 1000, 3000], 32), ([1025, 70000], 16)])
+def test_mla_decode_small(lib, lens, Hq):
+    dev, host = build_case(81, len(lens), Hq, 1, DQK, lens, mul=MUL, Dv=DV, share_kv=True)
+    run_and_check(lib, dev, host, SCALE, f"mla decode {lens}", rel=True, v_view=dev["k"][..., :DV])
+
+
+def test_mla_decode_separate_v(lib):
+    lens = [300, 2000]
+    dev, host = build_case(82, len(lens), 16, 1, DQK, lens, mul=MUL, Dv=DV, share_kv=False)
+    run_and_check(lib, dev, host, SCALE, "mla decode separate v", rel=True)
+
+
+def test_mla_decode_full_size(lib):
+    """Batch 8 at context 1,048,576 (last block full), 128 heads."""
+    lens = [1048576] * 8
+    dev, host = build_case(4, 8, 128, 1, DQK, lens, mul=MUL, Dv=DV, share_kv=True)
+    run_and_check(lib, dev, host, SCALE, "mla decode 1M", rel=True, v_view=dev["k"][..., :DV])
