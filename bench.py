@@ -6,6 +6,8 @@ One step = one pass over every row of the path on resident synthetic inputs:
   a1  block index            (256 query blocks)
   a2  SSA prefill            B=1, H=16, d=128, L=32768, bf16, layout [B, H, L, D]
   a3  SSA decode             batch 64, H=16/16, d=128, context ~ U[65536, 131072]
+  a4  latent-shared shape    prefill B=1, L=262144, 128 heads x 576/512 (V = first 512
+                             channels of the shared latent); decode batch 8 at 1,048,576
   a5  dense causal layer     same tensors as a2 (the comparison layer)
   a6+a7 page selection       L=131072, H=16, d=128, M=8
   a8  page-selected prefill  over those lists
@@ -47,6 +49,7 @@ PEAK_HBM_GBS = 8000.0
 W2 = dict(B=1, L=32768, H=16, D=128, seed=2)
 W3 = dict(B=64, H=16, D=128, lo=65536, hi=131072, seed=3)
 W5 = dict(B=1, L=131072, H=16, D=128, M=8, seed=5)
+W4 = dict(L=262144, H=128, DQK=576, DV=512, seed=4, dec_B=8, dec_n=1048576, dec_rot=32)
 
 
 def keys_ssa(i: int) -> int:
@@ -66,6 +69,15 @@ def pairs(L: int, keys) -> int:
 
 def ssa_flops(L, H, D, B=1):
     return 4 * D * pairs(L, keys_ssa) * H * B
+
+
+def mla_flops(L, H, DQK, DV, B=1):
+    return 2 * (DQK + DV) * pairs(L, keys_ssa) * H * B
+
+
+def mla_decode_bytes(lens, Hq, DQK, DV):
+    # the latent row is read once and serves as key and value
+    return sum(keys_ssa(int(n) - 1) for n in lens) * DQK * 2 + len(lens) * Hq * (DQK + DV) * 2
 
 
 def dense_flops(L, H, D, B=1):
@@ -175,7 +187,7 @@ def main():
     ap.add_argument("--rotations", type=int, default=2, help="independent decode page sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=25.0)
-    ap.add_argument("--only", default="", help="comma list of rows to run (prefill,decode,dense,page); "
+    ap.add_argument("--only", default="", help="comma list of rows to run (prefill,decode,dense,page,mla); "
                     "for profiling one kernel -- the JSON line is printed only for a full run")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -241,14 +253,36 @@ def main():
     idx5 = torch.empty((1, H5, nqb5, 8 + M5), dtype=torch.int32, device=dev)
     cnt5 = torch.empty((1, H5, nqb5), dtype=torch.int32, device=dev)
     ws5 = torch.empty((ssa.page_select_workspace_size(q5, k5) + 256,), dtype=torch.uint8, device=dev)
+    # a4 inputs: values N(0,1)/24, drawn on the device (the query is 38.6 GB)
+    L4, H4, DQ4, DV4, s4 = W4["L"], W4["H"], W4["DQK"], W4["DV"], W4["seed"]
+    q4 = synth.torch_normal_bf16(1000 * s4 + 1, (1, L4, H4, DQ4), 1 / 24, device=dev)
+    c4 = synth.torch_normal_bf16(1000 * s4 + 2, (1, L4, 1, DQ4), 1 / 24, device=dev)
+    o4 = torch.empty((1, L4, H4, DV4), dtype=torch.bfloat16, device=dev)
+    B4d, n4d, R4 = W4["dec_B"], W4["dec_n"], W4["dec_rot"]
+    lens4 = np.full(B4d, n4d, np.int32)
+    nb4 = n4d // 128
+    # R4 tables over one pool; each table's window pages are distinct from the others'
+    P4 = B4d * nb4
+    pool4 = torch.full((P4, 1, 128, DQ4), float("nan"), dtype=torch.bfloat16, device=dev)
+    tables4 = []
+    for r in range(R4):
+        bt4, _ = synth.decode_block_table(s4, lens4, 128, rotation=r)
+        tables4.append(bt4)
+    win_ids = sorted({int(bt[b, t]) for bt in tables4 for b in range(B4d) for t in [0] + list(range(nb4 - 7, nb4))})
+    pool4[torch.tensor(win_ids, dtype=torch.long, device=dev)] = synth.torch_normal_bf16(
+        1000 * s4 + 3, (len(win_ids), 1, 128, DQ4), 1 / 24, device=dev)
+    q4d = [synth.torch_normal_bf16(1000 * s4 + 10 + r, (B4d, H4, DQ4), 1 / 24, device=dev) for r in range(R4)]
+    bts4 = [torch.from_numpy(bt).to(dev) for bt in tables4]
+    sl4 = torch.from_numpy(lens4).to(dev)
+    o4d = torch.empty((B4d, H4, DV4), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
     rows = ["a1 block_index", "a2 ssa_prefill", "a3 ssa_decode", "a5 dense_causal", "a6-a7 page_select",
-            "a8 page_prefill"]
+            "a8 page_prefill", "a4 mla_prefill", "a4 mla_decode"]
     nev = len(rows) + 1
 
     only = set(x for x in args.only.split(",") if x)
-    run = {name: (not only) or (name in only) for name in ("prefill", "decode", "dense", "page")}
+    run = {name: (not only) or (name in only) for name in ("prefill", "decode", "dense", "page", "mla")}
 
     def step(s, ev=None):
         def mark(i):
@@ -273,6 +307,14 @@ def main():
         if run["page"]:
             ssa.prefill(q5, k5, v5, ssa.lists_per_head(i5, c5), out=o5)
         mark(6)
+        if run["mla"]:
+            ssa.prefill(q4, c4, c4[..., :DV4], ssa.lists_from_index(*ssa.block_index(L4 // 128, device=dev)),
+                        scale=1 / 24, out=o4)
+        mark(7)
+        if run["mla"]:
+            r4 = s % R4
+            ssa.decode(q4d[r4], pool4, pool4[..., :DV4], bts4[r4], sl4, scale=1 / 24, out=o4d)
+        mark(8)
 
     print("[bench] warmup", flush=True)
     for s in range(args.warmup):
@@ -293,7 +335,8 @@ def main():
 
     if only:
         return
-    for t, name in ((o2, "ssa"), (o3, "decode"), (od, "dense"), (o5, "page")):
+    for t, name in ((o2, "ssa"), (o3, "decode"), (od, "dense"), (o5, "page"), (o4[0, -128:], "mla"),
+                    (o4d, "mla decode")):
         if not torch.isfinite(t.float()).all():
             raise RuntimeError(f"non-finite {name} output")
 
@@ -324,6 +367,14 @@ def main():
                          "us": per_row[5] * 1e3, "work": f5},
         "block_index": {"us": per_row[0] * 1e3},
     }
+    f4 = mla_flops(L4, H4, DQ4, DV4)
+    b4 = mla_decode_bytes(lens4, H4, DQ4, DV4)
+    kernels["mla_prefill"] = {"bound": "mfma", "achieved": f4 / (per_row[6] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                              "unit": "TFLOP/s", "frac": f4 / (per_row[6] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                              "us": per_row[6] * 1e3, "work": f4}
+    kernels["mla_decode"] = {"bound": "hbm", "achieved": b4 / (per_row[7] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": b4 / (per_row[7] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                             "us": per_row[7] * 1e3, "work": b4}
     out = {
         "metric": "SSA prefill TFLOP/s (frac MFMA peak) + decode GB/s (frac HBM) at 128K ctx",
         "value": tf2,
@@ -340,7 +391,8 @@ def main():
         "config": {
             "workload": "SSA prefill B=1 H=16 d=128 L=32768 bf16 (value) + SSA decode batch 64 H=16/16 d=128 "
                         "ctx U[65536,131072] bf16 (decode) + dense causal (same shape) + page selection "
-                        "L=131072 H=16 d=128 M=8",
+                        "L=131072 H=16 d=128 M=8 + latent-shared 576/512 x 128 heads: prefill L=262144, "
+                        "decode batch 8 at 1048576",
             "prefill_tokens_per_s": L2 / t2,
             "decode_gbps": gb3,
             "decode_frac_hbm": gb3 / PEAK_HBM_GBS,

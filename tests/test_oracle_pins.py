@@ -418,3 +418,24 @@ def test_generator_rounding_matches_torch():
     assert np.array_equal(bits, tb)
     back = synth.bf16_bits_to_f32(bits)
     assert np.array_equal(back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_window_facts_from_the_pages():
+    """The oracle's default window reproduces the page-stated geometry: blocks of
+    128 tokens, 1 global + 7 local, at most S = 1024 keys per query."""
+    import os
+    facts = {}
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "window_facts.txt")):
+        if line.strip() and not line.startswith("#"):
+            k, v = line.split()
+            facts[k] = int(v)
+    w = oracle.DEFAULT_WINDOW
+    assert (w.block_size, w.n_global, w.n_local) == (facts["block_size"], facts["n_global"], facts["n_local"])
+    L = 4096
+    q = np.zeros((1, L, 1, 2))
+    k = RNG.standard_normal((1, L, 1, 2))
+    v = np.ones((1, L, 1, 1))
+    _, lse = oracle.ssa_attention(q, k, v, 1.0)
+    nkeys = np.exp(lse[0, 0])
+    assert abs(nkeys.max() - facts["window_tokens"]) < 1e-6
+    assert abs(nkeys[facts["window_tokens"] - 1] - facts["window_tokens"]) < 1e-6
