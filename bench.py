@@ -162,21 +162,127 @@ def cpu_baseline(budget_s: float = 25.0):
 # GPU part
 # ----------------------------------------------------------------------------
 
-def traffic_for(kernel_file: str, key: str):
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
+KERNEL_SOURCES = {  # row key -> (kernel-name fragments in the trace, source file)
+    "ssa_prefill": (("prefill_wide_kernel", "128"), "prefill_wide.hip"),
+    "ssa_decode": (("decode_mha_kernel", "128"), "decode.hip"),
+    "mla_prefill": (("prefill_wide_kernel", "576"), "prefill_wide.hip"),
+    "mla_decode": (("decode_mla_kernel", "true"), "decode_mla.hip"),
+}
+
+
+def source_sha(fname: str) -> str:
+    src = os.path.join(ROOT, "long_context_block_ssa_amd", "csrc", fname)
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(key: str):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current source of the kernel; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    src = os.path.join(ROOT, "long_context_block_ssa_amd", "csrc", kernel_file)
     try:
-        with open(path) as f:
-            data = json.load(f)
-        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-        ent = data.get(key)
-        if ent and ent.get("source_sha") == h:
-            return ent["bytes_per_launch"]
-    except Exception:
+        for line in open(TRAFFIC_FILE):
+            f = line.split()
+            if len(f) >= 4 and f[0] == key and f[2] == source_sha(KERNEL_SOURCES[key][1]):
+                return float(f[1])
+    except OSError:
         pass
     return None
+
+
+def write_traffic(fetch_dir: str, write_dir: str, out_path: str):
+    """Per-launch HBM bytes from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE,
+    KiB per dispatch) of `bench.py --only prefill,decode,mla,copy`, each scaled
+    by what the same counter reads for the plain 1 GiB copy (which moves exactly
+    1 GiB each way)."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                vals.setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+                vals[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"]) * 1024.0
+        return vals  # kernel name -> {dispatch: bytes}
+
+    def pick(vals, frags):
+        per = [v for k, v in vals.items() if all(f in k for f in frags)]
+        if not per:
+            return None
+        d = per[0]
+        return sum(d.values()) / len(d)
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    copy_bytes = float(1 << 30)
+    # the calibration copy is the largest copy dispatch of the run
+    copy_f = [x for k, v in fetch.items() if "copy" in k.lower() for x in v.values()]
+    copy_w = [x for k, v in write.items() if "copy" in k.lower() for x in v.values()]
+    fcal = copy_bytes / max(copy_f) if copy_f and max(copy_f) > 0 else 1.0
+    wcal = copy_bytes / max(copy_w) if copy_w and max(copy_w) > 0 else 1.0
+    lines = [f"# HBM bytes per launch: FETCH_SIZE * {fcal:.4f} + WRITE_SIZE * {wcal:.4f} (per dispatch, averaged);",
+             "# factors = 1 GiB / the counter's reading on a plain 1 GiB device copy (bench.py --only copy).",
+             "# key bytes_per_launch source_sha fetch_bytes write_bytes"]
+    for key, (frags, fname) in KERNEL_SOURCES.items():
+        fb, wb = pick(fetch, frags), pick(write, frags)
+        if fb is not None and wb is not None:
+            fb, wb = fb * fcal, wb * wcal
+            lines.append(f"{key} {fb + wb:.0f} {source_sha(fname)} {fb:.0f} {wb:.0f}")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def short_kernel_name(name: str) -> str:
+    """'void ssa::(anonymous namespace)::k<128, 128, false, 2, __bf16>(ssa::P)' -> 'k<128, 128, false, 2, __bf16>'."""
+    n = name.replace("void ", "").replace("ssa::(anonymous namespace)::", "").replace("ssa::", "")
+    depth = 0
+    for i, ch in enumerate(n):  # cut at the argument list (the first '(' outside template brackets)
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return n[:i]
+    return n
+
+
+def write_trace_summary(stats_csv: str, out_path: str, command: str):
+    """Short text summary of a rocprofv3 --kernel-trace --stats run: this library's kernels,
+    one line per (kernel, workgroup count) -- the same kernel serves rows of different sizes -- with calls and
+    average / min / max duration, from the per-dispatch kernel_trace.csv beside kernel_stats.csv."""
+    import csv
+    import shutil
+    import subprocess
+
+    def demangle(n):
+        if n.startswith("_Z") and shutil.which("c++filt"):
+            # this c++filt predates the mangling of __bf16 (DF16b): spell it as float, then put it back
+            out = subprocess.run(["c++filt", n.replace("DF16b", "f")], capture_output=True, text=True).stdout.strip()
+            if out and not out.startswith("_Z"):
+                return out.replace(", float>", ", __bf16>") if "DF16b" in n else out
+        return n
+
+    trace_csv = stats_csv.replace("kernel_stats.csv", "kernel_trace.csv")
+    groups = {}
+    for r in csv.DictReader(open(trace_csv)):
+        n = demangle(r["Kernel_Name"])
+        if "ssa::" not in n:
+            continue
+        wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+        nwg = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) // max(wg, 1)
+        dt = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault((short_kernel_name(n), nwg, wg), []).append(dt)
+    rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
+    w = max([len(k[0]) for k, _ in rows] + [6])
+    lines = ["# rocprofv3 kernel-trace summary (this library's kernels; one line per kernel and grid; microseconds)",
+             f"# command: {command}",
+             f"{'kernel':{w}s} {'workgroups':>10s} {'wg_size':>7s} {'calls':>6s} {'avg_us':>11s} {'min_us':>11s} "
+             f"{'max_us':>11s}"]
+    lines += [f"{k:{w}s} {nwg:10d} {wg:7d} {len(v):6d} {sum(v) / len(v):11.1f} {min(v):11.1f} {max(v):11.1f}"
+              for (k, nwg, wg), v in rows]
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def main():
@@ -189,7 +295,17 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=25.0)
     ap.add_argument("--only", default="", help="comma list of rows to run (prefill,decode,dense,page,mla); "
                     "for profiling one kernel -- the JSON line is printed only for a full run")
+    ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
+                    help="summarise two rocprofv3 --pmc runs into a traffic file and exit")
+    ap.add_argument("--trace-summary", nargs=3, metavar=("KERNEL_STATS_CSV", "OUT", "COMMAND"),
+                    help="summarise a rocprofv3 --kernel-trace --stats run into a short text file and exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        write_trace_summary(*args.trace_summary)
+        return
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(every row of the path fits one MI355X; sharding is described in DESIGN.md)", file=sys.stderr)
@@ -212,77 +328,86 @@ def main():
             return t.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3)
         return t.to(dev)
 
+    only = set(x for x in args.only.split(",") if x)
+    run = {name: (not only) or (name in only) for name in ("prefill", "decode", "dense", "page", "mla")}
+    run["copy"] = "copy" in only  # calibration copy for the traffic counters, only on request
+
     print("[bench] generating inputs", flush=True)
     # a2 / a5 inputs
     L2, H2, D2, s2 = W2["L"], W2["H"], W2["D"], W2["seed"]
-    q2, k2, v2 = (up(synth.seq_tensor(s2, t, 1, L2, H2, D2)) for t in (synth.Q, synth.K, synth.V))
-    o2 = torch.empty((1, H2, L2, D2), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
-    od = torch.empty_like(o2)
     nqb2 = L2 // 128
+    if run["prefill"] or run["dense"]:
+        q2, k2, v2 = (up(synth.seq_tensor(s2, t, 1, L2, H2, D2)) for t in (synth.Q, synth.K, synth.V))
+        o2 = torch.empty((1, H2, L2, D2), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
+        od = torch.empty_like(o2)
     # a3 inputs: one paged pool, several independent (q, table) sets
     B3, H3, D3, s3 = W3["B"], W3["H"], W3["D"], W3["seed"]
     lens = synth.decode_seq_lens(s3, B3, W3["lo"], W3["hi"])
-    tables = []
-    P = None
-    for r in range(args.rotations):
-        bt, P = synth.decode_block_table(s3, lens, 128, rotation=r)
-        tables.append(bt)
-    kp = torch.full((P, H3, 128, D3), float("nan"), dtype=torch.bfloat16, device=dev)
-    vp = torch.full((P, H3, 128, D3), float("nan"), dtype=torch.bfloat16, device=dev)
-    fill = synth.decode_fill_blocks(lens, 128, 1, 7)
-    for r, bt in enumerate(tables):
-        ids, kh, vh = [], [], []
-        for b, blocks in enumerate(fill):
-            for t in blocks:
-                ids.append(int(bt[b, t]))
-                kh.append(synth.page_chunk(s3 + 100 * r, synth.K, b, t, H3, D3))
-                vh.append(synth.page_chunk(s3 + 100 * r, synth.V, b, t, H3, D3))
-        idx_t = torch.tensor(ids, dtype=torch.long, device=dev)
-        kp[idx_t] = up(np.stack(kh), head_major=False)
-        vp[idx_t] = up(np.stack(vh), head_major=False)
-    q3 = [up(synth.decode_query(s3, B3, H3, D3, rotation=r)[None], head_major=False)[0]
-          for r in range(args.rotations)]
-    bts = [torch.from_numpy(bt).to(dev) for bt in tables]
-    sl3 = torch.from_numpy(lens).to(dev)
-    o3 = torch.empty((B3, H3, D3), dtype=torch.bfloat16, device=dev)
+    if run["decode"]:
+        tables = []
+        P = None
+        for r in range(args.rotations):
+            bt, P = synth.decode_block_table(s3, lens, 128, rotation=r)
+            tables.append(bt)
+        kp = torch.full((P, H3, 128, D3), float("nan"), dtype=torch.bfloat16, device=dev)
+        vp = torch.full((P, H3, 128, D3), float("nan"), dtype=torch.bfloat16, device=dev)
+        fill = synth.decode_fill_blocks(lens, 128, 1, 7)
+        for r, bt in enumerate(tables):
+            ids, kh, vh = [], [], []
+            for b, blocks in enumerate(fill):
+                for t in blocks:
+                    ids.append(int(bt[b, t]))
+                    kh.append(synth.page_chunk(s3 + 100 * r, synth.K, b, t, H3, D3))
+                    vh.append(synth.page_chunk(s3 + 100 * r, synth.V, b, t, H3, D3))
+            idx_t = torch.tensor(ids, dtype=torch.long, device=dev)
+            kp[idx_t] = up(np.stack(kh), head_major=False)
+            vp[idx_t] = up(np.stack(vh), head_major=False)
+        q3 = [up(synth.decode_query(s3, B3, H3, D3, rotation=r)[None], head_major=False)[0]
+              for r in range(args.rotations)]
+        bts = [torch.from_numpy(bt).to(dev) for bt in tables]
+        sl3 = torch.from_numpy(lens).to(dev)
+        o3 = torch.empty((B3, H3, D3), dtype=torch.bfloat16, device=dev)
     # a6-a8 inputs
-    L5, H5, D5, M5, s5 = W5["L"], W5["H"], W5["D"], W5["M"], W5["seed"]
-    q5, k5, v5 = (up(synth.seq_tensor(s5, t, 1, L5, H5, D5)) for t in (synth.Q, synth.K, synth.V))
-    o5 = torch.empty((1, H5, L5, D5), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
-    nqb5 = L5 // 128
-    idx5 = torch.empty((1, H5, nqb5, 8 + M5), dtype=torch.int32, device=dev)
-    cnt5 = torch.empty((1, H5, nqb5), dtype=torch.int32, device=dev)
-    ws5 = torch.empty((ssa.page_select_workspace_size(q5, k5) + 256,), dtype=torch.uint8, device=dev)
+    if run["page"]:
+        L5, H5, D5, M5, s5 = W5["L"], W5["H"], W5["D"], W5["M"], W5["seed"]
+        q5, k5, v5 = (up(synth.seq_tensor(s5, t, 1, L5, H5, D5)) for t in (synth.Q, synth.K, synth.V))
+        o5 = torch.empty((1, H5, L5, D5), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
+        nqb5 = L5 // 128
+        idx5 = torch.empty((1, H5, nqb5, 8 + M5), dtype=torch.int32, device=dev)
+        cnt5 = torch.empty((1, H5, nqb5), dtype=torch.int32, device=dev)
+        ws5 = torch.empty((ssa.page_select_workspace_size(q5, k5) + 256,), dtype=torch.uint8, device=dev)
     # a4 inputs: values N(0,1)/24, drawn on the device (the query is 38.6 GB)
-    L4, H4, DQ4, DV4, s4 = W4["L"], W4["H"], W4["DQK"], W4["DV"], W4["seed"]
-    q4 = synth.torch_normal_bf16(1000 * s4 + 1, (1, L4, H4, DQ4), 1 / 24, device=dev)
-    c4 = synth.torch_normal_bf16(1000 * s4 + 2, (1, L4, 1, DQ4), 1 / 24, device=dev)
-    o4 = torch.empty((1, L4, H4, DV4), dtype=torch.bfloat16, device=dev)
-    B4d, n4d, R4 = W4["dec_B"], W4["dec_n"], W4["dec_rot"]
-    lens4 = np.full(B4d, n4d, np.int32)
-    nb4 = n4d // 128
-    # R4 tables over one pool; each table's window pages are distinct from the others'
-    P4 = B4d * nb4
-    pool4 = torch.full((P4, 1, 128, DQ4), float("nan"), dtype=torch.bfloat16, device=dev)
-    tables4 = []
-    for r in range(R4):
-        bt4, _ = synth.decode_block_table(s4, lens4, 128, rotation=r)
-        tables4.append(bt4)
-    win_ids = sorted({int(bt[b, t]) for bt in tables4 for b in range(B4d) for t in [0] + list(range(nb4 - 7, nb4))})
-    pool4[torch.tensor(win_ids, dtype=torch.long, device=dev)] = synth.torch_normal_bf16(
-        1000 * s4 + 3, (len(win_ids), 1, 128, DQ4), 1 / 24, device=dev)
-    q4d = [synth.torch_normal_bf16(1000 * s4 + 10 + r, (B4d, H4, DQ4), 1 / 24, device=dev) for r in range(R4)]
-    bts4 = [torch.from_numpy(bt).to(dev) for bt in tables4]
-    sl4 = torch.from_numpy(lens4).to(dev)
-    o4d = torch.empty((B4d, H4, DV4), dtype=torch.bfloat16, device=dev)
+    if run["mla"]:
+        L4, H4, DQ4, DV4, s4 = W4["L"], W4["H"], W4["DQK"], W4["DV"], W4["seed"]
+        q4 = synth.torch_normal_bf16(1000 * s4 + 1, (1, L4, H4, DQ4), 1 / 24, device=dev)
+        c4 = synth.torch_normal_bf16(1000 * s4 + 2, (1, L4, 1, DQ4), 1 / 24, device=dev)
+        o4 = torch.empty((1, L4, H4, DV4), dtype=torch.bfloat16, device=dev)
+        B4d, n4d, R4 = W4["dec_B"], W4["dec_n"], W4["dec_rot"]
+        lens4 = np.full(B4d, n4d, np.int32)
+        nb4 = n4d // 128
+        # R4 tables over one pool; each table's window pages are distinct from the others'
+        P4 = B4d * nb4
+        pool4 = torch.full((P4, 1, 128, DQ4), float("nan"), dtype=torch.bfloat16, device=dev)
+        tables4 = []
+        for r in range(R4):
+            bt4, _ = synth.decode_block_table(s4, lens4, 128, rotation=r)
+            tables4.append(bt4)
+        win_ids = sorted({int(bt[b, t]) for bt in tables4 for b in range(B4d) for t in [0] + list(range(nb4 - 7, nb4))})
+        pool4[torch.tensor(win_ids, dtype=torch.long, device=dev)] = synth.torch_normal_bf16(
+            1000 * s4 + 3, (len(win_ids), 1, 128, DQ4), 1 / 24, device=dev)
+        q4d = [synth.torch_normal_bf16(1000 * s4 + 10 + r, (B4d, H4, DQ4), 1 / 24, device=dev) for r in range(R4)]
+        bts4 = [torch.from_numpy(bt).to(dev) for bt in tables4]
+        sl4 = torch.from_numpy(lens4).to(dev)
+        o4d = torch.empty((B4d, H4, DV4), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
     rows = ["a1 block_index", "a2 ssa_prefill", "a3 ssa_decode", "a5 dense_causal", "a6-a7 page_select",
             "a8 page_prefill", "a4 mla_prefill", "a4 mla_decode"]
     nev = len(rows) + 1
 
-    only = set(x for x in args.only.split(",") if x)
-    run = {name: (not only) or (name in only) for name in ("prefill", "decode", "dense", "page", "mla")}
+    if run["copy"]:
+        cp_src = torch.ones((1 << 29,), dtype=torch.bfloat16, device=dev)
+        cp_dst = torch.empty_like(cp_src)
 
     def step(s, ev=None):
         def mark(i):
@@ -315,6 +440,8 @@ def main():
             r4 = s % R4
             ssa.decode(q4d[r4], pool4, pool4[..., :DV4], bts4[r4], sl4, scale=1 / 24, out=o4d)
         mark(8)
+        if run["copy"]:
+            cp_dst.copy_(cp_src)
 
     print("[bench] warmup", flush=True)
     for s in range(args.warmup):
@@ -351,10 +478,10 @@ def main():
     b5 = 2 * L5 * H5 * D5 * 2
     kernels = {
         "ssa_prefill": {"bound": "mfma", "achieved": tf2, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                        "frac": tf2 / PEAK_BF16_TFLOPS, "traffic": traffic_for("prefill.hip", "ssa_prefill"),
+                        "frac": tf2 / PEAK_BF16_TFLOPS, "traffic": traffic_for("ssa_prefill"),
                         "us": per_row[1] * 1e3, "work": f2},
         "ssa_decode": {"bound": "hbm", "achieved": gb3, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                       "frac": gb3 / PEAK_HBM_GBS, "traffic": traffic_for("decode.hip", "ssa_decode"),
+                       "frac": gb3 / PEAK_HBM_GBS, "traffic": traffic_for("ssa_decode"),
                        "us": per_row[2] * 1e3, "work": b3},
         "dense_causal": {"bound": "mfma", "achieved": fd / (per_row[3] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": fd / (per_row[3] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -371,10 +498,10 @@ def main():
     b4 = mla_decode_bytes(lens4, H4, DQ4, DV4)
     kernels["mla_prefill"] = {"bound": "mfma", "achieved": f4 / (per_row[6] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                               "unit": "TFLOP/s", "frac": f4 / (per_row[6] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                              "us": per_row[6] * 1e3, "work": f4}
+                              "traffic": traffic_for("mla_prefill"), "us": per_row[6] * 1e3, "work": f4}
     kernels["mla_decode"] = {"bound": "hbm", "achieved": b4 / (per_row[7] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                              "unit": "GB/s", "frac": b4 / (per_row[7] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                             "us": per_row[7] * 1e3, "work": b4}
+                             "traffic": traffic_for("mla_decode"), "us": per_row[7] * 1e3, "work": b4}
     out = {
         "metric": "SSA prefill TFLOP/s (frac MFMA peak) + decode GB/s (frac HBM) at 128K ctx",
         "value": tf2,

@@ -89,8 +89,10 @@ void decode_mla_kernel(DecodeParams p) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int hgroups = p.Hq / kHeads;
-  const int b = blockIdx.x / hgroups, h0 = (blockIdx.x % hgroups) * kHeads;
+  // sequence fastest: consecutive workgroups go to consecutive XCDs, so with
+  // B a multiple of 8 every head group of a sequence runs on one XCD and the
+  // sequence's latent pages are fetched into that XCD's L2 once
+  const int b = blockIdx.x % p.B, h0 = (blockIdx.x / p.B) * kHeads;
   const int n = p.seq_lens[b];
   if (threadIdx.x == 0) bad = 0;
   __syncthreads();

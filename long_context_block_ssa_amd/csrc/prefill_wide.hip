@@ -1,19 +1,24 @@
-// Block-sparse causal attention prefill for wide heads on gfx950: the
-// latent-shared (MLA-like) shape Dqk = 576, Dv = 512, where every query head
-// reads one shared latent row per key and the value is its first 512
-// channels.  LoZA rewrites LongCat's MLA attention (QbitAI report on LongCat
-// LoZA); within the listed key blocks this is the masked softmax of equation
-// (2) of the "LoZA: ZigZag sparse attention" page, section 2.1, causal in
-// the own block (section 2.2.1), evaluated as an exact online softmax.
+// Block-sparse causal attention prefill in bf16 on gfx950: the streaming
+// kernel for every bf16 shape -- Dqk = Dv = 64 or 128, and the latent-shared
+// (MLA-like) shape Dqk = 576, Dv = 512, where every query head reads one
+// shared latent row per key and the value is its first 512 channels (LoZA
+// rewrites LongCat's MLA attention, QbitAI report on LongCat LoZA).  Within
+// the listed key blocks (SSA window, page-selected list, or all blocks for
+// the dense layer) this is the masked softmax of equation (2) of the "LoZA:
+// ZigZag sparse attention" page, section 2.1, causal in the own block
+// (section 2.2.1), evaluated as an exact online softmax.
 //
-// One workgroup = one 128-query block of one head: 4 waves x 32 queries,
-// one wave per SIMD (the 32 x 512 fp32 output accumulator alone is 256
-// registers per lane).  Keys stream in 64-key stages through two LDS slots:
+// One workgroup = one 128-query block of one head, 16*NQ queries per wave
+// (NQ = 2 for d <= 128: 4 waves; NQ = 1 for the 512-wide accumulator:
+// 8 waves), two waves per SIMD.  Keys stream in 64-key stages through two
+// LDS slots:
 //   - staging uses global_load_lds_dwordx4 (global -> LDS, no registers);
 //     rows are padded by one 16-byte unit so that the 16 lanes reading a
 //     fragment column hit 16 distinct bank groups;
-//   - S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K rows, ds_read_b128);
-//   - O^T = V^T P^T: the V^T operand is read from the row-major K/V slab with
+//   - S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K rows, ds_read_b128;
+//     B = Q^T held in registers), so each lane owns one query column;
+//   - O^T = V^T P^T: P^T comes from the S^T accumulators converted to bf16;
+//     the V^T operand is read from the row-major V slab with
 //     ds_read_b64_tr_b16, which hands each lane 4 keys of one channel, so the
 //     latent is staged once and serves as both K and V;
 //   - the running max is refreshed lazily: the accumulator is rescaled only
@@ -34,10 +39,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlk = 128;
 constexpr int kStageKeys = 64;
-constexpr int kNQ = 1;                 // 16-query tiles per wave
-constexpr int kRows = 16 * kNQ;        // queries per wave
-constexpr int kWWaves = kBlk / kRows;  // waves per workgroup (one query block)
-constexpr int kWThreads = kWWaves * 64;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;  // log2 headroom before the accumulator is rescaled
@@ -74,29 +75,72 @@ struct WideGeom {
   static_assert(KUNITS % 64 == 0 && VUNITS % 64 == 0, "slab = whole 1 KB wave writes");
 };
 
-// Stage `rows0 .. rows0+63` of a [L, D] operand into an LDS slab with row
-// pitch U units.  The wave issues instruction i for linear units
-// [ (w + i*NW) * 64, +64 ); a lane on the pad unit loads unit 0 of its row.
-// Keys at or past L are clamped to row L-1 (finite data, masked later).
-template <int D, int U>
-__device__ __forceinline__ void stage_rows(SSA_LDS u32x4* slab, const __bf16* base, int64_t stride_l, int key0,
-                                           int L, int wave, int lane) {
-  constexpr int TOTAL = kStageKeys * U / 64;  // wave-instructions for the slab
-#pragma unroll 4
-  for (int i = wave; i < TOTAL; i += kWWaves) {
-    const int pidx = i * 64 + lane;
-    const int row = pidx / U, pos = pidx - row * U;
-    const int unit = pos < D / 8 ? pos : 0;
-    const int key = min(key0 + row, L - 1);
-    const __bf16* src = base + static_cast<int64_t>(key) * stride_l + unit * 8;
-    __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(src), (SSA_LDS void*)(slab + i * 64), 16, 0, 0);
-  }
-}
+// Stages rows key0 .. key0+63 of a [L, D] operand into an LDS slab with row
+// pitch U units (one 16-byte unit per lane per wave-instruction: the wave
+// issues instructions i = wave, wave + NW, ... for linear units
+// [i*64, i*64+64)).  A lane's (row, unit) is the same for every stage; with
+// CACHE its element offset row*stride + unit*8 is kept in registers, else it
+// is recomputed per stage (the 512-wide accumulator leaves no registers).  A
+// lane on a row's pad unit loads unit 0 of its row.  Keys at or past L are
+// clamped to row L-1 (finite data, masked later).
+template <int D, int U, int NW, bool CACHE>
+struct Stager {
+  static constexpr int TOTAL = kStageKeys * U / 64;  // wave-instructions per slab
+  static constexpr int PER = (TOTAL + NW - 1) / NW;  // per wave
+  int32_t off[CACHE ? PER : 1];
 
-template <int DQK, int DV, bool SHARED, typename OutT>
-__global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(kWWaves / 4, kWWaves / 4)))
+  __device__ __forceinline__ static void place(int i, int lane, int& row, int& unit) {
+    const int pidx = i * 64 + lane;
+    row = pidx / U;
+    const int pos = pidx - row * U;
+    unit = pos < D / 8 ? pos : 0;
+  }
+  __device__ __forceinline__ void init(int64_t stride_l, int wave, int lane) {
+    if constexpr (CACHE) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        int row, unit;
+        place(wave + j * NW, lane, row, unit);
+        off[j] = static_cast<int32_t>(row * stride_l) + unit * 8;
+      }
+    }
+  }
+  __device__ __forceinline__ void issue(SSA_LDS u32x4* slab, const __bf16* base, int64_t stride_l, int key0, int L,
+                                        int wave, int lane) const {
+    const bool ragged = key0 + kStageKeys > L;  // uniform: only the last block of a ragged L
+    if (CACHE && !ragged) {
+      const __bf16* row0 = base + static_cast<int64_t>(key0) * stride_l;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = wave + j * NW;
+        if (i < TOTAL)
+          __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(row0 + off[CACHE ? j : 0]),
+                                           (SSA_LDS void*)(slab + i * 64), 16, 0, 0);
+      }
+      return;
+    }
+#pragma unroll 4
+    for (int i = wave; i < TOTAL; i += NW) {
+      int row, unit;
+      place(i, lane, row, unit);
+      const int key = min(key0 + row, L - 1);
+      const __bf16* src = base + static_cast<int64_t>(key) * stride_l + unit * 8;
+      __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(src), (SSA_LDS void*)(slab + i * 64), 16, 0, 0);
+    }
+  }
+};
+
+// NQ = 16-query tiles per wave; the workgroup's 128 / (16 NQ) waves cover one
+// query block.  Two waves per SIMD: one 8-wave workgroup (NQ = 1) or two
+// independent 4-wave workgroups (NQ = 2) per CU.  DENSE: every block
+// 0 .. qb, own block first (the dense comparison layer); else the block list.
+template <int DQK, int DV, bool SHARED, int NQ, bool DENSE, typename OutT>
+__global__ __launch_bounds__(kBlk / (16 * NQ) * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_wide_kernel(PrefillParams p) {
   using G = WideGeom<DQK, DV, SHARED>;
+  constexpr int kNQ = NQ;
+  constexpr int kRows = 16 * NQ;
+  constexpr int kWWaves = kBlk / kRows;
   constexpr int NC = DQK / 32;  // 32-channel contraction chunks
   constexpr int NJ = DV / 16;   // 16-channel output tiles
   // two distinct LDS objects, so the compiler can tell a read of one slot from
@@ -104,7 +148,8 @@ void prefill_wide_kernel(PrefillParams p) {
   __shared__ u32x4 slot_a[G::SLOT];
   __shared__ u32x4 slot_b[G::NSLOTS == 2 ? G::SLOT : 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave-level branches scalar
   const int r = lane & 15, g = lane >> 4;
   // tile order: query blocks last to first, then batch, heads fastest, so the
   // workgroups in flight share their key blocks through L2
@@ -122,7 +167,7 @@ void prefill_wide_kernel(PrefillParams p) {
   // direct-to-LDS prefetch (vector-memory counters drain in order)
   __shared__ int32_t blist[64];
   int count;
-  if (p.dense) {
+  if constexpr (DENSE) {
     count = qb + 1;
   } else {
     count = min(p.cnt[b * p.cnt_sb + h * p.cnt_sh + qb], p.W);
@@ -131,7 +176,9 @@ void prefill_wide_kernel(PrefillParams p) {
     __syncthreads();
   }
   auto block_of = [&](int s) -> int {  // -1: skip
-    const int kb = p.dense ? qb - s : blist[s];
+    // the list entry is the same in every lane: say so, so that everything
+    // derived from it (addresses, masks, branches) stays scalar
+    const int kb = DENSE ? qb - s : __builtin_amdgcn_readfirstlane(blist[s]);
     return (kb < 0 || kb > qb || kb >= p.nqb) ? -1 : kb;
   };
   const int nst = 2 * count;
@@ -162,13 +209,17 @@ void prefill_wide_kernel(PrefillParams p) {
     for (int n = 0; n < kNQ; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int NS = G::NSLOTS;
+  Stager<DQK, G::UK, kWWaves, (kNQ >= 2)> kst;
+  kst.init(p.ks_l, wave, lane);
+  Stager<DV, G::UV, kWWaves, (kNQ >= 2)> vst;
+  if constexpr (!SHARED) vst.init(p.vs_l, wave, lane);
   auto issue = [&](int s, u32x4* slot_generic) {
     const int kb = block_of(s >> 1);
     if (kb < 0) return;
     SSA_LDS u32x4* slot = (SSA_LDS u32x4*)(slot_generic);
     const int key0 = kb * kBlk + (s & 1) * kStageKeys;
-    stage_rows<DQK, G::UK>(slot, kbase, p.ks_l, key0, p.L, wave, lane);
-    if constexpr (!SHARED) stage_rows<DV, G::UV>(slot + G::KUNITS, vbase, p.vs_l, key0, p.L, wave, lane);
+    kst.issue(slot, kbase, p.ks_l, key0, p.L, wave, lane);
+    if constexpr (!SHARED) vst.issue(slot + G::KUNITS, vbase, p.vs_l, key0, p.L, wave, lane);
   };
 
   // one stage: keys (s>>1)*128 + (s&1)*64 .. +63, staged in `cur`
@@ -185,14 +236,46 @@ void prefill_wide_kernel(PrefillParams p) {
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int n = 0; n < kNQ; ++n) sc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kNQ >= 2) {
+      // K fragments are read KD channel chunks ahead of their MFMAs so that the
+      // LDS latency is covered by the MFMAs of the chunks in between
+      constexpr int KD = 1;
+      bf16x8 kf[KD + 1][4];
+      auto load_k = [&](int c) {
+  #pragma unroll
+        for (int t = 0; t < 4; ++t)
+          kf[c % (KD + 1)][t] = __builtin_bit_cast(bf16x8, kslab[(t * 16 + r) * G::UK + c * 4 + g]);
+      };
+  #pragma unroll
+      for (int c = 0; c < KD && c < NC; ++c) load_k(c);
+  #pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if (c + KD < NC) load_k(c + KD);
+  #pragma unroll
+        for (int t = 0; t < 4; ++t)
+  #pragma unroll
+          for (int n = 0; n < kNQ; ++n)
+            sc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c % (KD + 1)][t], qf[n][c], sc[t][n], 0, 0, 0);
+      }
+      // keep that order: first reads, then per chunk its MFMAs after the next reads
+  #pragma unroll
+      for (int c = 0; c < KD && c < NC; ++c) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  #pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if (c + KD < NC) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * kNQ, 0);
+      }
+    } else {
+      // the 512-wide accumulator leaves no registers for read-ahead here
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
+      for (int c = 0; c < NC; ++c) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, kslab[(t * 16 + r) * G::UK + c * 4 + g]);
+        for (int t = 0; t < 4; ++t) {
+          const bf16x8 kf1 = __builtin_bit_cast(bf16x8, kslab[(t * 16 + r) * G::UK + c * 4 + g]);
 #pragma unroll
-        for (int n = 0; n < kNQ; ++n)
-          sc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[n][c], sc[t][n], 0, 0, 0);
+          for (int n = 0; n < kNQ; ++n)
+            sc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf1, qf[n][c], sc[t][n], 0, 0, 0);
+        }
       }
     }
     const bool valid_all = (kb + 1) * kBlk <= p.L && kb < qb;
@@ -241,32 +324,75 @@ void prefill_wide_kernel(PrefillParams p) {
         }
       l[n] += xlane_sum(rs);
     }
-    // O^T += V^T P^T over two 32-key chunks
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      bf16x8 pf[kNQ];
-#pragma unroll
-      for (int n = 0; n < kNQ; ++n) {
-        const bf16x4 a = __builtin_convertvector(sc[2 * c][n], bf16x4);
-        const bf16x4 bq = __builtin_convertvector(sc[2 * c + 1][n], bf16x4);
-        pf[n] = bf16x8{a[0], a[1], a[2], a[3], bq[0], bq[1], bq[2], bq[3]};
-      }
-      // transposed reads: lane j of group g points at key c*32 + h2*16 +
-      // 4g + j/4, channels 16*jt + 4*(j%4) .. +3; it receives channel
-      // 16*jt + j of keys c*32 + h2*16 + 4g .. +3
-      const int krow = c * 32 + 4 * g + (r >> 2);
-      const int ch_off = 4 * (r & 3);
-#pragma unroll
-      for (int jt = 0; jt < NJ; ++jt) {
-        const int ch = jt * 16 + ch_off;
+    // O^T += V^T P^T over two 32-key chunks.  Step st = c * NJ + jt: the
+    // V^T fragment of (chunk c, channel tile jt) is two transposed reads --
+    // lane j of group g points at key c*32 + h2*16 + 4g + j/4, channels
+    // 16*jt + 4*(j%4) .. +3, and receives channel 16*jt + j of keys
+    // c*32 + h2*16 + 4g .. +3 -- issued VD steps ahead of its MFMAs.
+    if constexpr (kNQ >= 2) {
+      constexpr int VD = 4;
+      constexpr int NSTEP = 2 * NJ;
+      bf16x8 vfr[VD + 1];
+      auto load_v = [&](int st) {
+        const int c = st / NJ, jt = st % NJ;
+        const int krow = c * 32 + 4 * g + (r >> 2);
+        const int ch = jt * 16 + 4 * (r & 3);
         const SSA_LDS char* base0 = (const SSA_LDS char*)(vslab + krow * UV + (ch >> 3)) + (ch & 7) * 2;
         const SSA_LDS char* base1 = base0 + 16 * UV * 16;
         const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSA_LDS bf16x4*)base0);
         const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSA_LDS bf16x4*)base1);
-        const bf16x8 vf = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-#pragma unroll
+        vfr[st % (VD + 1)] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      };
+      bf16x8 pf[2][kNQ];
+  #pragma unroll
+      for (int c = 0; c < 2; ++c)
+  #pragma unroll
+        for (int n = 0; n < kNQ; ++n) {
+          const bf16x4 a = __builtin_convertvector(sc[2 * c][n], bf16x4);
+          const bf16x4 bq = __builtin_convertvector(sc[2 * c + 1][n], bf16x4);
+          pf[c][n] = bf16x8{a[0], a[1], a[2], a[3], bq[0], bq[1], bq[2], bq[3]};
+        }
+  #pragma unroll
+      for (int st = 0; st < VD && st < NSTEP; ++st) load_v(st);
+  #pragma unroll
+      for (int st = 0; st < NSTEP; ++st) {
+        if (st + VD < NSTEP) load_v(st + VD);
+        const int c = st / NJ, jt = st % NJ;
+  #pragma unroll
         for (int n = 0; n < kNQ; ++n)
-          acc[jt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[n], acc[jt][n], 0, 0, 0);
+          acc[jt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr[st % (VD + 1)], pf[c][n], acc[jt][n], 0, 0, 0);
+      }
+  #pragma unroll
+      for (int st = 0; st < VD && st < NSTEP; ++st) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+  #pragma unroll
+      for (int st = 0; st < NSTEP; ++st) {
+        if (st + VD < NSTEP) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, kNQ, 1);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        bf16x8 pf1[kNQ];
+#pragma unroll
+        for (int n = 0; n < kNQ; ++n) {
+          const bf16x4 a = __builtin_convertvector(sc[2 * c][n], bf16x4);
+          const bf16x4 bq = __builtin_convertvector(sc[2 * c + 1][n], bf16x4);
+          pf1[n] = bf16x8{a[0], a[1], a[2], a[3], bq[0], bq[1], bq[2], bq[3]};
+        }
+        const int krow = c * 32 + 4 * g + (r >> 2);
+        const int ch_off = 4 * (r & 3);
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
+          const int ch = jt * 16 + ch_off;
+          const SSA_LDS char* base0 = (const SSA_LDS char*)(vslab + krow * UV + (ch >> 3)) + (ch & 7) * 2;
+          const SSA_LDS char* base1 = base0 + 16 * UV * 16;
+          const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSA_LDS bf16x4*)base0);
+          const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSA_LDS bf16x4*)base1);
+          const bf16x8 vf = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+          for (int n = 0; n < kNQ; ++n)
+            acc[jt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf1[n], acc[jt][n], 0, 0, 0);
+        }
       }
     }
   };
@@ -311,20 +437,35 @@ void prefill_wide_kernel(PrefillParams p) {
   }
 }
 
-template <int DQK, int DV, bool SHARED, typename OutT>
+template <int DQK, int DV, bool SHARED, int NQ, bool DENSE, typename OutT>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.nqb) * p.B * p.Hq);
-  return launch_kernel(prefill_wide_kernel<DQK, DV, SHARED, OutT>, grid, dim3(kWThreads), 0, stream, p);
+  return launch_kernel(prefill_wide_kernel<DQK, DV, SHARED, NQ, DENSE, OutT>, grid, dim3(kBlk / (16 * NQ) * 64), 0,
+                       stream, p);
+}
+
+template <int DQK, int DV, bool SHARED, int NQ>
+hipError_t launch_mode(const PrefillParams& p, bool out_f32, hipStream_t stream) {
+  if (p.dense)
+    return out_f32 ? launch_one<DQK, DV, SHARED, NQ, true, float>(p, stream)
+                   : launch_one<DQK, DV, SHARED, NQ, true, __bf16>(p, stream);
+  return out_f32 ? launch_one<DQK, DV, SHARED, NQ, false, float>(p, stream)
+                 : launch_one<DQK, DV, SHARED, NQ, false, __bf16>(p, stream);
+}
+
+template <int DQK, int DV, int NQ>
+hipError_t launch_dims(const PrefillParams& p, bool shared, bool out_f32, hipStream_t stream) {
+  return shared ? launch_mode<DQK, DV, true, NQ>(p, out_f32, stream) : launch_mode<DQK, DV, false, NQ>(p, out_f32, stream);
 }
 
 }  // namespace
 
 hipError_t launch_prefill_wide(const PrefillParams& p, int dqk, int dv, bool out_f32, hipStream_t stream) {
-  if (dqk != 576 || dv != 512) return hipErrorNotSupported;
   const bool shared = p.v == p.k && p.vs_b == p.ks_b && p.vs_l == p.ks_l && p.vs_h == p.ks_h;
-  if (shared)
-    return out_f32 ? launch_one<576, 512, true, float>(p, stream) : launch_one<576, 512, true, __bf16>(p, stream);
-  return out_f32 ? launch_one<576, 512, false, float>(p, stream) : launch_one<576, 512, false, __bf16>(p, stream);
+  if (dqk == 576 && dv == 512) return launch_dims<576, 512, 1>(p, shared, out_f32, stream);
+  if (dqk == 128 && dv == 128) return launch_dims<128, 128, 2>(p, shared, out_f32, stream);
+  if (dqk == 64 && dv == 64) return launch_dims<64, 64, 2>(p, shared, out_f32, stream);
+  return hipErrorNotSupported;
 }
 
 }  // namespace ssa

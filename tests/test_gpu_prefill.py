@@ -94,8 +94,8 @@ def test_dense_causal_parity_small(lib):
 
 
 def test_ssa_equals_dense_below_window(lib):
-    """L <= 1024: SSA and the dense layer read the same keys; the two kernels
-    then run the same arithmetic and must agree bit for bit."""
+    """L <= 1024: every key is inside the window, so SSA and the dense layer
+    compute the same attention."""
     B, L, H, D = 1, 1024, 2, 128
     _, q = gen(9, synth.Q, B, L, H, D)
     _, k = gen(9, synth.K, B, L, H, D)
@@ -104,8 +104,9 @@ def test_ssa_equals_dense_below_window(lib):
     o1, _ = lib.ssa(q, k, v)
     o2, _ = lib.dense_causal(q, k, v)
     torch.cuda.synchronize()
-    # same blocks, but visited in a different order: equal up to rounding
-    assert (o1.float() - o2.float()).abs().max().item() <= 2e-3
+    # same keys, visited in a different order (and rescaled at different
+    # moments): equal up to the bf16 rounding of the outputs
+    assert (o1.float() - o2.float()).abs().max().item() <= 1e-2
 
 
 def test_structural_onehot_prefill(lib):
