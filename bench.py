@@ -164,7 +164,7 @@ def cpu_baseline(budget_s: float = 25.0):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
 KERNEL_SOURCES = {  # row key -> (kernel-name fragments in the trace, source file)
-    "ssa_prefill": (("prefill_wide_kernel", "128"), "prefill_wide.hip"),
+    "ssa_prefill": (("prefill_d128_kernel",), "prefill_d128.hip"),
     "ssa_decode": (("decode_mha_kernel", "128"), "decode.hip"),
     "mla_prefill": (("prefill_wide_kernel", "576"), "prefill_wide.hip"),
     "mla_decode": (("decode_mla_kernel", "true"), "decode_mla.hip"),
@@ -235,6 +235,8 @@ def write_traffic(fetch_dir: str, write_dir: str, out_path: str):
 
 def short_kernel_name(name: str) -> str:
     """'void ssa::(anonymous namespace)::k<128, 128, false, 2, __bf16>(ssa::P)' -> 'k<128, 128, false, 2, __bf16>'."""
+    # the profiler's own demangler prints the template arguments <__bf16, true> as <bool _Accum, bool, E>
+    name = name.replace("<bool _Accum, bool, E>", "<__bf16, true>")
     n = name.replace("void ", "").replace("ssa::(anonymous namespace)::", "").replace("ssa::", "")
     depth = 0
     for i, ch in enumerate(n):  # cut at the argument list (the first '(' outside template brackets)
@@ -257,10 +259,12 @@ def write_trace_summary(stats_csv: str, out_path: str, command: str):
 
     def demangle(n):
         if n.startswith("_Z") and shutil.which("c++filt"):
-            # this c++filt predates the mangling of __bf16 (DF16b): spell it as float, then put it back
-            out = subprocess.run(["c++filt", n.replace("DF16b", "f")], capture_output=True, text=True).stdout.strip()
+            # this c++filt predates the mangling of __bf16 (DF16b): spell it as a
+            # placeholder class name, then put it back
+            out = subprocess.run(["c++filt", n.replace("DF16b", "9BFLOAT16x")], capture_output=True,
+                                 text=True).stdout.strip()
             if out and not out.startswith("_Z"):
-                return out.replace(", float>", ", __bf16>") if "DF16b" in n else out
+                return out.replace("BFLOAT16x", "__bf16")
         return n
 
     trace_csv = stats_csv.replace("kernel_stats.csv", "kernel_trace.csv")

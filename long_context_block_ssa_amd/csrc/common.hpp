@@ -98,6 +98,9 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, int dqk, int dv, bo
 
 // Dqk = 576, Dv = 512 (latent-shared heads); called by launch_prefill
 hipError_t launch_prefill_wide(const PrefillParams& p, int dqk, int dv, bool out_f32, hipStream_t stream);
+// bf16, Dqk = Dv = 128: 32 queries per wave, two waves per SIMD
+bool prefill_d128_supports(const PrefillParams& p, int dqk, int dv);
+hipError_t launch_prefill_d128(const PrefillParams& p, bool out_f32, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeParams& p, int dqk, int dv, hipStream_t stream);
 

@@ -17,8 +17,9 @@
 // instruction contracts over 4 keys, so for O^T = V^T P^T the S^T elements a
 // lane holds are exactly its P^T operand and V is read row-major from LDS.
 //
-// bf16 shapes (64/64, 128/128 and the latent-shared 576/512) run the
-// streaming kernel of prefill_wide.hip.
+// bf16 shapes: 128/128 runs the kernel of prefill_d128.hip,
+// 64/64 and the latent-shared 576/512 the streaming kernel of
+// prefill_wide.hip.
 #include "common.hpp"
 
 namespace ssa {
@@ -219,6 +220,7 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, int dqk, int dv, bo
     const dim3 grid(static_cast<unsigned>(p.nqb) * p.B * p.Hq);
     return launch_kernel(prefill_f32_kernel<64>, grid, dim3(kThreads), 0, stream, p);
   }
+  if (prefill_d128_supports(p, dqk, dv)) return launch_prefill_d128(p, out_f32, stream);
   return launch_prefill_wide(p, dqk, dv, out_f32, stream);
 }
 

@@ -1,0 +1,419 @@
+// Block-sparse causal attention prefill, bf16, Dqk = Dv = 128, on gfx950.
+//
+// Within the key blocks listed for a query block (the SSA window: block 0 +
+// the 7 most recent blocks, QbitAI report on LongCat LoZA; a page-selected
+// list; or all blocks 0..qb for the dense layer) this is the masked softmax of
+// equation (2) of the "LoZA: ZigZag sparse attention" page (section 2.1),
+// causal in the own block (section 2.2.1), evaluated as an exact online
+// softmax.
+//
+// Layout of the work:
+//   - one workgroup = one 128-query block of one head: 4 waves of 32 queries,
+//     two workgroups per CU, so each SIMD interleaves two waves;
+//   - keys stream in 32-key stages through a 4-slot LDS ring filled with
+//     global_load_lds_dwordx4 (global -> LDS, no registers), 3 stages in
+//     flight, one barrier per stage;
+//   - S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16: each lane
+//     owns one query column of the 32 x 32 tile and 16 of its keys, so the
+//     row max needs one cross-lane swap (v_permlane32_swap) and the row sum
+//     none until the end; P^T is the score accumulator converted to bf16;
+//     V^T is read with ds_read_b64_tr_b16 in the key order the P^T registers
+//     imply;
+//   - rows are stored in LDS with the 16-byte units of row r XOR-permuted by
+//     f(r) = 4 (r mod 4) + (r / 4 mod 4): the fragment reads (16 rows, one
+//     unit) and the transposed reads (4 rows, 4 units) hit distinct banks,
+//     and a 32-row slab is exactly 8 wave-wide DMA writes, two per wave;
+//   - no rescaling inside the loop: a query column's reference max is the max
+//     of the first stage that has a key for it (its accumulator and sum are
+//     still zero then) and stays fixed, so later weights exp(s - ref) may
+//     exceed 1.  The true max is tracked on the side; if it ends more than
+//     2^64 above the reference (weights, sums and outputs could then
+//     approach the fp32 range), the workgroup runs its tile again with the
+//     true max as the reference.  Any fixed reference gives the same
+//     normalised result, so this is exact.
+#include "common.hpp"
+
+namespace ssa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define SSA_LDS __attribute__((address_space(3)))
+#define SSA_GLB __attribute__((address_space(1)))
+
+constexpr int kD = 128;
+constexpr int kBlk = 128;
+constexpr int kSK = 32;                   // keys per stage
+constexpr int kSlots = 4;                 // LDS ring depth
+constexpr int kUnits = kD / 8;            // 16-byte units per row
+constexpr int kSlab = kSK * kUnits;       // units per K (or V) slab: 8 KB
+constexpr int kSlotBytes = 2 * kSlab * 16;  // K slab, then V slab: 16 KB
+constexpr int kWaves = 4;
+constexpr int kMaxW = 64;  // longest block list a query block may have
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kHeadroom = 64.f;  // log2 growth of the max over the reference before a rerun
+
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+// max / sum with the lane 32 apart (the other half of the same query column)
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(x, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// vmcnt(4 k) alone (expcnt and lgkmcnt left at their maximum): all but this
+// wave's loads of the last k stages have landed (4 loads a stage)
+__device__ __forceinline__ void wait_stages(int k) {
+  if (k >= 2)
+    __builtin_amdgcn_s_waitcnt(0x0F78);
+  else if (k == 1)
+    __builtin_amdgcn_s_waitcnt(0x0F74);
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Workgroup barrier for the stage loop.  __syncthreads() would also wait for
+// every outstanding vector-memory load (its release fence), draining the
+// prefetch ring; the only memory the barrier has to order here is LDS
+// written by this wave's direct-to-LDS loads, which wait_stages has already
+// waited for, and LDS reads that have returned before their MFMAs issued.
+// The empty asm statements keep the compiler from moving LDS accesses
+// across the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Reads of a ring slot.  The compiler cannot tell which in-flight
+// direct-to-LDS load a plain LDS read may overlap, and would wait for all of
+// them (draining the ring) before the slot's first read.  The stage's own
+// loads are already waited for and published by the stage barrier, so the
+// reads are issued from asm blocks the compiler does not track; each block
+// waits for its reads before it ends, and its outputs are early-clobber so
+// that no output register can be an address still to be read.  OFF is the
+// slot's byte offset in the ring (an instruction immediate).
+template <int OFF>
+__device__ __forceinline__ void lds_read_k4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x4 (&o)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%8\n"
+      "ds_read_b128 %1, %5 offset:%8\n"
+      "ds_read_b128 %2, %6 offset:%8\n"
+      "ds_read_b128 %3, %7 offset:%8\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "i"(OFF)
+      : "memory");
+}
+// eight transposed 8-byte reads: at a0..a3, then 16 rows on (+4096 bytes)
+template <int OFF>
+__device__ __forceinline__ void lds_read_vt8(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x2 (&o)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%12\n"
+      "ds_read_b64_tr_b16 %1, %9 offset:%12\n"
+      "ds_read_b64_tr_b16 %2, %10 offset:%12\n"
+      "ds_read_b64_tr_b16 %3, %11 offset:%12\n"
+      "ds_read_b64_tr_b16 %4, %8 offset:%13\n"
+      "ds_read_b64_tr_b16 %5, %9 offset:%13\n"
+      "ds_read_b64_tr_b16 %6, %10 offset:%13\n"
+      "ds_read_b64_tr_b16 %7, %11 offset:%13\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "i"(OFF), "i"(OFF + 4096)
+      : "memory");
+}
+
+template <typename OutT>
+__device__ __forceinline__ void store4(OutT* dst, f32x4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float* dst, f32x4 v) {
+  *reinterpret_cast<f32x4*>(dst) = v;
+}
+template <>
+__device__ __forceinline__ void store4<__bf16>(__bf16* dst, f32x4 v) {
+  *reinterpret_cast<bf16x4*>(dst) = __builtin_convertvector(v, bf16x4);
+}
+
+template <typename OutT, bool DENSE>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_d128_kernel(PrefillParams p) {
+  __shared__ u32x4 ring[kSlots * kSlotBytes / 16];
+  __shared__ int32_t blist[kMaxW];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h32 = lane >> 5;  // which half of the 32-lane column pair
+  const int c32 = lane & 31;
+  // tile order: query blocks last to first (the dense layer's longest rows
+  // first), then batch, heads fastest
+  const int bh_count = p.B * p.Hq;
+  const int qb = p.nqb - 1 - static_cast<int>(blockIdx.x) / bh_count;
+  const int bh = static_cast<int>(blockIdx.x) % bh_count;
+  const int b = bh / p.Hq, h = bh % p.Hq;
+  const int hk = h / p.group;
+  const int qoff = wave * 32;  // this wave's first query inside the block
+
+  const __bf16* qbase = static_cast<const __bf16*>(p.q) + b * p.qs_b + h * p.qs_h;
+  const __bf16* kbase = static_cast<const __bf16*>(p.k) + b * p.ks_b + hk * p.ks_h;
+  const __bf16* vbase = static_cast<const __bf16*>(p.v) + b * p.vs_b + hk * p.vs_h;
+
+  // ---- the block list, kept in LDS: a global read inside the stage loop
+  // would make its wait also wait for the in-flight direct-to-LDS loads ----
+  int nblk;
+  if constexpr (DENSE) {
+    nblk = qb + 1;  // own block first, then down to 0
+  } else {
+    nblk = min(p.cnt[b * p.cnt_sb + h * p.cnt_sh + qb], p.W);
+    const int32_t* list = p.idx + b * p.idx_sb + h * p.idx_sh + static_cast<int64_t>(qb) * p.W;
+    if (tid < kMaxW) {
+      const int kb = tid < nblk ? list[tid] : -1;
+      blist[tid] = (kb < 0 || kb > qb || kb >= p.nqb) ? -1 : kb;
+    }
+    __syncthreads();
+  }
+  const int nst = nblk * (kBlk / kSK);
+  // block of stage s; -1 for a skipped list entry and for stages past the end
+  auto stage_block = [&](int s) -> int {
+    if (s >= nst) return -1;
+    if constexpr (DENSE) return qb - (s >> 2);
+    return __builtin_amdgcn_readfirstlane(blist[s >> 2]);
+  };
+
+  // ---- per-lane constants -----------------------------------------------
+  // DMA: slab instruction j covers rows 4j .. 4j+3 (row 4j + lane/16; the lane
+  // on physical unit lane%16 loads logical unit (lane%16) ^ f(row)); wave w
+  // issues j = w and j = w + 4 of the K slab and of the V slab, whose rows
+  // (16 apart) share f
+  const int drow = 4 * wave + (lane >> 4);
+  const int dunit = (lane & 15) ^ swz(drow);
+  const uint32_t koff = static_cast<uint32_t>(drow * p.ks_l + dunit * 8);
+  const uint32_t voff = static_cast<uint32_t>(drow * p.vs_l + dunit * 8);
+  const int64_t k16 = 16 * p.ks_l, v16 = 16 * p.vs_l;
+  const uint32_t ring0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SSA_LDS u32x4*)(ring)));
+  // K fragment c (A operand): row c32, logical unit 2c + h32
+  uint32_t kaddr[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) kaddr[c] = ring0 + (c32 * kUnits + ((2 * c + h32) ^ swz(c32))) * 16;
+  // V^T fragment (dim tile dt, read e): lane i of 16-lane group g points at
+  // key 8e + 4(g/2) + i/4 (+ 16 for the second 16-key chunk), channels
+  // 32dt + 16(g%2) + 4(i%4) .. +3
+  uint32_t vaddr[2][4];
+  {
+    const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int row = 8 * e + 4 * (g >> 1) + (i >> 2);
+        const int ch = 32 * dt + 16 * (g & 1) + 4 * (i & 3);
+        vaddr[e][dt] = ring0 + (kSlab + row * kUnits + ((ch >> 3) ^ swz(row))) * 16 + (ch & 7) * 2;
+      }
+  }
+
+  // ---- queries (B operand of S^T = K Q^T) -------------------------------
+  bf16x8 qf[8];
+  {
+    const int row = qb * kBlk + qoff + c32;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      u32x4 v = {0, 0, 0, 0};
+      if (row < p.L) v = *reinterpret_cast<const u32x4*>(qbase + row * p.qs_l + c * 16 + h32 * 8);
+      qf[c] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  // m: reference max of this lane's query column (raw score units),
+  // mt: true max so far
+  float m = kNegInf, mt = kNegInf, l;
+  f32x16 acc[4];
+
+  // ---- staging: this wave's four loads of stage s into ring slot `slot` ---
+  auto issue = [&](int s, int slot) {
+    const int kb = max(stage_block(s), 0);  // skipped entries stage block 0 (unused)
+    const int key0 = kb * kBlk + (s & 3) * kSK;
+    SSA_LDS u32x4* kd = (SSA_LDS u32x4*)(ring) + slot * (kSlotBytes / 16) + wave * 64;
+    SSA_LDS u32x4* vd = kd + kSlab;
+#define SSA_DMA(src, dst) \
+  __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(src), (SSA_LDS void*)(dst), 16, 0, 0)
+    if (key0 + kSK <= p.L) {
+      const __bf16* ks = kbase + static_cast<int64_t>(key0) * p.ks_l + koff;
+      const __bf16* vs = vbase + static_cast<int64_t>(key0) * p.vs_l + voff;
+      SSA_DMA(ks, kd);
+      SSA_DMA(ks + k16, kd + 256);
+      SSA_DMA(vs, vd);
+      SSA_DMA(vs + v16, vd + 256);
+    } else {
+      // last block of a ragged L: rows at or past L repeat row L-1 (finite, masked later)
+      const int64_t r0 = min(key0 + drow, p.L - 1), r1 = min(key0 + drow + 16, p.L - 1);
+      SSA_DMA(kbase + r0 * p.ks_l + dunit * 8, kd);
+      SSA_DMA(kbase + r1 * p.ks_l + dunit * 8, kd + 256);
+      SSA_DMA(vbase + r0 * p.vs_l + dunit * 8, vd);
+      SSA_DMA(vbase + r1 * p.vs_l + dunit * 8, vd + 256);
+    }
+#undef SSA_DMA
+  };
+
+  // ---- one stage: keys of stage s in ring slot SLOT; first this wave's
+  // loads of stage ns (if any) into slot nslot ------------------------------
+  auto stage = [&](auto slot_tag, int s, int ns, int nslot) {
+    constexpr int SLOT = decltype(slot_tag)::value;
+    constexpr int OFF = SLOT * kSlotBytes;
+    const int kb = stage_block(s);
+    const int sub = s & 3;
+    const int key0 = kb * kBlk + sub * kSK;
+    const bool need = kb >= 0 && key0 < p.L && !(kb == qb && sub * kSK > qoff + 31);
+    if (ns < nst) issue(ns, nslot);
+    if (!need) return;
+    // S^T = K Q^T: 32 keys x 32 queries
+    f32x16 sc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+#pragma unroll
+    for (int h4 = 0; h4 < 2; ++h4) {  // K fragments in two batches of four
+      u32x4 kraw[4];
+      lds_read_k4<OFF>(kaddr[4 * h4], kaddr[4 * h4 + 1], kaddr[4 * h4 + 2], kaddr[4 * h4 + 3], kraw);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kraw[c]), qf[4 * h4 + c], sc, 0, 0, 0);
+    }
+    // own block: key > query; keys at or past L
+    if (kb == qb || key0 + kSK > p.L) {
+      const int qi = qb * kBlk + qoff + c32;
+      const int lim = min(qi, p.L - 1) - key0 - 4 * h32;  // last valid key offset
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + (i & 3) > lim) sc[i] = kNegInf;
+    }
+    // softmax with a fixed reference max
+    float a8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a8[i] = fmaxf(sc[i], sc[i + 8]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a8[i] = fmaxf(a8[i], a8[i + 4]);
+    const float mx = pair_max(fmaxf(fmaxf(a8[0], a8[1]), fmaxf(a8[2], a8[3])));
+    mt = fmaxf(mt, mx);
+    if (m == kNegInf) m = mx;  // first keys of this column: nothing to rescale
+    // a column with no key seen yet keeps m = -inf: its scores are all -inf
+    const float mc = m == kNegInf ? 0.f : m * p.c1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], p.c1, -mc));
+    float r8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r8[i] = sc[i] + sc[i + 8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r8[i] += r8[i + 4];
+    l += (r8[0] + r8[1]) + (r8[2] + r8[3]);
+    bf16x8 pf[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16x4 a = __builtin_convertvector((f32x4){sc[8 * c], sc[8 * c + 1], sc[8 * c + 2], sc[8 * c + 3]}, bf16x4);
+      const bf16x4 bq =
+          __builtin_convertvector((f32x4){sc[8 * c + 4], sc[8 * c + 5], sc[8 * c + 6], sc[8 * c + 7]}, bf16x4);
+      pf[c] = bf16x8{a[0], a[1], a[2], a[3], bq[0], bq[1], bq[2], bq[3]};
+    }
+    // O^T += V^T P^T: chunk c = keys 16c .. 16c+15 in the P^T register order
+    u32x2 v0raw[8], v1raw[8];  // [c * 4 + dt]: reads e = 0 and e = 1
+    lds_read_vt8<OFF>(vaddr[0][0], vaddr[0][1], vaddr[0][2], vaddr[0][3], v0raw);
+    lds_read_vt8<OFF>(vaddr[1][0], vaddr[1][1], vaddr[1][2], vaddr[1][3], v1raw);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const bf16x4 v0 = __builtin_bit_cast(bf16x4, v0raw[c * 4 + dt]);
+        const bf16x4 v1 = __builtin_bit_cast(bf16x4, v1raw[c * 4 + dt]);
+        const bf16x8 vf = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], acc[dt], 0, 0, 0);
+      }
+  };
+
+  // stage s + 1 must have landed (this wave's loads), then every wave's
+  auto settle = [&](int s) {
+    const int last = max(kSlots - 2, min(s + kSlots - 1, nst - 1));  // last stage issued
+    wait_stages(last - (s + 1));
+    stage_barrier();
+  };
+
+  for (int pass = 0; pass < 2; ++pass) {
+    l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+    // prologue: stages 0 .. 2 in flight.  They are issued whether or not they
+    // exist (a stage past the end stages rows of block 0 into a slot nobody
+    // reads), so the number of loads behind the queries is fixed and the
+    // compiler's wait for them is exact.
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    wait_stages(2);  // stage 0
+    stage_barrier();
+    // Whole groups of 4 stages, so that the loop is left only at its end;
+    // stages past the end only take the barrier.
+    const int nst_pad = (nst + kSlots - 1) & ~(kSlots - 1);
+    for (int s0 = 0; s0 < nst_pad; s0 += kSlots) {
+#define SSA_STAGE(k)                                                                 \
+  {                                                                                  \
+    const int s = s0 + (k);                                                          \
+    if (s < nst) stage(std::integral_constant<int, (k)>{}, s, s + kSlots - 1, ((k) + kSlots - 1) % kSlots); \
+    settle(s);                                                                       \
+  }
+      SSA_STAGE(0)
+      SSA_STAGE(1)
+      SSA_STAGE(2)
+      SSA_STAGE(3)
+#undef SSA_STAGE
+    }
+    // the max grew too far above the reference somewhere in the workgroup:
+    // run the tile again with the true max as the reference
+    const bool far = (mt - m) * p.c1 > kHeadroom;
+    if (pass == 1 || !__syncthreads_or(far)) break;
+    m = mt;
+  }
+
+  // ---- output ------------------------------------------------------------
+  OutT* obase = static_cast<OutT*>(p.o) + b * p.os_b + h * p.os_h;
+  const float lt = pair_sum(l);
+  const int row = qb * kBlk + qoff + c32;
+  if (row >= p.L) return;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x4 v = {acc[dt][4 * k], acc[dt][4 * k + 1], acc[dt][4 * k + 2], acc[dt][4 * k + 3]};
+      store4<OutT>(obase + row * p.os_l + 32 * dt + 8 * k + 4 * h32, v * inv);
+    }
+  if (p.lse && h32 == 0) {
+    const float v = lt > 0.f ? m * p.scale + __builtin_amdgcn_logf(lt) * kLn2 : kNegInf;
+    p.lse[(static_cast<int64_t>(b) * p.Hq + h) * p.L + row] = v;
+  }
+}
+
+template <typename OutT, bool DENSE>
+hipError_t launch_d128(const PrefillParams& p, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(p.nqb) * p.B * p.Hq);
+  return launch_kernel(prefill_d128_kernel<OutT, DENSE>, grid, dim3(kWaves * 64), 0, stream, p);
+}
+
+}  // namespace
+
+bool prefill_d128_supports(const PrefillParams& p, int dqk, int dv) {
+  return dqk == kD && dv == kD && (p.dense || p.W <= kMaxW);
+}
+
+hipError_t launch_prefill_d128(const PrefillParams& p, bool out_f32, hipStream_t stream) {
+  if (p.dense) return out_f32 ? launch_d128<float, true>(p, stream) : launch_d128<__bf16, true>(p, stream);
+  return out_f32 ? launch_d128<float, false>(p, stream) : launch_d128<__bf16, false>(p, stream);
+}
+
+}  // namespace ssa

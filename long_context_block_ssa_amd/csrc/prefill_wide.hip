@@ -1,5 +1,5 @@
 // Block-sparse causal attention prefill in bf16 on gfx950: the streaming
-// kernel for every bf16 shape -- Dqk = Dv = 64 or 128, and the latent-shared
+// kernel for Dqk = Dv = 64 and for the latent-shared
 // (MLA-like) shape Dqk = 576, Dv = 512, where every query head reads one
 // shared latent row per key and the value is its first 512 channels (LoZA
 // rewrites LongCat's MLA attention, QbitAI report on LongCat LoZA).  Within
@@ -9,7 +9,7 @@
 // (section 2.2.1), evaluated as an exact online softmax.
 //
 // One workgroup = one 128-query block of one head, 16*NQ queries per wave
-// (NQ = 2 for d <= 128: 4 waves; NQ = 1 for the 512-wide accumulator:
+// (NQ = 2 for d = 64: 4 waves; NQ = 1 for the 512-wide accumulator:
 // 8 waves), two waves per SIMD.  Keys stream in 64-key stages through two
 // LDS slots:
 //   - staging uses global_load_lds_dwordx4 (global -> LDS, no registers);
@@ -463,7 +463,6 @@ hipError_t launch_dims(const PrefillParams& p, bool shared, bool out_f32, hipStr
 hipError_t launch_prefill_wide(const PrefillParams& p, int dqk, int dv, bool out_f32, hipStream_t stream) {
   const bool shared = p.v == p.k && p.vs_b == p.ks_b && p.vs_l == p.ks_l && p.vs_h == p.ks_h;
   if (dqk == 576 && dv == 512) return launch_dims<576, 512, 1>(p, shared, out_f32, stream);
-  if (dqk == 128 && dv == 128) return launch_dims<128, 128, 2>(p, shared, out_f32, stream);
   if (dqk == 64 && dv == 64) return launch_dims<64, 64, 2>(p, shared, out_f32, stream);
   return hipErrorNotSupported;
 }
