@@ -70,7 +70,7 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4 v, float* f) {
 
 constexpr int kMaxWaves = 16;
 #ifndef SSA_DECODE_SUB
-#define SSA_DECODE_SUB 32
+#define SSA_DECODE_SUB 16
 #endif
 #ifndef SSA_DECODE_PIPE
 #define SSA_DECODE_PIPE 0
@@ -91,10 +91,12 @@ __device__ __forceinline__ float dot8_bf16(const float* q, const u32x4 k) {
 
 // One workgroup per (sequence, kv head).  The window's blocks are split over
 // the waves: `split` waves per block (128 / split keys each), streamed in
-// sub-passes of 32 keys -- 16-byte loads, D/8 lanes per key row, so a wave
-// reads 4 (D = 128) or 8 (D = 64) whole rows per instruction.
-template <int D>
-__global__ __launch_bounds__(1024) void decode_mha_kernel(DecodeParams p, int split) {
+// sub-passes of kSub keys -- 16-byte loads, D/8 lanes per key row, so a wave
+// reads 4 (D = 128) or 8 (D = 64) whole rows per instruction.  MAXT: the
+// largest workgroup the instantiation serves (512 threads leave each wave
+// twice the registers 1024 would).
+template <int D, int MAXT>
+__global__ __launch_bounds__(MAXT) void decode_mha_kernel(DecodeParams p, int split) {
   constexpr int CPR = D / 8;     // lanes per key row (16 B each)
   constexpr int KPI = 64 / CPR;  // keys per wave-wide load
   constexpr int NI = kSub / KPI; // loads per sub-pass and operand
@@ -246,8 +248,13 @@ hipError_t launch_decode(const DecodeParams& p, int dqk, int dv, hipStream_t str
   const int split = width <= 8 ? SSA_DECODE_SPLIT8 : 1;  // waves per window block
   const dim3 grid(static_cast<unsigned>(p.B) * p.Hkv);
   const dim3 block(64 * width * split);
-  if (dqk == 128 && dv == 128) return launch_kernel(decode_mha_kernel<128>, grid, block, 0, stream, p, split);
-  if (dqk == 64 && dv == 64) return launch_kernel(decode_mha_kernel<64>, grid, block, 0, stream, p, split);
+  const bool small = block.x <= 512;
+  if (dqk == 128 && dv == 128)
+    return small ? launch_kernel(decode_mha_kernel<128, 512>, grid, block, 0, stream, p, split)
+                 : launch_kernel(decode_mha_kernel<128, 1024>, grid, block, 0, stream, p, split);
+  if (dqk == 64 && dv == 64)
+    return small ? launch_kernel(decode_mha_kernel<64, 512>, grid, block, 0, stream, p, split)
+                 : launch_kernel(decode_mha_kernel<64, 1024>, grid, block, 0, stream, p, split);
   return hipErrorNotSupported;
 }
 
