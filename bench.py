@@ -167,7 +167,7 @@ KERNEL_SOURCES = {  # row key -> (kernel-name fragments in the trace, source fil
     "ssa_prefill": (("prefill_d128_kernel",), "prefill_d128.hip"),
     "ssa_decode": (("decode_mha_kernel", "128"), "decode.hip"),
     "mla_prefill": (("prefill_wide_kernel", "576"), "prefill_wide.hip"),
-    "mla_decode": (("decode_mla_kernel", "true"), "decode_mla.hip"),
+    "mla_decode": (("decode_mla_partial_kernel", "true"), "decode_mla.hip"),
 }
 
 
@@ -403,6 +403,7 @@ def main():
         bts4 = [torch.from_numpy(bt).to(dev) for bt in tables4]
         sl4 = torch.from_numpy(lens4).to(dev)
         o4d = torch.empty((B4d, H4, DV4), dtype=torch.bfloat16, device=dev)
+        ws4 = torch.empty((ssa.decode_workspace_size(B4d, H4, DQ4, DV4) + 256,), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     rows = ["a1 block_index", "a2 ssa_prefill", "a3 ssa_decode", "a5 dense_causal", "a6-a7 page_select",
@@ -442,7 +443,7 @@ def main():
         mark(7)
         if run["mla"]:
             r4 = s % R4
-            ssa.decode(q4d[r4], pool4, pool4[..., :DV4], bts4[r4], sl4, scale=1 / 24, out=o4d)
+            ssa.decode(q4d[r4], pool4, pool4[..., :DV4], bts4[r4], sl4, scale=1 / 24, out=o4d, workspace=ws4)
         mark(8)
         if run["copy"]:
             cp_dst.copy_(cp_src)

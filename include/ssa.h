@@ -116,7 +116,11 @@ typedef struct ssa_block_lists {
  * window names a page outside [0, num_pages), gets an all-NaN output row (and
  * lse = NaN) and nothing out of range is read.
  * Supported (dtype, Dqk, Dv): (BF16, 64, 64), (BF16, 128, 128) with
- * Hq/Hkv <= 16, and (BF16, 576, 512) with Hkv == 1. */
+ * Hq/Hkv <= 16, and (BF16, 576, 512) with Hkv == 1 and Hq a multiple of 16.
+ * The (576, 512) shape splits every window over its blocks and keeps fp32
+ * per-block partials in a caller-owned device workspace of at least
+ * ssa_decode_workspace_size bytes, 256-byte aligned (SSA_ERR_WORKSPACE if it
+ * is missing or short); the other shapes ignore both fields. */
 typedef struct ssa_decode_args {
   int32_t dtype; /* of q, k_pages, v_pages and o: BF16 */
   int32_t B, Hq, Hkv, Dqk, Dv;
@@ -135,6 +139,8 @@ typedef struct ssa_decode_args {
   int64_t v_stride[3];
   int64_t o_stride[2];
   int64_t bt_stride;
+  void* workspace;        /* device scratch, contents on entry ignored */
+  size_t workspace_bytes; /* its size */
 } ssa_decode_args;
 
 /* ---------------------------------------------------------------------------
@@ -171,10 +177,20 @@ int ssa_dense_causal(const ssa_attn_args* a, void* stream);
  * ssa_decode -- one decode step of SSA over a paged cache: the query at
  * position n - 1 reads the window of its block (block 0 and the 7 most recent
  * blocks, the last one holding (n - 1) mod 128 + 1 valid keys).  The window is
- * split over its blocks and the per-block softmax partials are merged inside
- * the kernel.  No workspace.
+ * split over its blocks and the per-block softmax partials are merged exactly
+ * (max-subtracted pieces rescaled to the common maximum): inside one kernel
+ * for the 64- and 128-wide heads, through the workspace and a second kernel
+ * for the 576/512 latent.  Two calls that share a workspace must be ordered
+ * (same stream); the workspace may be reused as soon as the call's work on
+ * the stream is done.
  * ------------------------------------------------------------------------- */
 int ssa_decode(const ssa_decode_args* a, const ssa_window* win, void* stream);
+
+/* Bytes of workspace ssa_decode needs for these sizes and window: 0 for the
+ * 64- and 128-wide heads, B * Hq * (n_global + n_local) * 2064 rounded up to
+ * a multiple of 256 for Dqk = 576, Dv = 512.  Reads only B, Hq, Dqk, Dv and
+ * the window; 0 for NULL arguments. */
+size_t ssa_decode_workspace_size(const ssa_decode_args* a, const ssa_window* win);
 
 /* ---------------------------------------------------------------------------
  * ssa_page_select -- block lists for the page-selected variant (LongCat

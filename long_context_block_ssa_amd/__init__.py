@@ -29,7 +29,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 # every symbol include/ssa.h declares
 EXPORTS = (
     "ssa_block_index", "ssa_block_index_seq", "ssa_prefill", "ssa_dense_causal", "ssa_decode",
-    "ssa_page_select", "ssa_page_select_workspace_size", "ssa_last_error", "ssa_version",
+    "ssa_decode_workspace_size", "ssa_page_select", "ssa_page_select_workspace_size", "ssa_last_error", "ssa_version",
 )
 
 
@@ -82,6 +82,7 @@ class CDecodeArgs(ctypes.Structure):
         ("q_stride", ctypes.c_int64 * 2), ("k_stride", ctypes.c_int64 * 3),
         ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 2),
         ("bt_stride", ctypes.c_int64),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -120,6 +121,8 @@ def load(path: str = LIB_PATH):
     lib.ssa_prefill.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CBlockLists), vp]
     lib.ssa_dense_causal.argtypes = [ctypes.POINTER(CAttnArgs), vp]
     lib.ssa_decode.argtypes = [ctypes.POINTER(CDecodeArgs), ctypes.POINTER(CWindow), vp]
+    lib.ssa_decode_workspace_size.argtypes = [ctypes.POINTER(CDecodeArgs), ctypes.POINTER(CWindow)]
+    lib.ssa_decode_workspace_size.restype = ctypes.c_size_t
     lib.ssa_page_select_workspace_size.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CWindow)]
     lib.ssa_page_select_workspace_size.restype = ctypes.c_size_t
     lib.ssa_page_select.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CWindow), i32, vp, vp, vp,
@@ -272,9 +275,20 @@ def dense_causal(q, k, v, scale=None, out=None, out_dtype=None, with_lse=False, 
     return out, lse
 
 
+def decode_workspace_size(B: int, Hq: int, Dqk: int, Dv: int, window: Window = DEFAULT_WINDOW) -> int:
+    """ssa_decode_workspace_size: bytes of device workspace ssa_decode needs (0 for most shapes)."""
+    a = CDecodeArgs()
+    a.B, a.Hq, a.Dqk, a.Dv = B, Hq, Dqk, Dv
+    w = window.c()
+    return int(load().ssa_decode_workspace_size(ctypes.byref(a), ctypes.byref(w)))
+
+
 def decode(q, k_pages, v_pages, block_table, seq_lens, scale=None, window: Window = DEFAULT_WINDOW,
-           out=None, with_lse=False, lse=None, stream=None):
-    """ssa_decode over a paged cache.  Returns (o [B, Hq, Dv], lse [B, Hq] or None)."""
+           out=None, with_lse=False, lse=None, workspace=None, stream=None):
+    """ssa_decode over a paged cache.  Returns (o [B, Hq, Dv], lse [B, Hq] or None).
+
+    ``workspace`` (a uint8 device tensor) is allocated here when the shape
+    needs one and none is given."""
     lib = load()
     B, Hq, Dqk = q.shape
     P, Hkv, page, _ = k_pages.shape
@@ -299,6 +313,13 @@ def decode(q, k_pages, v_pages, block_table, seq_lens, scale=None, window: Windo
     a.o_stride = (ctypes.c_int64 * 2)(out.stride(0), out.stride(1))
     a.bt_stride = block_table.stride(0)
     w = window.c()
+    need = int(lib.ssa_decode_workspace_size(ctypes.byref(a), ctypes.byref(w)))
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty((need + 256,), dtype=torch.uint8, device=q.device)
+        base = workspace.data_ptr()
+        off = (-base) % 256
+        a.workspace, a.workspace_bytes = base + off, max(workspace.numel() - off, 0)
     _check(lib.ssa_decode(ctypes.byref(a), ctypes.byref(w), _stream(stream)))
     return out, lse
 

@@ -202,6 +202,12 @@ int ssa_dense_causal(const ssa_attn_args* a, void* stream) {
   return device_status(e, who);
 }
 
+size_t ssa_decode_workspace_size(const ssa_decode_args* a, const ssa_window* win) {
+  if (!a || !win || a->B < 1 || a->Hq < 1 || win->n_global < 0 || win->n_local < 0) return 0;
+  if (!(a->Dqk == 576 && a->Dv == 512)) return 0;
+  return (ssa::decode_mla_workspace_bytes(a->B, a->Hq, win->n_global + win->n_local) + 255) / 256 * 256;
+}
+
 int ssa_decode(const ssa_decode_args* a, const ssa_window* win, void* stream) {
   const char* who = "ssa_decode";
   if (!a) return fail(SSA_ERR_INVALID, "%s: args is NULL", who);
@@ -233,11 +239,18 @@ int ssa_decode(const ssa_decode_args* a, const ssa_window* win, void* stream) {
     return fail(SSA_ERR_INVALID, "%s: bt_stride=%lld < max_blocks=%d", who, static_cast<long long>(a->bt_stride),
                 a->max_blocks);
   const bool mha = (a->Dqk == 64 && a->Dv == 64) || (a->Dqk == 128 && a->Dv == 128);
-  const bool mla = a->Dqk == 576 && a->Dv == 512 && a->Hkv == 1;
+  const bool mla = a->Dqk == 576 && a->Dv == 512 && a->Hkv == 1 && a->Hq % 16 == 0;
   if (!(mha && a->Hq / a->Hkv <= 16) && !mla)
     return fail(SSA_ERR_UNSUPPORTED, "%s: no kernel for Dqk=%d Dv=%d Hq=%d Hkv=%d", who, a->Dqk, a->Dv, a->Hq,
                 a->Hkv);
   if (win->block_size != 128) return fail(SSA_ERR_UNSUPPORTED, "%s: block_size must be 128", who);
+  const size_t need = ssa_decode_workspace_size(a, win);
+  if (need > 0) {
+    if (!a->workspace || a->workspace_bytes < need)
+      return fail(SSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
+                  a->workspace ? a->workspace_bytes : static_cast<size_t>(0));
+    if (!aligned(a->workspace, 256)) return fail(SSA_ERR_INVALID, "%s: workspace must be 256-byte aligned", who);
+  }
   ssa::DecodeParams p{};
   p.q = a->q;
   p.k = a->k_pages;
@@ -267,6 +280,7 @@ int ssa_decode(const ssa_decode_args* a, const ssa_window* win, void* stream) {
   p.n_local = win->n_local;
   p.scale = a->scale;
   p.c1 = static_cast<float>(static_cast<double>(a->scale) * 1.4426950408889634);
+  p.work = need > 0 ? static_cast<float*>(a->workspace) : nullptr;
   hipError_t e = ssa::launch_decode(p, a->Dqk, a->Dv, as_stream(stream));
   if (e == hipErrorNotSupported) return fail(SSA_ERR_UNSUPPORTED, "%s: no kernel for Dqk=%d Dv=%d in this build", who, a->Dqk, a->Dv);
   return device_status(e, who);

@@ -68,6 +68,7 @@ struct DecodeParams {
   int32_t n_global, n_local;
   float c1;
   float scale;
+  float* work;  // Dqk = 576 only: per-(sequence, head, window slot) partials
 };
 
 struct PageSelectParams {
@@ -104,8 +105,10 @@ hipError_t launch_prefill_d128(const PrefillParams& p, bool out_f32, hipStream_t
 
 hipError_t launch_decode(const DecodeParams& p, int dqk, int dv, hipStream_t stream);
 
-// Dqk = 576, Dv = 512 with one kv head; called by launch_decode
+// Dqk = 576, Dv = 512 with one kv head; called by launch_decode.  Needs
+// p.work of decode_mla_workspace_bytes(B, Hq, n_global + n_local) bytes.
 hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t stream);
+size_t decode_mla_workspace_bytes(int32_t B, int32_t Hq, int32_t W);
 
 hipError_t launch_page_select(const PageSelectParams& p, hipStream_t stream);
 

@@ -162,6 +162,42 @@ def test_decode_rejects_window(lib):
     assert lib.ssa_decode(ctypes.byref(a), ctypes.byref(w), None) == ssa.SSA_ERR_INVALID
 
 
+def mla_decode_args(**over):
+    base = dict(B=3, Hq=32, Hkv=1, Dqk=576, Dv=512,
+                q_stride=(ctypes.c_int64 * 2)(32 * 576, 576),
+                k_stride=(ctypes.c_int64 * 3)(128 * 576, 128 * 576, 576),
+                v_stride=(ctypes.c_int64 * 3)(128 * 576, 128 * 576, 576),
+                o_stride=(ctypes.c_int64 * 2)(32 * 512, 512))
+    base.update(over)
+    return decode_args(**base)
+
+
+def test_decode_workspace_size(lib):
+    w = ssa.CWindow(128, 1, 7)
+    a = mla_decode_args()
+    # fp32 (512 channels + m + l + 2 pad) per (sequence, head, window slot)
+    assert lib.ssa_decode_workspace_size(ctypes.byref(a), ctypes.byref(w)) == (3 * 32 * 8 * 516 * 4 + 255) // 256 * 256
+    w2 = ssa.CWindow(128, 2, 3)
+    assert lib.ssa_decode_workspace_size(ctypes.byref(a), ctypes.byref(w2)) == (3 * 32 * 5 * 516 * 4 + 255) // 256 * 256
+    assert lib.ssa_decode_workspace_size(ctypes.byref(decode_args()), ctypes.byref(w)) == 0
+    assert lib.ssa_decode_workspace_size(None, ctypes.byref(w)) == 0
+    assert ssa.decode_workspace_size(3, 32, 576, 512) == (3 * 32 * 8 * 516 * 4 + 255) // 256 * 256
+
+
+def test_decode_mla_workspace_rules(lib):
+    w = ssa.CWindow(128, 1, 7)
+    a = mla_decode_args()
+    need = lib.ssa_decode_workspace_size(ctypes.byref(a), ctypes.byref(w))
+    assert lib.ssa_decode(ctypes.byref(a), ctypes.byref(w), None) == ssa.SSA_ERR_WORKSPACE
+    a = mla_decode_args(workspace=FAKE, workspace_bytes=need - 1)
+    assert lib.ssa_decode(ctypes.byref(a), ctypes.byref(w), None) == ssa.SSA_ERR_WORKSPACE
+    assert "workspace" in lib.ssa_last_error().decode()
+    a = mla_decode_args(workspace=FAKE + 16, workspace_bytes=need)
+    assert lib.ssa_decode(ctypes.byref(a), ctypes.byref(w), None) == ssa.SSA_ERR_INVALID
+    a = mla_decode_args(Hq=24, workspace=FAKE, workspace_bytes=1 << 30)  # 16 heads per workgroup
+    assert lib.ssa_decode(ctypes.byref(a), ctypes.byref(w), None) == ssa.SSA_ERR_UNSUPPORTED
+
+
 def test_page_select_rejects(lib):
     a = good_args()
     w = ssa.CWindow(128, 1, 7)

@@ -91,3 +91,30 @@ def test_mla_decode_full_size(lib):
     lens = [1048576] * 8
     dev, host = build_case(4, 8, 128, 1, DQK, lens, mul=MUL, Dv=DV, share_kv=True)
     run_and_check(lib, dev, host, SCALE, "mla decode 1M", rel=True, v_view=dev["k"][..., :DV])
+
+
+def test_mla_decode_reused_workspace_and_invalid_rows(lib):
+    """A workspace holding NaN bytes from elsewhere, reused by a second call on
+    fewer sequences; rows with a bad length or page are NaN, the others match."""
+    lens = [500, 1300, 900, 700, 2000]
+    dev, host = build_case(83, len(lens), 16, 1, DQK, lens, mul=MUL, Dv=DV, share_kv=True)
+    ws = torch.full((lib.decode_workspace_size(len(lens), 16, DQK, DV) + 256,), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    vv = dev["k"][..., :DV]
+    ro, rl = oracle.decode(host["q"], host["k"], host["k"][..., :DV], host["bt"], host["sl"], SCALE)
+    say("mla decode dirty workspace")
+    o, lse = lib.decode(dev["q"], dev["k"], vv, dev["bt"], dev["sl"], scale=SCALE, with_lse=True, workspace=ws)
+    torch.cuda.synchronize()
+    check_close(to_f64(o), ro, "mla dirty workspace o", rel=True)
+    check_close(to_f64(lse), rl, "mla dirty workspace lse")
+    sl, bt = dev["sl"][:4].clone(), dev["bt"][:4].clone()
+    sl[1] = 0
+    bt[2, (900 - 1) // 128] = 10 ** 6  # own block of sequence 2 points outside the pool
+    sl[3] = bt.shape[1] * 128 + 1
+    say("mla decode invalid rows, reused workspace")
+    o2, l2 = lib.decode(dev["q"][:4], dev["k"], vv, bt, sl, scale=SCALE, with_lse=True, workspace=ws)
+    torch.cuda.synchronize()
+    o2n = o2.float().cpu().numpy()
+    assert np.isnan(o2n[1:]).all() and np.isnan(l2.cpu().numpy()[1:]).all()
+    check_close(to_f64(o2[0:1]), ro[0:1], "mla valid row beside invalid ones", rel=True)
+    check_close(to_f64(l2[0:1]), rl[0:1], "mla valid row lse")
