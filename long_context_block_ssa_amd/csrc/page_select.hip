@@ -12,10 +12,11 @@
 //   1. block_sums: one workgroup per (b, head, block) of q and of k; fp64
 //      sums of 128 bf16 rows (exact for these inputs, so the order of the
 //      additions does not matter).  An HBM scan of q and k.
-//   2. select: one workgroup per (b, query head, query block); fp64 scores of
-//      the candidate pages [n_global, qb - n_local], top-M by repeated
-//      arg-max (equal scores -> lower page), then the ascending list
-//      global blocks + chosen pages + local blocks, padded with -1.
+//   2. select: one workgroup per (b, query head, 16 query blocks); fp64
+//      scores of the candidate pages [n_global, qb - n_local] on the fp64
+//      matrix cores, top-M kept as a sorted per-row list (equal scores ->
+//      lower page), then the ascending list global blocks + chosen pages +
+//      local blocks, padded with -1.
 #include "common.hpp"
 
 namespace ssa {
@@ -73,105 +74,168 @@ __global__ __launch_bounds__(kSumThreads) void block_sums_kernel(PageSelectParam
   }
 }
 
+// ---------------------------------------------------------------------------
+// select: one workgroup of 4 waves per (b, query head, 16 query blocks).
+// Scores are a dense product: S[c][qb] = <ksum[c], qsum[qb]> over D
+// channels, taken 256 candidate pages at a time on v_mfma_f64_16x16x4_f64
+// (16 candidates x 16 query blocks per tile; lane (n, g) feeds candidate /
+// query block n and channels 8m + 2g, 8m + 2g + 1 for m = 0 .. D/8-1, so a
+// row's 4 lanes read 64 contiguous bytes per load).  Each query block keeps
+// a sorted list of its best top_m pages across the lanes of one wave; a
+// chunk's candidate enters only if it beats the list's last entry, by an
+// insertion at the rank a ballot gives.  "Beats" is a total order: higher
+// score, equal scores -> lower page (a NaN score counts as -inf).
+// ---------------------------------------------------------------------------
 constexpr int kSelThreads = 256;
+constexpr int kRows = 16;     // query blocks per workgroup
+constexpr int kChunk = 256;   // candidate pages scored per round
+constexpr int kPad = kChunk + 4;
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bool better(double sa, int ca, double sb, int cb) {
   return sa > sb || (sa == sb && ca < cb);
 }
 
-// dynamic LDS: scores[nqb] doubles
+__device__ __forceinline__ double read_lane_f64(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(u), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(u >> 32), l);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+template <int D>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(PageSelectParams p) {
-  extern __shared__ double scores[];
-  __shared__ double qs[128];
-  __shared__ double red_s[kSelThreads / 64];
-  __shared__ int red_c[kSelThreads / 64];
-  __shared__ int chosen[32];
+  constexpr int NM = D / 8;  // 16-byte loads per operand row share; 2 MFMAs each
+  __shared__ double sc[kRows][kPad];
 
-  const int t = blockIdx.x;
-  const int qb = t % p.nqb;
-  const int h = (t / p.nqb) % p.Hq;
-  const int b = t / (p.nqb * p.Hq);
+  const int tiles = (p.nqb + kRows - 1) / kRows;
+  const int tile = blockIdx.x % tiles;
+  const int h = (blockIdx.x / tiles) % p.Hq;
+  const int b = blockIdx.x / (tiles * p.Hq);
   const int hk = h / p.group;
-  const int D = p.D;
-  int32_t* out = p.idx + static_cast<int64_t>(t) * p.W;
+  const int qb0 = tile * kRows;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
 
-  const int g_end = min(p.n_global, qb + 1);
-  const int l_begin = max(g_end, qb - p.n_local + 1);
-  // candidate pages [g_end, l_begin)
-  const int ncand = l_begin - g_end;
-  const int take = min(ncand, p.top_m);
+  auto g_end_of = [&](int qb) { return min(p.n_global, qb + 1); };
+  auto l_begin_of = [&](int qb) { return max(g_end_of(qb), qb - p.n_local + 1); };
+  const int qb_last = min(qb0 + kRows, p.nqb) - 1;
+  const int ce = l_begin_of(qb_last);  // candidates of every row lie in [n_global, ce)
 
-  if (ncand > p.top_m) {
-    const double* qrow = p.qsum + static_cast<int64_t>(t) * D;
-    for (int d = threadIdx.x; d < D; d += kSelThreads) qs[d] = qrow[d];
-    __syncthreads();
-    const double* kbase = p.ksum + (static_cast<int64_t>(b) * p.Hkv + hk) * p.nqb * D;
-    for (int c = g_end + threadIdx.x; c < l_begin; c += kSelThreads) {
-      const double* kr = kbase + static_cast<int64_t>(c) * D;
-      double s = 0.0;
-      for (int d = 0; d < D; ++d) s = __builtin_fma(qs[d], kr[d], s);
-      scores[c] = s;
-    }
-    __syncthreads();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int r = 0; r < take; ++r) {
-      double bs = -__builtin_inf();
-      int bc = 0x7fffffff;
-      for (int c = g_end + threadIdx.x; c < l_begin; c += kSelThreads) {
-        const double s = scores[c];
-        if (better(s, c, bs, bc)) {
-          bs = s;
-          bc = c;
-        }
-      }
+  // B operand: query-block sums, lane (n, g) = query block qb0 + n
+  f64x2 qf[NM];
+  {
+    const int qrow = min(qb0 + n, p.nqb - 1);
+    const double* qs = p.qsum + ((static_cast<int64_t>(b) * p.Hq + h) * p.nqb + qrow) * D;
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const double os = __shfl_xor(bs, o);
-        const int oc = __shfl_xor(bc, o);
-        if (better(os, oc, bs, bc)) {
-          bs = os;
-          bc = oc;
+    for (int m = 0; m < NM; ++m) qf[m] = *reinterpret_cast<const f64x2*>(qs + 8 * m + 2 * g);
+  }
+  const double* kbase = p.ksum + (static_cast<int64_t>(b) * p.Hkv + hk) * p.nqb * D;
+
+  // the rows of this wave: qb0 + wave + 4 rr; list entry i of a row on lane i
+  double ls[kRows / 4];
+  int li[kRows / 4];
+#pragma unroll
+  for (int rr = 0; rr < kRows / 4; ++rr) {
+    ls[rr] = -__builtin_inf();
+    li[rr] = 0x7fffffff;
+  }
+  const int M = p.top_m;
+
+  for (int cc = p.n_global; cc < ce; cc += kChunk) {
+    // scores of candidates cc .. cc+255 for the 16 query blocks
+    for (int tt = wave; tt < kChunk / 16; tt += 4) {
+      const int c0 = cc + tt * 16;
+      if (c0 >= ce) break;
+      const double* kr = kbase + static_cast<int64_t>(min(c0 + n, ce - 1)) * D;
+      f64x2 kf[NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) kf[m] = *reinterpret_cast<const f64x2*>(kr + 8 * m + 2 * g);
+      f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(kf[m][0], qf[m][0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(kf[m][1], qf[m][1], acc, 0, 0, 0);
+      }
+      // lane (n, g), register r holds candidate c0 + g + 4r of query block
+      // qb0 + n (the f64 16x16 output puts row lane/16 + 4 r in register r)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[n][tt * 16 + g + 4 * r] = acc[r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < kRows / 4; ++rr) {
+      const int qb = qb0 + wave + 4 * rr;
+      if (qb >= p.nqb) continue;
+      const int c_lo = g_end_of(qb), c_hi = l_begin_of(qb);
+      if (c_hi - c_lo <= M) continue;  // every candidate is taken; no ranking
+      double ts = read_lane_f64(ls[rr], M - 1);
+      int tc = __builtin_amdgcn_readlane(li[rr], M - 1);
+#pragma unroll
+      for (int k = 0; k < kChunk / 64; ++k) {
+        const int c = cc + 64 * k + lane;
+        double s = sc[wave + 4 * rr][64 * k + lane];
+        if (s != s) s = -__builtin_inf();
+        bool q = c >= c_lo && c < c_hi && better(s, c, ts, tc);
+        uint64_t mask = __builtin_amdgcn_ballot_w64(q);
+        while (mask) {
+          const int src = __builtin_ctzll(mask);
+          mask &= mask - 1;
+          const double xs = read_lane_f64(s, src);
+          const int xc = cc + 64 * k + src;
+          if (!better(xs, xc, ts, tc)) continue;  // the bar rose since the ballot
+          // rank of x: list entries that beat it
+          const bool above = lane < M && better(ls[rr], li[rr], xs, xc);
+          const int pos = __builtin_popcountll(__builtin_amdgcn_ballot_w64(above));
+          // entries at or below pos move down by one (a whole-wave DPP shift:
+          // lane i receives lane i-1); x takes pos
+          const uint64_t u = __builtin_bit_cast(uint64_t, ls[rr]);
+          const uint32_t plo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(u), 0x138, 0xF, 0xF, false);
+          const uint32_t phi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(u >> 32), 0x138, 0xF, 0xF, false);
+          const int pc = __builtin_amdgcn_update_dpp(0, li[rr], 0x138, 0xF, 0xF, false);
+          if (lane > pos && lane < M) {
+            ls[rr] = __builtin_bit_cast(double, (static_cast<uint64_t>(phi) << 32) | plo);
+            li[rr] = pc;
+          } else if (lane == pos) {
+            ls[rr] = xs;
+            li[rr] = xc;
+          }
+          ts = read_lane_f64(ls[rr], M - 1);
+          tc = __builtin_amdgcn_readlane(li[rr], M - 1);
         }
       }
-      if (lane == 0) {
-        red_s[wave] = bs;
-        red_c[wave] = bc;
-      }
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        double ws = red_s[0];
-        int wc = red_c[0];
-        for (int w = 1; w < kSelThreads / 64; ++w)
-          if (better(red_s[w], red_c[w], ws, wc)) {
-            ws = red_s[w];
-            wc = red_c[w];
-          }
-        chosen[r] = wc;
-        scores[wc] = -__builtin_inf();  // removed from later rounds
-      }
-      __syncthreads();
     }
-  } else {
-    for (int r = threadIdx.x; r < take; r += kSelThreads) chosen[r] = g_end + r;
-    __syncthreads();
+    __syncthreads();  // the next chunk overwrites the scores
   }
-  if (threadIdx.x == 0) {
-    // sort the chosen pages (at most 32) ascending
-    for (int i = 1; i < take; ++i) {
-      const int x = chosen[i];
-      int j = i - 1;
-      while (j >= 0 && chosen[j] > x) {
-        chosen[j + 1] = chosen[j];
-        --j;
-      }
-      chosen[j + 1] = x;
+
+  // lists: global blocks, chosen pages ascending, local blocks, padding
+#pragma unroll
+  for (int rr = 0; rr < kRows / 4; ++rr) {
+    const int qb = qb0 + wave + 4 * rr;
+    if (qb >= p.nqb) continue;
+    const int g_end = g_end_of(qb), l_begin = l_begin_of(qb);
+    const int ncand = l_begin - g_end;
+    const int take = min(ncand, M);
+    const int64_t row = (static_cast<int64_t>(b) * p.Hq + h) * p.nqb + qb;
+    int32_t* out = p.idx + row * p.W;
+    const int nloc = qb - l_begin + 1;
+    const int count = g_end + take + nloc;
+    for (int pos = lane; pos < p.W; pos += 64) {
+      int v = -1;
+      if (pos < g_end) v = pos;
+      else if (pos >= g_end + take && pos < count) v = l_begin + (pos - g_end - take);
+      else if (pos < g_end + take && ncand <= M) v = pos;  // all candidates, already ascending
+      if (!(pos >= g_end && pos < g_end + take && ncand > M)) out[pos] = v;
     }
-    int s = 0;
-    for (int c = 0; c < g_end; ++c) out[s++] = c;
-    for (int i = 0; i < take; ++i) out[s++] = chosen[i];
-    for (int c = l_begin; c <= qb; ++c) out[s++] = c;
-    p.cnt[t] = s;
-    for (; s < p.W; ++s) out[s] = -1;
+    if (ncand > M) {
+      // lane i < take holds chosen page li; its place is its rank by page id
+      int rank = 0;
+      for (int j = 0; j < take; ++j) rank += __builtin_amdgcn_readlane(li[rr], j) < li[rr];
+      if (lane < take) out[g_end + rank] = li[rr];
+    }
+    if (lane == 0) p.cnt[row] = count;
   }
 }
 
@@ -181,9 +245,10 @@ hipError_t launch_page_select(const PageSelectParams& p, hipStream_t stream) {
   const int64_t nsum = static_cast<int64_t>(p.B) * (p.Hq + p.Hkv) * p.nqb;
   hipError_t e = launch_kernel(block_sums_kernel, dim3(static_cast<unsigned>(nsum)), dim3(kSumThreads), 0, stream, p);
   if (e != hipSuccess) return e;
-  const size_t lds = sizeof(double) * static_cast<size_t>(p.nqb);
-  return launch_kernel(select_kernel, dim3(static_cast<unsigned>(static_cast<int64_t>(p.B) * p.Hq * p.nqb)),
-                       dim3(kSelThreads), lds, stream, p);
+  const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.Hq * ((p.nqb + kRows - 1) / kRows));
+  if (p.D == 128) return launch_kernel(select_kernel<128>, dim3(grid), dim3(kSelThreads), 0, stream, p);
+  if (p.D == 64) return launch_kernel(select_kernel<64>, dim3(grid), dim3(kSelThreads), 0, stream, p);
+  return hipErrorNotSupported;
 }
 
 }  // namespace ssa
