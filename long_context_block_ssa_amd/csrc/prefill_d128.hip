@@ -12,7 +12,9 @@
 //     two workgroups per CU, so each SIMD interleaves two waves;
 //   - keys stream in 32-key stages through a 4-slot LDS ring filled with
 //     global_load_lds_dwordx4 (global -> LDS, no registers), 3 stages in
-//     flight, one barrier per stage;
+//     flight, one barrier per stage; a stage's K fragments are read in one
+//     batch, and its V^T fragments in a second batch issued behind the score
+//     MFMAs, so the LDS latency is exposed twice per stage;
 //   - S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16: each lane
 //     owns one query column of the 32 x 32 tile and 16 of its keys, so the
 //     row max needs one cross-lane swap (v_permlane32_swap) and the row sum
@@ -26,11 +28,13 @@
 //   - no rescaling inside the loop: a query column's reference max is the max
 //     of the first stage that has a key for it (its accumulator and sum are
 //     still zero then) and stays fixed, so later weights exp(s - ref) may
-//     exceed 1.  The true max is tracked on the side; if it ends more than
-//     2^64 above the reference (weights, sums and outputs could then
-//     approach the fp32 range), the workgroup runs its tile again with the
-//     true max as the reference.  Any fixed reference gives the same
-//     normalised result, so this is exact.
+//     exceed 1.  The first pass computes no max once every column has its
+//     reference; a weight above 2^64 (whose sums and outputs could approach
+//     the fp32 range) then shows as a partial row sum above 2^64, inf or
+//     NaN.  If any column of the workgroup shows one, the tile runs again
+//     tracking the true max, and once more with it as the reference if it
+//     ended more than 2^64 above the first.  Any fixed reference gives the
+//     same normalised result, so this is exact.
 #include "common.hpp"
 
 namespace ssa {
@@ -103,33 +107,50 @@ __device__ __forceinline__ void stage_barrier() {
 // waits for its reads before it ends, and its outputs are early-clobber so
 // that no output register can be an address still to be read.  OFF is the
 // slot's byte offset in the ring (an instruction immediate).
+//
+// the 8 K fragments of a stage
 template <int OFF>
-__device__ __forceinline__ void lds_read_k4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x4 (&o)[4]) {
+__device__ __forceinline__ void lds_read_k8(const uint32_t (&a)[8], u32x4 (&o)[8]) {
   asm volatile(
-      "ds_read_b128 %0, %4 offset:%8\n"
-      "ds_read_b128 %1, %5 offset:%8\n"
-      "ds_read_b128 %2, %6 offset:%8\n"
-      "ds_read_b128 %3, %7 offset:%8\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "i"(OFF)
-      : "memory");
-}
-// eight transposed 8-byte reads: at a0..a3, then 16 rows on (+4096 bytes)
-template <int OFF>
-__device__ __forceinline__ void lds_read_vt8(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x2 (&o)[8]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8 offset:%12\n"
-      "ds_read_b64_tr_b16 %1, %9 offset:%12\n"
-      "ds_read_b64_tr_b16 %2, %10 offset:%12\n"
-      "ds_read_b64_tr_b16 %3, %11 offset:%12\n"
-      "ds_read_b64_tr_b16 %4, %8 offset:%13\n"
-      "ds_read_b64_tr_b16 %5, %9 offset:%13\n"
-      "ds_read_b64_tr_b16 %6, %10 offset:%13\n"
-      "ds_read_b64_tr_b16 %7, %11 offset:%13\n"
+      "ds_read_b128 %0, %8 offset:%16\n"
+      "ds_read_b128 %1, %9 offset:%16\n"
+      "ds_read_b128 %2, %10 offset:%16\n"
+      "ds_read_b128 %3, %11 offset:%16\n"
+      "ds_read_b128 %4, %12 offset:%16\n"
+      "ds_read_b128 %5, %13 offset:%16\n"
+      "ds_read_b128 %6, %14 offset:%16\n"
+      "ds_read_b128 %7, %15 offset:%16\n"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "i"(OFF), "i"(OFF + 4096)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF)
+      : "memory");
+}
+// the 16 transposed V reads of a stage: e = 0 rows at a[0][0..3] and 16 rows
+// on (+4096 bytes), then e = 1 at a[1][0..3] and +4096
+template <int OFF>
+__device__ __forceinline__ void lds_read_vt16(const uint32_t (&a)[2][4], u32x2 (&o)[16]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:%24\n"
+      "ds_read_b64_tr_b16 %1, %17 offset:%24\n"
+      "ds_read_b64_tr_b16 %2, %18 offset:%24\n"
+      "ds_read_b64_tr_b16 %3, %19 offset:%24\n"
+      "ds_read_b64_tr_b16 %4, %16 offset:%25\n"
+      "ds_read_b64_tr_b16 %5, %17 offset:%25\n"
+      "ds_read_b64_tr_b16 %6, %18 offset:%25\n"
+      "ds_read_b64_tr_b16 %7, %19 offset:%25\n"
+      "ds_read_b64_tr_b16 %8, %20 offset:%24\n"
+      "ds_read_b64_tr_b16 %9, %21 offset:%24\n"
+      "ds_read_b64_tr_b16 %10, %22 offset:%24\n"
+      "ds_read_b64_tr_b16 %11, %23 offset:%24\n"
+      "ds_read_b64_tr_b16 %12, %20 offset:%25\n"
+      "ds_read_b64_tr_b16 %13, %21 offset:%25\n"
+      "ds_read_b64_tr_b16 %14, %22 offset:%25\n"
+      "ds_read_b64_tr_b16 %15, %23 offset:%25\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]),
+        "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]), "=&v"(o[12]), "=&v"(o[13]), "=&v"(o[14]), "=&v"(o[15])
+      : "v"(a[0][0]), "v"(a[0][1]), "v"(a[0][2]), "v"(a[0][3]), "v"(a[1][0]), "v"(a[1][1]), "v"(a[1][2]), "v"(a[1][3]),
+        "i"(OFF), "i"(OFF + 4096)
       : "memory");
 }
 
@@ -148,7 +169,6 @@ template <typename OutT, bool DENSE>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_d128_kernel(PrefillParams p) {
   __shared__ u32x4 ring[kSlots * kSlotBytes / 16];
-  __shared__ int32_t blist[kMaxW];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -167,26 +187,24 @@ void prefill_d128_kernel(PrefillParams p) {
   const __bf16* kbase = static_cast<const __bf16*>(p.k) + b * p.ks_b + hk * p.ks_h;
   const __bf16* vbase = static_cast<const __bf16*>(p.v) + b * p.vs_b + hk * p.vs_h;
 
-  // ---- the block list, kept in LDS: a global read inside the stage loop
+  // ---- the block list, read once into registers (entry i on lane i of
+  // every wave, fetched with readlane): a global read inside the stage loop
   // would make its wait also wait for the in-flight direct-to-LDS loads ----
-  int nblk;
+  int nblk, blane = -1;
   if constexpr (DENSE) {
     nblk = qb + 1;  // own block first, then down to 0
   } else {
     nblk = min(p.cnt[b * p.cnt_sb + h * p.cnt_sh + qb], p.W);
     const int32_t* list = p.idx + b * p.idx_sb + h * p.idx_sh + static_cast<int64_t>(qb) * p.W;
-    if (tid < kMaxW) {
-      const int kb = tid < nblk ? list[tid] : -1;
-      blist[tid] = (kb < 0 || kb > qb || kb >= p.nqb) ? -1 : kb;
-    }
-    __syncthreads();
+    const int kb = lane < nblk ? list[lane] : -1;
+    blane = (kb < 0 || kb > qb || kb >= p.nqb) ? -1 : kb;
   }
   const int nst = nblk * (kBlk / kSK);
   // block of stage s; -1 for a skipped list entry and for stages past the end
   auto stage_block = [&](int s) -> int {
     if (s >= nst) return -1;
     if constexpr (DENSE) return qb - (s >> 2);
-    return __builtin_amdgcn_readfirstlane(blist[s >> 2]);
+    return __builtin_amdgcn_readlane(blane, s >> 2);
   };
 
   // ---- per-lane constants -----------------------------------------------
@@ -234,6 +252,7 @@ void prefill_d128_kernel(PrefillParams p) {
   // m: reference max of this lane's query column (raw score units),
   // mt: true max so far
   float m = kNegInf, mt = kNegInf, l;
+  bool track = false;  // track the true max mt (reruns only)
   f32x16 acc[4];
 
   // ---- staging: this wave's four loads of stage s into ring slot `slot` ---
@@ -277,14 +296,16 @@ void prefill_d128_kernel(PrefillParams p) {
     f32x16 sc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+    {
+      u32x4 kraw[8];
+      lds_read_k8<OFF>(kaddr, kraw);
 #pragma unroll
-    for (int h4 = 0; h4 < 2; ++h4) {  // K fragments in two batches of four
-      u32x4 kraw[4];
-      lds_read_k4<OFF>(kaddr[4 * h4], kaddr[4 * h4 + 1], kaddr[4 * h4 + 2], kaddr[4 * h4 + 3], kraw);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kraw[c]), qf[4 * h4 + c], sc, 0, 0, 0);
+      for (int c = 0; c < 8; ++c)
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kraw[c]), qf[c], sc, 0, 0, 0);
     }
+    // V^T of the stage, read while the score MFMAs run
+    u32x2 vraw[16];
+    lds_read_vt16<OFF>(vaddr, vraw);
     // own block: key > query; keys at or past L
     if (kb == qb || key0 + kSK > p.L) {
       const int qi = qb * kBlk + qoff + c32;
@@ -293,15 +314,19 @@ void prefill_d128_kernel(PrefillParams p) {
       for (int i = 0; i < 16; ++i)
         if (8 * (i >> 2) + (i & 3) > lim) sc[i] = kNegInf;
     }
-    // softmax with a fixed reference max
-    float a8[8];
+    // softmax with a fixed reference max.  The column max is needed only
+    // until every column of the wave has its reference, or when the true max
+    // is tracked (a rerun)
+    if (track || __builtin_amdgcn_ballot_w64(m == kNegInf) != 0) {
+      float a8[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a8[i] = fmaxf(sc[i], sc[i + 8]);
+      for (int i = 0; i < 8; ++i) a8[i] = fmaxf(sc[i], sc[i + 8]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a8[i] = fmaxf(a8[i], a8[i + 4]);
-    const float mx = pair_max(fmaxf(fmaxf(a8[0], a8[1]), fmaxf(a8[2], a8[3])));
-    mt = fmaxf(mt, mx);
-    if (m == kNegInf) m = mx;  // first keys of this column: nothing to rescale
+      for (int i = 0; i < 4; ++i) a8[i] = fmaxf(a8[i], a8[i + 4]);
+      const float mx = pair_max(fmaxf(fmaxf(a8[0], a8[1]), fmaxf(a8[2], a8[3])));
+      mt = fmaxf(mt, mx);
+      if (m == kNegInf) m = mx;  // first keys of this column: nothing to rescale
+    }
     // a column with no key seen yet keeps m = -inf: its scores are all -inf
     const float mc = m == kNegInf ? 0.f : m * p.c1;
 #pragma unroll
@@ -321,9 +346,8 @@ void prefill_d128_kernel(PrefillParams p) {
       pf[c] = bf16x8{a[0], a[1], a[2], a[3], bq[0], bq[1], bq[2], bq[3]};
     }
     // O^T += V^T P^T: chunk c = keys 16c .. 16c+15 in the P^T register order
-    u32x2 v0raw[8], v1raw[8];  // [c * 4 + dt]: reads e = 0 and e = 1
-    lds_read_vt8<OFF>(vaddr[0][0], vaddr[0][1], vaddr[0][2], vaddr[0][3], v0raw);
-    lds_read_vt8<OFF>(vaddr[1][0], vaddr[1][1], vaddr[1][2], vaddr[1][3], v1raw);
+    const u32x2* v0raw = vraw;      // [c * 4 + dt]: reads e = 0
+    const u32x2* v1raw = vraw + 8;  // and e = 1
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -342,7 +366,8 @@ void prefill_d128_kernel(PrefillParams p) {
     stage_barrier();
   };
 
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < 3; ++pass) {
+    track = pass > 0;
     l = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -352,10 +377,9 @@ void prefill_d128_kernel(PrefillParams p) {
     // exist (a stage past the end stages rows of block 0 into a slot nobody
     // reads), so the number of loads behind the queries is fixed and the
     // compiler's wait for them is exact.
-    issue(0, 0);
-    issue(1, 1);
-    issue(2, 2);
-    wait_stages(2);  // stage 0
+#pragma unroll
+    for (int i = 0; i < kSlots - 1; ++i) issue(i, i);
+    wait_stages(kSlots - 2);  // stage 0
     stage_barrier();
     // Whole groups of 4 stages, so that the loop is left only at its end;
     // stages past the end only take the barrier.
@@ -375,9 +399,28 @@ void prefill_d128_kernel(PrefillParams p) {
     }
     // the max grew too far above the reference somewhere in the workgroup:
     // run the tile again with the true max as the reference
-    const bool far = (mt - m) * p.c1 > kHeadroom;
-    if (pass == 1 || !__syncthreads_or(far)) break;
-    m = mt;
+    // pass 0 does not know the true max: a weight above 2^64 shows as a
+    // partial row sum above 2^64 (or inf / NaN), and then pass 1 runs the
+    // tile again tracking the max; if that max grew too far above the
+    // reference, pass 2 uses it as the reference
+    const bool far = pass == 0 ? !(l <= 18446744073709551616.f) : (mt - m) * p.c1 > kHeadroom;
+    if (pass == 2) break;
+    // workgroup vote through the (now idle) ring: every load has landed and
+    // every wave is past the last barrier
+    int* vote = reinterpret_cast<int*>(ring);
+    if (tid == 0) *vote = 0;
+    __syncthreads();
+    if (far) *vote = 1;
+    __syncthreads();
+    const bool any = *vote != 0;
+    __syncthreads();  // every wave has read the vote before the ring is refilled
+    if (!any) break;
+    if (pass == 0) {
+      m = kNegInf;
+      mt = kNegInf;
+    } else {
+      m = mt;
+    }
   }
 
   // ---- output ------------------------------------------------------------

@@ -158,6 +158,29 @@ def test_prefill_nan_outside_window(lib):
     check_close(to_f64(o[0, rows]), ro, "nan-poison rows")
 
 
+@pytest.mark.parametrize("jump", [40.0, 60.0, 100.0])
+def test_prefill_reference_max_rerun(lib, jump):
+    """Scores jump by `jump` nats at block 3, far above the reference max the
+    kernel takes from the first keys it sees (block 0).  40: weights up to
+    2^58 -- their sums pass 2^64, so the tile is rerun once tracking the max,
+    and kept; 60: weights up to 2^87, rerun again with the true max; 100:
+    weights overflow fp32 on the first pass.  Every row must still match."""
+    B, L, H, D = 1, 1024, 2, 128
+    scale = 1.0 / math.sqrt(D)
+    g = torch.Generator().manual_seed(int(jump))
+    q = torch.ones((B, L, H, D)).bfloat16()
+    k = (0.05 * torch.randn((B, L, H, D), generator=g)).bfloat16()
+    k[:, 3 * 128:4 * 128] = jump / (D * scale)  # q.k * scale = jump (up to bf16 rounding)
+    v = torch.randn((B, L, H, D), generator=g).bfloat16()
+    say(f"prefill reference-max rerun jump={jump}")
+    o, lse = lib.ssa(q.cuda(), k.cuda(), v.cuda(), scale=scale, with_lse=True)
+    torch.cuda.synchronize()
+    f64 = lambda t: t.float().double().numpy()
+    ro, rl = oracle.ssa_attention(f64(q), f64(k), f64(v), scale)
+    check_close(to_f64(o), ro, f"rerun jump={jump} o")
+    check_close(to_f64(lse), rl, f"rerun jump={jump} lse")
+
+
 def test_prefill_deterministic(lib):
     B, L, H, D = 1, 4096, 4, 128
     _, q = gen(8, synth.Q, B, L, H, D)
