@@ -82,8 +82,9 @@ __global__ __launch_bounds__(kSumThreads) void block_sums_kernel(PageSelectParam
 // query block n and channels 8m + 2g, 8m + 2g + 1 for m = 0 .. D/8-1, so a
 // row's 4 lanes read 64 contiguous bytes per load).  Each query block keeps
 // a sorted list of its best top_m pages across the lanes of one wave; a
-// chunk's candidate enters only if it beats the list's last entry, by an
-// insertion at the rank a ballot gives.  "Beats" is a total order: higher
+// chunk's candidate enters only if it beats the list's last entry (and, on a
+// row's first chunk, is no worse than the M-th best of the lanes' bests), by
+// an insertion at the rank a ballot gives.  "Beats" is a total order: higher
 // score, equal scores -> lower page (a NaN score counts as -inf).
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 256;
@@ -173,12 +174,50 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(PageSelectParams p)
       if (c_hi - c_lo <= M) continue;  // every candidate is taken; no ranking
       double ts = read_lane_f64(ls[rr], M - 1);
       int tc = __builtin_amdgcn_readlane(li[rr], M - 1);
+      // While the list is not full (a row's first chunk), bound the chunk's
+      // M-th best from below by the M-th best of the 64 per-lane bests: an
+      // item worse than that bar is beaten by M items of the chunk and can be
+      // skipped.  The bar comes from a bitonic sort across the lanes.
+      double bs = -__builtin_inf();
+      int bc = 0x7fffffff;
+      if (tc == 0x7fffffff) {
+#pragma unroll
+        for (int k = 0; k < kChunk / 64; ++k) {
+          const int c = cc + 64 * k + lane;
+          double s = sc[wave + 4 * rr][64 * k + lane];
+          if (s != s) s = -__builtin_inf();
+          if (c >= c_lo && c < c_hi && better(s, c, bs, bc)) {
+            bs = s;
+            bc = c;
+          }
+        }
+        // sort the lane bests, best first: lane i ends with the i-th best
+#pragma unroll
+        for (int kk = 2; kk <= 64; kk <<= 1)
+#pragma unroll
+          for (int j = kk >> 1; j > 0; j >>= 1) {
+            const uint64_t u = __builtin_bit_cast(uint64_t, bs);
+            const uint32_t plo = __shfl_xor(static_cast<uint32_t>(u), j);
+            const uint32_t phi = __shfl_xor(static_cast<uint32_t>(u >> 32), j);
+            const double ps = __builtin_bit_cast(double, (static_cast<uint64_t>(phi) << 32) | plo);
+            const int pc = __shfl_xor(bc, j);
+            const bool keep_better = ((lane & kk) == 0) == ((lane & j) == 0);
+            if (keep_better ? better(ps, pc, bs, bc) : better(bs, bc, ps, pc)) {
+              bs = ps;
+              bc = pc;
+            }
+          }
+        const double b_s = read_lane_f64(bs, M - 1);
+        const int b_c = __builtin_amdgcn_readlane(bc, M - 1);
+        bs = b_s;
+        bc = b_c;
+      }
 #pragma unroll
       for (int k = 0; k < kChunk / 64; ++k) {
         const int c = cc + 64 * k + lane;
         double s = sc[wave + 4 * rr][64 * k + lane];
         if (s != s) s = -__builtin_inf();
-        bool q = c >= c_lo && c < c_hi && better(s, c, ts, tc);
+        bool q = c >= c_lo && c < c_hi && better(s, c, ts, tc) && !better(bs, bc, s, c);
         uint64_t mask = __builtin_amdgcn_ballot_w64(q);
         while (mask) {
           const int src = __builtin_ctzll(mask);
