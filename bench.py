@@ -221,8 +221,13 @@ def write_traffic(fetch_dir: str, write_dir: str, out_path: str):
     copy_w = [x for k, v in write.items() if "copy" in k.lower() for x in v.values()]
     fcal = copy_bytes / max(copy_f) if copy_f and max(copy_f) > 0 else 1.0
     wcal = copy_bytes / max(copy_w) if copy_w and max(copy_w) > 0 else 1.0
+    run = ("cd /tmp && rocprofv3 --pmc {c} --output-format csv -d <out>/pmc_{c} -o run -- python3 "
+           "/root/repo/bench.py --only prefill,decode,mla,copy --steps 2 --warmup 1 --no-cpu-baseline")
     lines = [f"# HBM bytes per launch: FETCH_SIZE * {fcal:.4f} + WRITE_SIZE * {wcal:.4f} (per dispatch, averaged);",
              "# factors = 1 GiB / the counter's reading on a plain 1 GiB device copy (bench.py --only copy).",
+             "# commands: " + run.format(c="FETCH_SIZE"),
+             "#           " + run.format(c="WRITE_SIZE"),
+             "#           python3 bench.py --write-traffic <out>/pmc_FETCH_SIZE <out>/pmc_WRITE_SIZE profiles/traffic.txt",
              "# key bytes_per_launch source_sha fetch_bytes write_bytes"]
     for key, (frags, fname) in KERNEL_SOURCES.items():
         fb, wb = pick(fetch, frags), pick(write, frags)
