@@ -78,6 +78,22 @@ def test_decode_small_nan_poisoned(lib, D, Hq, Hkv):
     run_and_check(lib, dev, host, 1 / math.sqrt(D), f"small D={D} Hq={Hq} Hkv={Hkv}")
 
 
+@pytest.mark.parametrize("win,D,Hq,Hkv", [((128, 2, 3), 128, 4, 2), ((128, 1, 15), 128, 2, 2),
+                                         ((128, 0, 6), 64, 3, 1), ((128, 4, 12), 64, 2, 1)])
+def test_decode_other_windows(lib, win, D, Hq, Hkv):
+    """Other window geometries; a 16-block window runs the 1024-thread
+    instantiation (one wave per block)."""
+    lens = [1, 130, 700, 2048, 2049, 3001]
+    w = oracle.Window(*win)
+    dev, host = build_case(23, len(lens), Hq, Hkv, D, lens, head=win[1], tail=win[2])
+    say(f"ssa_decode window={win} D={D} Hq={Hq} Hkv={Hkv}")
+    o, lse = lib.decode(dev["q"], dev["k"], dev["v"], dev["bt"], dev["sl"], window=lib.Window(*win), with_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(host["q"], host["k"], host["v"], host["bt"], host["sl"], 1 / math.sqrt(D), w)
+    check_close(to_f64(o), ro, f"decode window {win} o")
+    check_close(to_f64(lse), rl, f"decode window {win} lse")
+
+
 def test_decode_cfg3_full(lib):
     """Batch 64, 16/16 heads, d = 128, lengths uniform in [65536, 131072]."""
     lens = synth.decode_seq_lens(3, 64, 65536, 131072)

@@ -118,3 +118,19 @@ def test_mla_decode_reused_workspace_and_invalid_rows(lib):
     assert np.isnan(o2n[1:]).all() and np.isnan(l2.cpu().numpy()[1:]).all()
     check_close(to_f64(o2[0:1]), ro[0:1], "mla valid row beside invalid ones", rel=True)
     check_close(to_f64(l2[0:1]), rl[0:1], "mla valid row lse")
+
+
+@pytest.mark.parametrize("win", [(128, 2, 5), (128, 1, 11)])
+def test_mla_decode_other_windows(lib, win):
+    """The split kernel's grid and workspace follow the window width."""
+    lens = [1, 300, 2500]
+    w = oracle.Window(*win)
+    dev, host = build_case(84, len(lens), 32, 1, DQK, lens, mul=MUL, Dv=DV, share_kv=True, head=win[1], tail=win[2])
+    say(f"mla decode window={win}")
+    vv = dev["k"][..., :DV]
+    o, lse = lib.decode(dev["q"], dev["k"], vv, dev["bt"], dev["sl"], scale=SCALE, window=lib.Window(*win),
+                        with_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(host["q"], host["k"], host["k"][..., :DV], host["bt"], host["sl"], SCALE, w)
+    check_close(to_f64(o), ro, f"mla window {win} o", rel=True)
+    check_close(to_f64(lse), rl, f"mla window {win} lse")

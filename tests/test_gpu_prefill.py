@@ -80,6 +80,23 @@ def test_ssa_prefill_parity(lib, case):
     check_close(to_f64(lse), rl, f"{name} lse")
 
 
+@pytest.mark.parametrize("win,D", [((128, 0, 5), 128), ((128, 2, 3), 128), ((128, 3, 13), 128),
+                                   ((128, 2, 9), 64)])
+def test_ssa_prefill_other_windows(lib, win, D):
+    """Window geometries other than 1 global + 7 local blocks, through the
+    same kernels (list widths 5 to 16)."""
+    B, L, H = 1, 128 * 24 + 40, 2
+    qh, q = gen(13, synth.Q, B, L, H, D)
+    kh, k = gen(13, synth.K, B, L, H, D)
+    vh, v = gen(13, synth.V, B, L, H, D)
+    say(f"ssa_prefill window={win} D={D}")
+    o, lse = lib.ssa(q, k, v, window=lib.Window(*win), with_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.ssa_attention(qh.astype(np.float64), kh, vh, 1 / math.sqrt(D), oracle.Window(*win))
+    check_close(to_f64(o), ro, f"window {win} o")
+    check_close(to_f64(lse), rl, f"window {win} lse")
+
+
 def test_dense_causal_parity_small(lib):
     B, L, Hq, Hkv, D = 1, 1500, 2, 1, 128
     qh, q = gen(5, synth.Q, B, L, Hq, D)
