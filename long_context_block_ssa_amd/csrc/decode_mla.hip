@@ -10,21 +10,22 @@
 // cores.  A sequence's window is only ~1 MB and one CU moves only ~50-100
 // GB/s from memory, so the window is spread over all CUs and the pieces are
 // merged afterwards:
-//   - partial kernel: one workgroup per (sequence, 16 query heads, window
-//     block); its 4 waves split the channels: wave w owns value channels
-//     128w .. 128w+127 and, for the scores, those plus 16 of the 64 rope
+//   - partial kernel: one workgroup per (sequence, 16 or 32 query heads,
+//     window block); its 8 waves split the channels: wave w owns value
+//     channels 64w .. 64w+63 and, for the scores, those plus 8 of the 64 rope
 //     channels.  A wave loads its share of all 8 16-key steps of the block
-//     into registers at once (16 keys x 144 channels per step), so the whole
+//     into registers at once (16 keys x 72 channels per step), so the whole
 //     block is in flight from the start;
-//   - per step: partial S^T (16 keys x 16 heads) over the wave's channels on
+//   - partial S^T (16 keys x 16 heads) over the wave's channels on
 //     v_mfma_f32_16x16x32_bf16 (+ one 16x16x16 for the rope channels),
-//     straight from the loaded registers; the 4 partials are summed through
-//     LDS in a fixed order, so every wave holds the same scores and the same
-//     online-softmax state (m, l) per head; the wave's value tile goes to a
-//     wave-private LDS tile from which ds_read_b64_tr_b16 hands the V^T
-//     operand (4 keys of one channel per lane) of O^T += V^T P^T on
-//     v_mfma_f32_16x16x16_bf16;
-//   - each wave writes its 128 channels of the block's (o, m, l) per head, in
+//     straight from the loaded registers; the 8 partials go through LDS and
+//     wave w sums those of step w in a fixed order, so the scores do not
+//     depend on which wave sums them; a block holds only 128 keys, so the
+//     softmax is exact in two passes (block max, then P) with no rescale;
+//   - the wave's value tile goes to a wave-private LDS tile from which
+//     ds_read_b64_tr_b16 hands the V^T operand (4 keys of one channel per
+//     lane) of O^T += V^T P^T on v_mfma_f32_16x16x16_bf16;
+//   - each wave writes its 64 channels of the block's (o, m, l) per head, in
 //     fp32, to the workspace: no merge of output tiles inside the workgroup;
 //   - merge kernel: one workgroup per (sequence, head) combines the blocks:
 //     M = max m_t, o = sum o_t e^(m_t - M) / sum l_t e^(m_t - M), the exact
@@ -47,11 +48,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDqk = 576, kDv = 512;
 constexpr int kHeads = 16;             // query heads per workgroup (one MFMA tile)
-constexpr int kMWaves = 4;             // channel quarters
+constexpr int kMWaves = 8;             // channel eighths
 constexpr int kStep = 16;              // keys per step
 constexpr int kSteps = 128 / kStep;    // steps per block
-constexpr int kWaveCh = kDv / kMWaves;                 // 128 value channels per wave
-constexpr int kRopeCh = (kDqk - kDv) / kMWaves;        // 16 rope channels per wave
+constexpr int kWaveCh = kDv / kMWaves;                 // 64 value channels per wave
+constexpr int kRopeCh = (kDqk - kDv) / kMWaves;        // 8 rope channels per wave
+constexpr int kGroups = kWaveCh / 32;                  // 32-channel groups per wave
 constexpr int kMaxW = 16;              // window slots the merge kernel handles
 constexpr int kPart = kDv + 4;         // workspace floats per (sequence, head, window slot): o, m, l, pad
 constexpr float kNegInf = -__builtin_inff();
@@ -98,28 +100,38 @@ __device__ __forceinline__ T ldg(const __bf16* ptr) {
   return *(const SSA_GLB T*)(ptr);
 }
 
-// Partial kernel: grid (B * W * Hq/(16 HG)), 4 waves.  Each wave applies its
-// loaded channel slice to HG tiles of 16 heads, so a workgroup serves 16 HG
-// heads from one read of the block.  SHARED: the value is the first 512
-// channels of the latent row (one load serves both).
+// Partial kernel: grid (B * W * Hq/(16 HG)), 8 waves.  Each wave owns 64
+// value channels and 8 of the 64 rope channels, and applies them to HG tiles
+// of 16 heads, so a workgroup serves 16 HG heads from one read of the block.
+// SHARED: the value is the first 512 channels of the latent row (one load
+// serves both).
 //
-// A block holds only 128 keys, so the softmax takes two exact passes instead
-// of an online rescale: all partial scores of the block first (one LDS
-// exchange, one barrier), then the block max, then P and O^T += V^T P^T.
-// No accumulator is ever rescaled, which keeps the MFMA accumulators free of
-// vector arithmetic.
+// A block holds only 128 keys = 8 steps of 16, so the softmax takes two
+// exact passes instead of an online rescale, and its vector work is split by
+// step rather than repeated in every wave:
+//   1. each wave computes the partial S^T of all 8 steps over its channels;
+//   2. wave w sums the 8 partials of step w (a fixed order, so every step's
+//      scores are the same whoever sums them), masks them and publishes the
+//      step's max per head;
+//   3. wave w forms P of step w against the block max and publishes it (bf16)
+//      with its share of the row sum;
+//   4. every wave reads P of all steps and accumulates O^T = V^T P^T over its
+//      64 channels.
+// No accumulator is ever rescaled.
 template <bool SHARED, int HG>
-__global__ __launch_bounds__(kMWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kMWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_mla_partial_kernel(DecodeParams p) {
-  // steps loaded ahead: the whole block with a shared latent, three steps
-  // when the value rows are separate loads (register budget)
-  constexpr int DEPTH = SHARED ? kSteps : 3;
-  constexpr int NJ = kWaveCh / 16;
-  // dynamic LDS: partial scores [kSteps][HG][kMWaves][64] f32x4, then the
-  // per-wave value tiles [kMWaves][4 * 64] u32x4
+  static_assert(kSteps == kMWaves, "one step per wave in the softmax");
+  constexpr int NJ = kWaveCh / 16;  // 16-channel output tiles per wave
+  // dynamic LDS: partial scores sx [kSteps][HG][kMWaves][64] f32x4, value
+  // tiles [kMWaves][kGroups * 64] u32x4, P pb [kSteps][HG][64] bf16x4, step
+  // maxima mx [kSteps][HG][16] and row-sum parts ls [kSteps][HG][16] floats
   extern __shared__ f32x4 lds_dyn[];
   f32x4* sx = lds_dyn;
-  SSA_LDS u32x4* vtile = (SSA_LDS u32x4*)(lds_dyn + kSteps * HG * kMWaves * 64);
+  SSA_LDS u32x4* vtile = (SSA_LDS u32x4*)(sx + kSteps * HG * kMWaves * 64);
+  bf16x4* pbuf = reinterpret_cast<bf16x4*>(sx + kSteps * HG * kMWaves * 64 + kMWaves * kGroups * 64);
+  float* mxs = reinterpret_cast<float*>(pbuf + kSteps * HG * 64);
+  float* lsp = mxs + kSteps * HG * kHeads;
 
   const int W = p.n_global + p.n_local;
   // sequence fastest, then window slot, then head group: consecutive
@@ -131,17 +143,21 @@ void decode_mla_partial_kernel(DecodeParams p) {
   const int h0 = (blockIdx.x / (p.B * W)) * (kHeads * HG);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
+  const int ch0 = wave * kWaveCh;                 // this wave's value channels
+  const int rope0 = kDv + wave * kRopeCh + 4 * (g & 1);  // lanes g < 2 carry the rope slice
 
   // query fragments (B operand: lane (r, g) = head h0 + 16t + r, k-slice g),
-  // issued before the window lookup they do not depend on
-  bf16x8 qf[HG][4];
+  // issued before the window lookup they do not depend on; the rope operand
+  // has k-slices 0, 1 only (8 channels), slices 2, 3 are zero
+  bf16x8 qf[HG][kGroups];
   bf16x4 qr[HG];
 #pragma unroll
   for (int t = 0; t < HG; ++t) {
     const __bf16* qrow = static_cast<const __bf16*>(p.q) + b * p.qs_b + (h0 + kHeads * t + r) * p.qs_h;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qf[t][j] = ldg<bf16x8>(qrow + wave * kWaveCh + 32 * j + 8 * g);
-    qr[t] = ldg<bf16x4>(qrow + kDv + wave * kRopeCh + 4 * g);
+    for (int j = 0; j < kGroups; ++j) qf[t][j] = ldg<bf16x8>(qrow + ch0 + 32 * j + 8 * g);
+    qr[t] = ldg<bf16x4>(qrow + rope0);
+    if (g >= 2) qr[t] = bf16x4{};
   }
 
   const int n = p.seq_lens[b];
@@ -159,103 +175,103 @@ void decode_mla_partial_kernel(DecodeParams p) {
   }
   const int valid = min(128, n - blk * 128);  // keys of this block that exist, >= 1
 
-  // key rows (A operand: lane (r, g) = key r of the step, k-slice g).  Keys
-  // at or past `valid` are replaced by the last valid one: their scores are
-  // masked, and a masked zero weight times finite data stays zero inside the
-  // MFMA (times NaN it would not).  Every step is loaded and run, also past
-  // the last key of a partial block (fully masked, it adds nothing):
-  // branch-free code lets the compiler wait for exactly the loads each step
-  // uses instead of for all of them.
+  // key rows (A operand: lane (r, g) = key r of the step, k-slice g), all 8
+  // steps at once.  Keys at or past `valid` are replaced by the last valid
+  // one: their scores are masked, and a masked zero weight times finite data
+  // stays zero inside the MFMA (times NaN it would not).
   const __bf16* kpg = static_cast<const __bf16*>(p.k) + static_cast<int64_t>(page) * p.ks_p;
   const __bf16* vpg = static_cast<const __bf16*>(p.v) + static_cast<int64_t>(page) * p.vs_p;
-  bf16x8 kc[kSteps][4];
+  bf16x8 kc[kSteps][kGroups];
   bf16x4 kr[kSteps];
-  bf16x8 vc[SHARED ? 1 : kSteps][4];
-#define SSA_MLA_LOAD_K(S)                                                                      \
-  do {                                                                                         \
-    const int key_ = min((S) * kStep + r, valid - 1);                                          \
-    const __bf16* krow_ = kpg + static_cast<int64_t>(key_) * p.ks_s;                           \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) kc[S][j] =                                  \
-        ldg<bf16x8>(krow_ + wave * kWaveCh + 32 * j + 8 * g);                                  \
-    kr[S] = ldg<bf16x4>(krow_ + kDv + wave * kRopeCh + 4 * g);                                 \
-  } while (0)
-#define SSA_MLA_LOAD_V(S)                                                                      \
-  do {                                                                                         \
-    const int key_ = min((S) * kStep + r, valid - 1);                                          \
-    const __bf16* vrow_ = vpg + static_cast<int64_t>(key_) * p.vs_s;                           \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) vc[SHARED ? 0 : (S)][j] =                   \
-        ldg<bf16x8>(vrow_ + wave * kWaveCh + 32 * j + 8 * g);                                  \
-  } while (0)
+  bf16x8 vc[SHARED ? 1 : kSteps][kGroups];
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) SSA_MLA_LOAD_K(s);
-  if constexpr (!SHARED) {
+  for (int s = 0; s < kSteps; ++s) {
+    const int key = min(s * kStep + r, valid - 1);
+    const __bf16* krow = kpg + static_cast<int64_t>(key) * p.ks_s;
 #pragma unroll
-    for (int s = 0; s < DEPTH; ++s) SSA_MLA_LOAD_V(s);
+    for (int j = 0; j < kGroups; ++j) kc[s][j] = ldg<bf16x8>(krow + ch0 + 32 * j + 8 * g);
+    kr[s] = ldg<bf16x4>(krow + rope0);
+    if constexpr (!SHARED) {
+      const __bf16* vrow = vpg + static_cast<int64_t>(key) * p.vs_s;
+#pragma unroll
+      for (int j = 0; j < kGroups; ++j) vc[SHARED ? 0 : s][j] = ldg<bf16x8>(vrow + ch0 + 32 * j + 8 * g);
+    }
   }
 
-  // pass 1: partial S^T of every step over this wave's channels.  The rope
+  // 1. partial S^T of every step over this wave's channels.  The rope
   // product has its own accumulator: a 16x16x16 MFMA that takes a 16x16x32
   // result as its accumulator input a few instructions later has read a
-  // stale last register here, so chains stay within one opcode.
-  f32x4 part[kSteps][HG];
+  // stale last register, so chains stay within one opcode.
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s)
+  for (int s = 0; s < kSteps; ++s) {
+    const bf16x4 ks = g >= 2 ? bf16x4{} : kr[s];
 #pragma unroll
     for (int t = 0; t < HG; ++t) {
       f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[s][j], qf[t][j], a, 0, 0, 0);
+      for (int j = 0; j < kGroups; ++j) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[s][j], qf[t][j], a, 0, 0, 0);
       const f32x4 rope = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-          __builtin_bit_cast(s16x4, kr[s]), __builtin_bit_cast(s16x4, qr[t]), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      part[s][t] = a + rope;
-      sx[((s * HG + t) * kMWaves + wave) * 64 + lane] = part[s][t];
-    }
-  lds_barrier();
-  // full scores, summed in the same order by every wave; block max per head
-  float m[HG], l[HG];
-#pragma unroll
-  for (int t = 0; t < HG; ++t) m[t] = kNegInf;
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    const int kv = valid - s * kStep;  // keys of the step that exist (>= 1 for s = 0)
-#pragma unroll
-    for (int t = 0; t < HG; ++t) {
-      f32x4 sc4 = wave == 0 ? part[s][t] : sx[((s * HG + t) * kMWaves + 0) * 64 + lane];
-#pragma unroll
-      for (int w = 1; w < kMWaves; ++w) sc4 += wave == w ? part[s][t] : sx[((s * HG + t) * kMWaves + w) * 64 + lane];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (g * 4 + i >= kv) sc4[i] = kNegInf;
-      part[s][t] = sc4;
-      m[t] = fmaxf(m[t], fmaxf(fmaxf(sc4[0], sc4[1]), fmaxf(sc4[2], sc4[3])));
+          __builtin_bit_cast(s16x4, ks), __builtin_bit_cast(s16x4, qr[t]), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      sx[((s * HG + t) * kMWaves + wave) * 64 + lane] = a + rope;
     }
   }
-  bf16x4 pb[kSteps][HG];
+  lds_barrier();
+
+  // 2. step `wave`: full scores (the 8 partials in a fixed order), mask, max
+  const int s_own = wave;
+  const int kv = valid - s_own * kStep;  // keys of the step that exist (>= 1 for step 0)
+  f32x4 so[HG];
 #pragma unroll
   for (int t = 0; t < HG; ++t) {
-    m[t] = xlane_max(m[t]);  // finite: key 0 of step 0 exists
-    const float mc = m[t] * p.c1;
+    f32x4 v = sx[((s_own * HG + t) * kMWaves + 0) * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < kMWaves; ++w) v += sx[((s_own * HG + t) * kMWaves + w) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (g * 4 + i >= kv) v[i] = kNegInf;
+    so[t] = v;
+    const float mx = xlane_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+    if (g == 0) mxs[(s_own * HG + t) * kHeads + r] = mx;
+  }
+  lds_barrier();
+
+  // 3. block max per head, P of step `wave`, its share of the row sum
+  float m[HG];
+#pragma unroll
+  for (int t = 0; t < HG; ++t) {
+    float M = kNegInf;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) M = fmaxf(M, mxs[(s * HG + t) * kHeads + r]);
+    m[t] = M;  // finite: key 0 of step 0 exists
+    const float mc = M * p.c1;
+    f32x4 e;
     float rs = 0.f;
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      f32x4 e;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(part[s][t][i], p.c1, -mc));
-        rs += e[i];
-      }
-      pb[s][t] = __builtin_convertvector(e, bf16x4);
+    for (int i = 0; i < 4; ++i) {
+      e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(so[t][i], p.c1, -mc));
+      rs += e[i];
     }
-    l[t] = xlane_sum(rs);
+    rs = xlane_sum(rs);
+    pbuf[(s_own * HG + t) * 64 + lane] = __builtin_convertvector(e, bf16x4);
+    if (g == 0) lsp[(s_own * HG + t) * kHeads + r] = rs;
   }
+  lds_barrier();
 
-  // pass 2: O^T (128 channels x 16 heads) += V^T (128 x 16 keys) P^T (16 keys x 16 heads)
+  // 4. O^T (64 channels x 16 heads) += V^T (64 x 16 keys) P^T (16 keys x 16 heads)
+  float l[HG];
+#pragma unroll
+  for (int t = 0; t < HG; ++t) {
+    float v = 0.f;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) v += lsp[(s * HG + t) * kHeads + r];
+    l[t] = v;
+  }
   f32x4 acc[HG][NJ];
 #pragma unroll
   for (int t = 0; t < HG; ++t)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  SSA_LDS u32x4* vt = vtile + wave * 4 * 64;
+  SSA_LDS u32x4* vt = vtile + wave * kGroups * 64;
   const int wpos = 4 * r + (g ^ swz(r));
   // transposed read of output tile jt: key row 4g + r/4, channels
   // 16jt + 4(r mod 4) .. +3; the tr read then hands lane (r, g) channel
@@ -265,13 +281,14 @@ void decode_mla_partial_kernel(DecodeParams p) {
   const SSA_LDS char* vrd = (const SSA_LDS char*)(vt) + vrow * 64 + (r & 1) * 8;
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
-    if constexpr (!SHARED)
-      if (s + DEPTH < kSteps) SSA_MLA_LOAD_V(s + DEPTH < kSteps ? s + DEPTH : 0);
-    // value tile of this step (LDS is in order within a wave: the previous
+    // value tile of step s (LDS is in order within a wave: the previous
     // step's reads of the tile are done before these writes land)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kGroups; ++j)
       vt[j * 64 + wpos] = __builtin_bit_cast(u32x4, SHARED ? kc[s][j] : vc[SHARED ? 0 : s][j]);
+    bf16x4 pb[HG];
+#pragma unroll
+    for (int t = 0; t < HG; ++t) pb[t] = pbuf[(s * HG + t) * 64 + lane];
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) {
       const SSA_LDS char* a = vrd + (jt >> 1) * 1024 + (vpos ^ ((jt & 1) << 1)) * 16;
@@ -279,18 +296,16 @@ void decode_mla_partial_kernel(DecodeParams p) {
 #pragma unroll
       for (int t = 0; t < HG; ++t)
         acc[t][jt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vf),
-                                                                __builtin_bit_cast(s16x4, pb[s][t]), acc[t][jt], 0, 0, 0);
+                                                                __builtin_bit_cast(s16x4, pb[t]), acc[t][jt], 0, 0, 0);
     }
   }
-#undef SSA_MLA_LOAD_K
-#undef SSA_MLA_LOAD_V
 
-  // this wave's 128 channels of the block's (o, m, l)
+  // this wave's 64 channels of the block's (o, m, l)
 #pragma unroll
   for (int t = 0; t < HG; ++t) {
     float* oh = out + static_cast<int64_t>(kHeads * t + r) * W * kPart;
 #pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) *reinterpret_cast<f32x4*>(oh + wave * kWaveCh + jt * 16 + 4 * g) = acc[t][jt];
+    for (int jt = 0; jt < NJ; ++jt) *reinterpret_cast<f32x4*>(oh + ch0 + jt * 16 + 4 * g) = acc[t][jt];
     if (wave == 0 && g == 0) {
       oh[kDv] = m[t];
       oh[kDv + 1] = l[t];
@@ -359,7 +374,8 @@ template <bool SHARED, int HG>
 hipError_t launch_mla(const DecodeParams& p, hipStream_t stream) {
   const unsigned W = static_cast<unsigned>(p.n_global + p.n_local);
   const dim3 grid(static_cast<unsigned>(p.B) * W * static_cast<unsigned>(p.Hq / (kHeads * HG)));
-  const size_t lds = sizeof(f32x4) * kSteps * HG * kMWaves * 64 + sizeof(u32x4) * kMWaves * 4 * 64;
+  const size_t lds = sizeof(f32x4) * kSteps * HG * kMWaves * 64 + sizeof(u32x4) * kMWaves * kGroups * 64 +
+                     sizeof(bf16x4) * kSteps * HG * 64 + 2 * sizeof(float) * kSteps * HG * kHeads;
   auto kern = decode_mla_partial_kernel<SHARED, HG>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
