@@ -116,7 +116,9 @@ typedef struct ssa_block_lists {
  * window names a page outside [0, num_pages), gets an all-NaN output row (and
  * lse = NaN) and nothing out of range is read.
  * Supported (dtype, Dqk, Dv): (BF16, 64, 64), (BF16, 128, 128) with
- * Hq/Hkv <= 16, and (BF16, 576, 512) with Hkv == 1 and Hq a multiple of 16.
+ * Hq/Hkv <= 16 and a page's rows within 2^31 bytes of the page base
+ * (2 * (127 * slot stride + D) <= 2^31 - 1, else SSA_ERR_UNSUPPORTED), and
+ * (BF16, 576, 512) with Hkv == 1 and Hq a multiple of 16.
  * The (576, 512) shape splits every window over its blocks and keeps fp32
  * per-block partials in a caller-owned device workspace of at least
  * ssa_decode_workspace_size bytes, 256-byte aligned (SSA_ERR_WORKSPACE if it

@@ -3,6 +3,7 @@
 // contract of each entry point.
 #include "ssa.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -244,6 +245,12 @@ int ssa_decode(const ssa_decode_args* a, const ssa_window* win, void* stream) {
     return fail(SSA_ERR_UNSUPPORTED, "%s: no kernel for Dqk=%d Dv=%d Hq=%d Hkv=%d", who, a->Dqk, a->Dv, a->Hq,
                 a->Hkv);
   if (win->block_size != 128) return fail(SSA_ERR_UNSUPPORTED, "%s: block_size must be 128", who);
+  // the 64/128-wide kernel addresses a page's rows with 32-bit byte offsets
+  const int64_t row_span =
+      2 * (static_cast<int64_t>(win->block_size - 1) * std::max(a->k_stride[2], a->v_stride[2]) + a->Dqk);
+  if (mha && row_span > INT32_MAX)
+    return fail(SSA_ERR_UNSUPPORTED, "%s: slot strides (%lld, %lld) put a page's rows beyond 2^31 bytes", who,
+                static_cast<long long>(a->k_stride[2]), static_cast<long long>(a->v_stride[2]));
   const size_t need = ssa_decode_workspace_size(a, win);
   if (need > 0) {
     if (!a->workspace || a->workspace_bytes < need)

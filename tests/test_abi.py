@@ -147,6 +147,8 @@ def decode_args(**over):
     (dict(Dqk=576, Dv=512, Hkv=2), ssa.SSA_ERR_UNSUPPORTED),
     (dict(Hq=64, Hkv=2), ssa.SSA_ERR_UNSUPPORTED),
     (dict(k_stride=(ctypes.c_int64 * 3)(4 * 128 * 128, 128 * 128, 100)), ssa.SSA_ERR_INVALID),
+    # 127 slots of 2^24 elements: a page's rows span more than 2^31 bytes
+    (dict(v_stride=(ctypes.c_int64 * 3)(128 << 24, 128, 1 << 24)), ssa.SSA_ERR_UNSUPPORTED),
 ])
 def test_decode_rejects(lib, over, code):
     a = decode_args(**over)
