@@ -99,6 +99,12 @@ template <typename T>
 __device__ __forceinline__ T ldg(const __bf16* ptr) {
   return *(const SSA_GLB T*)(ptr);
 }
+// the latent block, read as a non-temporal stream (its other head groups
+// read it at about the same time)
+template <typename T>
+__device__ __forceinline__ T ldg_nt(const __bf16* ptr) {
+  return __builtin_nontemporal_load((const SSA_GLB T*)(ptr));
+}
 
 // Partial kernel: grid (B * W * Hq/(16 HG)), 8 waves.  Each wave owns 64
 // value channels and 8 of the 64 rope channels, and applies them to HG tiles
@@ -189,12 +195,12 @@ void decode_mla_partial_kernel(DecodeParams p) {
     const int key = min(s * kStep + r, valid - 1);
     const __bf16* krow = kpg + static_cast<int64_t>(key) * p.ks_s;
 #pragma unroll
-    for (int j = 0; j < kGroups; ++j) kc[s][j] = ldg<bf16x8>(krow + ch0 + 32 * j + 8 * g);
-    kr[s] = ldg<bf16x4>(krow + rope0);
+    for (int j = 0; j < kGroups; ++j) kc[s][j] = ldg_nt<bf16x8>(krow + ch0 + 32 * j + 8 * g);
+    kr[s] = ldg_nt<bf16x4>(krow + rope0);
     if constexpr (!SHARED) {
       const __bf16* vrow = vpg + static_cast<int64_t>(key) * p.vs_s;
 #pragma unroll
-      for (int j = 0; j < kGroups; ++j) vc[SHARED ? 0 : s][j] = ldg<bf16x8>(vrow + ch0 + 32 * j + 8 * g);
+      for (int j = 0; j < kGroups; ++j) vc[SHARED ? 0 : s][j] = ldg_nt<bf16x8>(vrow + ch0 + 32 * j + 8 * g);
     }
   }
 

@@ -11,7 +11,8 @@
 // Two kernels:
 //   1. block_sums: one workgroup per (b, head, block) of q and of k; fp64
 //      sums of 128 bf16 rows (exact for these inputs, so the order of the
-//      additions does not matter).  An HBM scan of q and k.
+//      additions does not matter).  An HBM scan of q and k with
+//      non-temporal loads.
 //   2. select: one workgroup per (b, query head, 16 query blocks); fp64
 //      scores of the candidate pages [n_global, qb - n_local] on the fp64
 //      matrix cores, top-M kept as a sorted per-row list (equal scores ->
@@ -27,8 +28,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kSumThreads = 256;
 
 // grid.x = B*Hq*nqb (q sums) + B*Hkv*nqb (k sums)
+template <int D>
 __global__ __launch_bounds__(kSumThreads) void block_sums_kernel(PageSelectParams p) {
-  const int D = p.D, CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int nrg = kSumThreads / CPR;     // row groups
+  constexpr int NR = 128 / nrg;              // rows per thread
   const int64_t nq = static_cast<int64_t>(p.B) * p.Hq * p.nqb;
   int64_t t = blockIdx.x;
   const bool is_q = t < nq;
@@ -42,18 +46,28 @@ __global__ __launch_bounds__(kSumThreads) void block_sums_kernel(PageSelectParam
   const int64_t sl = is_q ? p.qs_l : p.ks_l;
   double* out = (is_q ? p.qsum : p.ksum) + t * D;
 
-  const int cc = threadIdx.x % CPR, rg = threadIdx.x / CPR, nrg = kSumThreads / CPR;
+  const int cc = threadIdx.x % CPR, rg = threadIdx.x / CPR;
+  const int nrow = min(128, p.L - blk * 128);  // rows of this block, >= 1
+  // all of a thread's rows are loaded at once (a row past the last one reads
+  // the last again and is left out of the sum), as non-temporal loads: q and
+  // k are read once here
+  u32x4 v[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int row = blk * 128 + min(rg + nrg * i, nrow - 1);
+    v[i] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4*)(base + row * sl + cc * 8));
+  }
   double acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-  for (int r = rg; r < 128; r += nrg) {
-    const int row = blk * 128 + r;
-    if (row >= p.L) break;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(base + row * sl + cc * 8);
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    // a repeated row adds +0 (unconditionally, so that no load is sunk into a branch)
+    const u32x4 x = rg + nrg * i < nrow ? v[i] : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      acc[2 * w] += static_cast<double>(__builtin_bit_cast(float, v[w] << 16));
-      acc[2 * w + 1] += static_cast<double>(__builtin_bit_cast(float, v[w] & 0xFFFF0000u));
+      acc[2 * w] += static_cast<double>(__builtin_bit_cast(float, x[w] << 16));
+      acc[2 * w + 1] += static_cast<double>(__builtin_bit_cast(float, x[w] & 0xFFFF0000u));
     }
   }
   // reduce the nrg row groups: tree over LDS, 8 channels per thread
@@ -282,7 +296,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(PageSelectParams p)
 
 hipError_t launch_page_select(const PageSelectParams& p, hipStream_t stream) {
   const int64_t nsum = static_cast<int64_t>(p.B) * (p.Hq + p.Hkv) * p.nqb;
-  hipError_t e = launch_kernel(block_sums_kernel, dim3(static_cast<unsigned>(nsum)), dim3(kSumThreads), 0, stream, p);
+  hipError_t e = p.D == 128 ? launch_kernel(block_sums_kernel<128>, dim3(static_cast<unsigned>(nsum)), dim3(kSumThreads), 0, stream, p)
+               : p.D == 64  ? launch_kernel(block_sums_kernel<64>, dim3(static_cast<unsigned>(nsum)), dim3(kSumThreads), 0, stream, p)
+                            : hipErrorNotSupported;
   if (e != hipSuccess) return e;
   const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.Hq * ((p.nqb + kRows - 1) / kRows));
   if (p.D == 128) return launch_kernel(select_kernel<128>, dim3(grid), dim3(kSelThreads), 0, stream, p);
