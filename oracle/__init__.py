@@ -23,6 +23,9 @@ against the sources by eye:
   the comparison layer; written on its own, without the window code, so that
   "SSA equals dense when L <= 1024" is a real check.
 * ``decode`` -- one new query per sequence over a paged cache.
+* ``chunk_prefill`` -- a chunk of T new queries per sequence over a paged
+  cache, each with the window of its own block (the step between prefill and
+  decode: a long prompt prefilled in pieces).
 * ``block_sums`` / ``page_select`` / ``block_list_rows`` -- the page-selection
   variant (LongCat sparse attention article, section 3: streaming-aware
   indexing keeps sink + local window, hierarchical indexing scores 128-token
@@ -31,6 +34,7 @@ against the sources by eye:
 Parity status: every function here is pinned by the CPU tests (brute force on
 tiny inputs, the dense special case against torch's own attention routine,
 closed-form key counts, structural one-hot outputs, decode == last prefill row,
+chunked prefill == brute force over the cached sequence,
 exact rational re-scoring of page selections).  No function is "parity
 unpinned".
 """
@@ -45,6 +49,7 @@ from .ssa import (  # noqa: F401
     dense_causal_rows,
     dense_causal,
     decode,
+    chunk_prefill,
     block_sums,
     page_select,
     block_list_rows,

@@ -8,6 +8,7 @@
 * closed forms: block counts, keys per query, total pairs, lse of a zero query;
 * structural outputs: one-hot values per block, constant values, the first row;
 * decode of a sequence of length n == row n - 1 of the prefill on the same data;
+* a chunk of queries over a paged cache == brute force over the cached sequence;
 * page selection re-decided with exact rationals on tiny inputs.
 """
 import math
@@ -274,6 +275,63 @@ def test_decode_equals_prefill_last_row(n, Hq, Hkv):
     o_d, lse_d = oracle.decode(q[:, n - 1], kp, vp, bt, np.array([n]), 0.3)
     np.testing.assert_allclose(o_d[0], o_p[0, n - 1], rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(lse_d[0], lse_p[0, :, n - 1], rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill over a paged cache == brute force over the cached sequence
+# ---------------------------------------------------------------------------
+
+def _paged_kv(k_seq, v_seq, bs, rng, P_extra=5):
+    """Scatter one sequence's keys [n, H, D] and values [n, H, Dv] into NaN-filled
+    pages through one random table; returns pages and the table row."""
+    kp, perm = _paged(k_seq, bs, rng, P_extra)
+    n, H, Dv = v_seq.shape
+    vp = np.full((kp.shape[0], H, bs, Dv), np.nan)
+    for t in range((n + bs - 1) // bs):
+        rows = v_seq[t * bs:min((t + 1) * bs, n)]
+        vp[perm[t], :, :rows.shape[0]] = rows.transpose(1, 0, 2)
+    return kp, vp, perm
+
+
+@pytest.mark.parametrize("n,T,bs,ng,nl,Hq,Hkv", [
+    (37, 9, 4, 1, 3, 2, 1),    # chunk crosses two blocks, ragged end, GQA 2:1
+    (40, 40, 4, 1, 3, 1, 1),   # the whole sequence
+    (29, 1, 4, 2, 2, 2, 2),    # one query (a decode step), two global blocks
+    (33, 6, 4, 1, 3, 1, 1),    # chunk starts mid-block
+])
+def test_chunk_prefill_bruteforce_small(n, T, bs, ng, nl, Hq, Hkv):
+    rng = np.random.default_rng(1000 + n + T)
+    D, Dv = 3, 2
+    q = rng.standard_normal((1, n, Hq, D))
+    k = rng.standard_normal((1, n, Hkv, D))
+    v = rng.standard_normal((1, n, Hkv, Dv))
+    win = Window(bs, ng, nl)
+    kp, vp, perm = _paged_kv(k[0], v[0], bs, rng)
+    bt = np.full((1, len(perm) + 3), -1, np.int32)
+    bt[0, :len(perm)] = perm
+    o, lse = oracle.chunk_prefill(q[:, n - T:], kp, vp, bt, np.array([n]), 0.7, win)
+    ref = brute_rows(q, k, v, 0.7, range(n - T, n), lambda i: brute_window_keys(i, bs, ng, nl))
+    for (b, h, i), (ob, lb) in ref.items():
+        np.testing.assert_allclose(o[b, i - (n - T), h], ob, rtol=1e-12, atol=1e-12)
+        assert abs(lse[b, h, i - (n - T)] - lb) < 1e-12
+
+
+def test_chunk_prefill_bruteforce_real_geometry():
+    """128-token blocks, 1 + 7: a 700-query chunk ending at n = 2304 (it starts
+    mid-block and spans six query blocks); rows at every window edge."""
+    rng = np.random.default_rng(77)
+    n, T, D = 2304, 700, 2
+    q = rng.standard_normal((1, n, 1, D))
+    k = rng.standard_normal((1, n, 1, D))
+    v = rng.standard_normal((1, n, 1, D))
+    kp, vp, perm = _paged_kv(k[0], v[0], 128, rng)
+    bt = perm[None, :].astype(np.int32)
+    o, lse = oracle.chunk_prefill(q[:, n - T:], kp, vp, bt, np.array([n]), 1 / math.sqrt(D))
+    rows = [1604, 1605, 1663, 1664, 1791, 1792, 2047, 2048, 2175, 2176, 2303]
+    ref = brute_rows(q, k, v, 1 / math.sqrt(D), rows, lambda i: brute_window_keys(i, 128, 1, 7))
+    for (b, h, i), (ob, lb) in ref.items():
+        np.testing.assert_allclose(o[b, i - (n - T), h], ob, rtol=1e-11, atol=1e-12)
+        assert abs(lse[b, h, i - (n - T)] - lb) < 1e-11
 
 
 # ---------------------------------------------------------------------------
