@@ -11,6 +11,8 @@ One step = one pass over every row of the path on resident synthetic inputs:
   a5  dense causal layer     same tensors as a2 (the comparison layer)
   a6+a7 page selection       L=131072, H=16, d=128, M=8
   a8  page-selected prefill  over those lists
+  f1  chunked prefill        16 sequences at context ~ U[65536, 131072], the last 2048
+                             tokens of each as one chunk over the paged cache, H=16/16, d=128
 
 The headline value is the SSA prefill throughput (algorithmic TFLOP/s: 4*d per
 (query, key) pair the window admits) at the L=32768 workload; the decode GB/s
@@ -50,6 +52,7 @@ W2 = dict(B=1, L=32768, H=16, D=128, seed=2)
 W3 = dict(B=64, H=16, D=128, lo=65536, hi=131072, seed=3)
 W5 = dict(B=1, L=131072, H=16, D=128, M=8, seed=5)
 W4 = dict(L=262144, H=128, DQK=576, DV=512, seed=4, dec_B=8, dec_n=1048576, dec_rot=32)
+W6 = dict(B=16, T=2048, H=16, D=128, lo=65536, hi=131072, seed=6)
 
 
 def keys_ssa(i: int) -> int:
@@ -86,6 +89,11 @@ def dense_flops(L, H, D, B=1):
 
 def page_flops(L, H, D, M, B=1):
     return 4 * D * pairs(L, lambda i: keys_page(i, M)) * H * B
+
+
+def chunk_flops(lens, T, H, D):
+    """4*d per admitted pair over the last T positions of every sequence."""
+    return 4 * D * H * sum(keys_ssa(i) for n in lens for i in range(int(n) - T, int(n)))
 
 
 def decode_bytes(lens, Hq, Hkv, Dqk, Dv):
@@ -302,7 +310,7 @@ def main():
     ap.add_argument("--rotations", type=int, default=2, help="independent decode page sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=25.0)
-    ap.add_argument("--only", default="", help="comma list of rows to run (prefill,decode,dense,page,mla); "
+    ap.add_argument("--only", default="", help="comma list of rows to run (prefill,decode,dense,page,mla,chunk); "
                     "for profiling one kernel -- the JSON line is printed only for a full run")
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="summarise two rocprofv3 --pmc runs into a traffic file and exit")
@@ -338,7 +346,7 @@ def main():
         return t.to(dev)
 
     only = set(x for x in args.only.split(",") if x)
-    run = {name: (not only) or (name in only) for name in ("prefill", "decode", "dense", "page", "mla")}
+    run = {name: (not only) or (name in only) for name in ("prefill", "decode", "dense", "page", "mla", "chunk")}
     run["copy"] = "copy" in only  # calibration copy for the traffic counters, only on request
 
     print("[bench] generating inputs", flush=True)
@@ -409,10 +417,30 @@ def main():
         sl4 = torch.from_numpy(lens4).to(dev)
         o4d = torch.empty((B4d, H4, DV4), dtype=torch.bfloat16, device=dev)
         ws4 = torch.empty((ssa.decode_workspace_size(B4d, H4, DQ4, DV4) + 256,), dtype=torch.uint8, device=dev)
+    # f1 inputs: a compact pool holding only the pages the chunks read (block 0
+    # and the blocks from 6 before the chunk's first block to the end)
+    if run["chunk"]:
+        B6, T6, H6, D6, s6 = W6["B"], W6["T"], W6["H"], W6["D"], W6["seed"]
+        lens6 = synth.decode_seq_lens(s6, B6, W6["lo"], W6["hi"])
+        nblk6 = (lens6 + 127) // 128
+        bt6 = np.full((B6, int(nblk6.max())), -1, np.int32)
+        kh, vh = [], []
+        for b in range(B6):
+            need = sorted({0} | set(range(max(0, (int(lens6[b]) - T6) // 128 - 6), int(nblk6[b]))))
+            for t in need:
+                bt6[b, t] = len(kh)
+                kh.append(synth.page_chunk(s6, synth.K, b, t, H6, D6))
+                vh.append(synth.page_chunk(s6, synth.V, b, t, H6, D6))
+        kp6, vp6 = up(np.stack(kh), head_major=False), up(np.stack(vh), head_major=False)
+        q6 = up(synth.seq_tensor(s6, synth.Q, B6, T6, H6, D6), head_major=False)
+        o6 = torch.empty((B6, T6, H6, D6), dtype=torch.bfloat16, device=dev)
+        bt6d, sl6 = torch.from_numpy(bt6).to(dev), torch.from_numpy(lens6).to(dev)
+        idx6, cnt6 = ssa.block_index(bt6.shape[1], device=dev)
+        lists6 = ssa.lists_from_index(idx6, cnt6)
     torch.cuda.synchronize()
 
     rows = ["a1 block_index", "a2 ssa_prefill", "a3 ssa_decode", "a5 dense_causal", "a6-a7 page_select",
-            "a8 page_prefill", "a4 mla_prefill", "a4 mla_decode"]
+            "a8 page_prefill", "a4 mla_prefill", "a4 mla_decode", "f1 chunk_prefill"]
     nev = len(rows) + 1
 
     if run["copy"]:
@@ -450,6 +478,9 @@ def main():
             r4 = s % R4
             ssa.decode(q4d[r4], pool4, pool4[..., :DV4], bts4[r4], sl4, scale=1 / 24, out=o4d, workspace=ws4)
         mark(8)
+        if run["chunk"]:
+            ssa.prefill_chunk(q6, kp6, vp6, bt6d, sl6, lists6, out=o6)
+        mark(9)
         if run["copy"]:
             cp_dst.copy_(cp_src)
 
@@ -473,7 +504,7 @@ def main():
     if only:
         return
     for t, name in ((o2, "ssa"), (o3, "decode"), (od, "dense"), (o5, "page"), (o4[0, -128:], "mla"),
-                    (o4d, "mla decode")):
+                    (o4d, "mla decode"), (o6, "chunk")):
         if not torch.isfinite(t.float()).all():
             raise RuntimeError(f"non-finite {name} output")
 
@@ -512,6 +543,11 @@ def main():
     kernels["mla_decode"] = {"bound": "hbm", "achieved": b4 / (per_row[7] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                              "unit": "GB/s", "frac": b4 / (per_row[7] * 1e-3) / 1e9 / PEAK_HBM_GBS,
                              "traffic": traffic_for("mla_decode"), "us": per_row[7] * 1e3, "work": b4}
+    f6 = chunk_flops(lens6, T6, H6, D6)
+    kernels["chunk_prefill"] = {"bound": "mfma", "achieved": f6 / (per_row[8] * 1e-3) / 1e12,
+                                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                "frac": f6 / (per_row[8] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                "us": per_row[8] * 1e3, "work": f6}
     out = {
         "metric": "SSA prefill TFLOP/s (frac MFMA peak) + decode GB/s (frac HBM) at 128K ctx",
         "value": tf2,
@@ -529,7 +565,8 @@ def main():
             "workload": "SSA prefill B=1 H=16 d=128 L=32768 bf16 (value) + SSA decode batch 64 H=16/16 d=128 "
                         "ctx U[65536,131072] bf16 (decode) + dense causal (same shape) + page selection "
                         "L=131072 H=16 d=128 M=8 + latent-shared 576/512 x 128 heads: prefill L=262144, "
-                        "decode batch 8 at 1048576",
+                        "decode batch 8 at 1048576 + chunked prefill of the last 2048 tokens of 16 sequences "
+                        "at ctx U[65536,131072] over a paged cache",
             "prefill_tokens_per_s": L2 / t2,
             "decode_gbps": gb3,
             "decode_frac_hbm": gb3 / PEAK_HBM_GBS,

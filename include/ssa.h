@@ -195,6 +195,59 @@ int ssa_decode(const ssa_decode_args* a, const ssa_window* win, void* stream);
 size_t ssa_decode_workspace_size(const ssa_decode_args* a, const ssa_window* win);
 
 /* ---------------------------------------------------------------------------
+ * ssa_prefill_chunk -- chunked prefill over a paged cache: T new queries per
+ * sequence, at positions n_b - T .. n_b - 1, each reading the key blocks its
+ * row lists (row = the query's absolute block, position / 128) and keys
+ * j <= i.  With the lists of ssa_block_index this is the SSA window of the
+ * QbitAI report on LongCat LoZA applied to a cached sequence, so a long
+ * prompt can be prefilled in pieces (each piece's keys and values are
+ * appended to the cache first) with the same result as one ssa_prefill over
+ * the whole prompt.  Within the listed blocks the result is the masked
+ * softmax of equation (2) of the ZigZag page, section 2.1.
+ *
+ * Operands:
+ *   q [B, T, Hq, Dqk] -> o [B, T, Hq, Dv]  (strides for (b, t, h); channels
+ *     contiguous; o must not overlap any input)
+ *   k_pages, v_pages, block_table, bt_stride, num_pages, max_blocks,
+ *     page_size: as in ssa_decode_args (v may alias k)
+ *   seq_lens [B] int32: n_b, the cached length INCLUDING the chunk, whose keys
+ *     and values are already in the cache; query t sits at position n_b - T + t
+ *   lists: as for ssa_prefill, with n_qblocks >= max_blocks rows per (b, h),
+ *     indexed by absolute query block; entries < 0, > the row's block or past
+ *     the sequence are skipped
+ *   lse, when not NULL: fp32, contiguous [B, Hq, T]
+ * A sequence whose n_b lies outside [T, max_blocks * page_size] gets all-NaN
+ * output rows (and lse = NaN); so do the chunk's rows in a query block whose
+ * list names a block mapped to a page outside [0, num_pages), or in any block
+ * of a sequence whose block 0 is.  Nothing out of range is read.
+ * Supported: dtype BF16 with Dqk = Dv = 128, out_dtype BF16 or F32,
+ * page_size 128, Hq a multiple of Hkv, list width W <= 64; a page's rows
+ * within 2^31 bytes of its base.
+ * ------------------------------------------------------------------------- */
+typedef struct ssa_chunk_args {
+  int32_t dtype;     /* of q, k_pages, v_pages: BF16 */
+  int32_t out_dtype; /* of o: BF16 or F32        */
+  int32_t B, T, Hq, Hkv, Dqk, Dv;
+  int32_t page_size; /* 128 */
+  int32_t num_pages, max_blocks;
+  float scale;
+  const void* q;
+  const void* k_pages;
+  const void* v_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* o;
+  float* lse;
+  int64_t q_stride[3]; /* (b, t, h) element strides       */
+  int64_t k_stride[3]; /* (page, head, slot)              */
+  int64_t v_stride[3];
+  int64_t o_stride[3]; /* (b, t, h)                       */
+  int64_t bt_stride;   /* >= max_blocks when B > 1        */
+} ssa_chunk_args;
+
+int ssa_prefill_chunk(const ssa_chunk_args* a, const ssa_block_lists* lists, void* stream);
+
+/* ---------------------------------------------------------------------------
  * ssa_page_select -- block lists for the page-selected variant (LongCat
  * sparse attention article, section 3: streaming-aware indexing keeps the
  * sink and the local window; hierarchical indexing scores 128-token pages

@@ -28,7 +28,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 
 # every symbol include/ssa.h declares
 EXPORTS = (
-    "ssa_block_index", "ssa_block_index_seq", "ssa_prefill", "ssa_dense_causal", "ssa_decode",
+    "ssa_block_index", "ssa_block_index_seq", "ssa_prefill", "ssa_dense_causal", "ssa_prefill_chunk", "ssa_decode",
     "ssa_decode_workspace_size", "ssa_page_select", "ssa_page_select_workspace_size", "ssa_last_error", "ssa_version",
 )
 
@@ -86,6 +86,22 @@ class CDecodeArgs(ctypes.Structure):
     ]
 
 
+class CChunkArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("Dqk", ctypes.c_int32), ("Dv", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+        ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+        ("bt_stride", ctypes.c_int64),
+    ]
+
+
 @dataclass(frozen=True)
 class Window:
     """Window geometry; defaults = 1 global + 7 local blocks of 128 tokens."""
@@ -120,6 +136,7 @@ def load(path: str = LIB_PATH):
     lib.ssa_block_index_seq.argtypes = [ctypes.POINTER(CWindow), vp, i32, vp, vp, vp]
     lib.ssa_prefill.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CBlockLists), vp]
     lib.ssa_dense_causal.argtypes = [ctypes.POINTER(CAttnArgs), vp]
+    lib.ssa_prefill_chunk.argtypes = [ctypes.POINTER(CChunkArgs), ctypes.POINTER(CBlockLists), vp]
     lib.ssa_decode.argtypes = [ctypes.POINTER(CDecodeArgs), ctypes.POINTER(CWindow), vp]
     lib.ssa_decode_workspace_size.argtypes = [ctypes.POINTER(CDecodeArgs), ctypes.POINTER(CWindow)]
     lib.ssa_decode_workspace_size.restype = ctypes.c_size_t
@@ -130,7 +147,7 @@ def load(path: str = LIB_PATH):
     lib.ssa_last_error.restype = ctypes.c_char_p
     lib.ssa_last_error.argtypes = []
     lib.ssa_version.argtypes = []
-    for name in ("ssa_block_index", "ssa_block_index_seq", "ssa_prefill", "ssa_dense_causal",
+    for name in ("ssa_block_index", "ssa_block_index_seq", "ssa_prefill", "ssa_dense_causal", "ssa_prefill_chunk",
                  "ssa_decode", "ssa_page_select", "ssa_version"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -272,6 +289,37 @@ def dense_causal(q, k, v, scale=None, out=None, out_dtype=None, with_lse=False, 
         lse = lse if lse is not None else lse2
     a = _attn_args(q, k, v, out, lse, scale)
     _check(lib.ssa_dense_causal(ctypes.byref(a), _stream(stream)))
+    return out, lse
+
+
+def prefill_chunk(q, k_pages, v_pages, block_table, seq_lens, lists: CBlockLists, scale=None, out=None,
+                  out_dtype=None, with_lse=False, lse=None, stream=None):
+    """ssa_prefill_chunk: q [B, T, Hq, D] = the last T positions of each cached
+    sequence (seq_lens counts them).  Returns (o [B, T, Hq, Dv], lse [B, Hq, T] or None)."""
+    lib = load()
+    B, T, Hq, Dqk = q.shape
+    P, Hkv, page, _ = k_pages.shape
+    Dv = v_pages.shape[3]
+    if out is None:
+        out = torch.empty((B, T, Hq, Dv), dtype=out_dtype or q.dtype, device=q.device)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    for t, name in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (out, "o")):
+        if t.stride(-1) != 1:
+            raise SSAError(SSA_ERR_INVALID, f"{name} channel dimension must be contiguous")
+    a = CChunkArgs()
+    a.dtype, a.out_dtype = _dtype_code(q.dtype), _dtype_code(out.dtype)
+    a.B, a.T, a.Hq, a.Hkv, a.Dqk, a.Dv = B, T, Hq, Hkv, Dqk, Dv
+    a.page_size, a.num_pages, a.max_blocks = page, P, block_table.shape[1]
+    a.scale = float(1.0 / math.sqrt(Dqk) if scale is None else scale)
+    a.q, a.k_pages, a.v_pages = _ptr(q), _ptr(k_pages), _ptr(v_pages)
+    a.block_table, a.seq_lens, a.o, a.lse = _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse)
+    a.q_stride = (ctypes.c_int64 * 3)(q.stride(0), q.stride(1), q.stride(2))
+    a.k_stride = (ctypes.c_int64 * 3)(k_pages.stride(0), k_pages.stride(1), k_pages.stride(2))
+    a.v_stride = (ctypes.c_int64 * 3)(v_pages.stride(0), v_pages.stride(1), v_pages.stride(2))
+    a.o_stride = (ctypes.c_int64 * 3)(out.stride(0), out.stride(1), out.stride(2))
+    a.bt_stride = block_table.stride(0)
+    _check(lib.ssa_prefill_chunk(ctypes.byref(a), ctypes.byref(lists), _stream(stream)))
     return out, lse
 
 

@@ -203,6 +203,99 @@ int ssa_dense_causal(const ssa_attn_args* a, void* stream) {
   return device_status(e, who);
 }
 
+int ssa_prefill_chunk(const ssa_chunk_args* a, const ssa_block_lists* lists, void* stream) {
+  const char* who = "ssa_prefill_chunk";
+  if (!a) return fail(SSA_ERR_INVALID, "%s: args is NULL", who);
+  if (a->dtype != SSA_DTYPE_F32 && a->dtype != SSA_DTYPE_BF16)
+    return fail(SSA_ERR_INVALID, "%s: dtype %d is not an ssa_dtype", who, a->dtype);
+  if (a->out_dtype != SSA_DTYPE_F32 && a->out_dtype != SSA_DTYPE_BF16)
+    return fail(SSA_ERR_INVALID, "%s: out_dtype %d is not an ssa_dtype", who, a->out_dtype);
+  if (a->B < 1 || a->T < 1 || a->Hq < 1 || a->Hkv < 1 || a->Dqk < 1 || a->Dv < 1 || a->num_pages < 1 ||
+      a->max_blocks < 1)
+    return fail(SSA_ERR_INVALID, "%s: sizes B=%d T=%d Hq=%d Hkv=%d Dqk=%d Dv=%d num_pages=%d max_blocks=%d must be >= 1",
+                who, a->B, a->T, a->Hq, a->Hkv, a->Dqk, a->Dv, a->num_pages, a->max_blocks);
+  if (a->Hq % a->Hkv != 0) return fail(SSA_ERR_INVALID, "%s: Hq=%d is not a multiple of Hkv=%d", who, a->Hq, a->Hkv);
+  if (a->page_size != 128) return fail(SSA_ERR_INVALID, "%s: page_size=%d must be 128", who, a->page_size);
+  if (static_cast<int64_t>(a->max_blocks) * 128 > INT32_MAX)
+    return fail(SSA_ERR_INVALID, "%s: max_blocks=%d is too large", who, a->max_blocks);
+  if (a->T > a->max_blocks * 128)
+    return fail(SSA_ERR_INVALID, "%s: T=%d exceeds max_blocks * 128", who, a->T);
+  if (!(std::isfinite(a->scale) && a->scale > 0.f))
+    return fail(SSA_ERR_INVALID, "%s: scale %g must be finite and > 0", who, static_cast<double>(a->scale));
+  if (!a->q || !a->k_pages || !a->v_pages || !a->block_table || !a->seq_lens || !a->o)
+    return fail(SSA_ERR_INVALID, "%s: q, k_pages, v_pages, block_table, seq_lens and o must be non-NULL", who);
+  if (!aligned(a->q, 16) || !aligned(a->k_pages, 16) || !aligned(a->v_pages, 16) || !aligned(a->o, 16))
+    return fail(SSA_ERR_INVALID, "%s: q, k_pages, v_pages and o must be 16-byte aligned", who);
+  if (!aligned(a->block_table, 4) || !aligned(a->seq_lens, 4) || (a->lse && !aligned(a->lse, 4)))
+    return fail(SSA_ERR_INVALID, "%s: block_table, seq_lens and lse must be 4-byte aligned", who);
+  const size_t es = elem_size(a->dtype), eo = elem_size(a->out_dtype);
+  if (!valid_strides(a->q_stride, es, who, "q") || !valid_strides(a->k_stride, es, who, "k") ||
+      !valid_strides(a->v_stride, es, who, "v") || !valid_strides(a->o_stride, eo, who, "o"))
+    return SSA_ERR_INVALID;
+  if (a->B > 1 && a->bt_stride < a->max_blocks)
+    return fail(SSA_ERR_INVALID, "%s: bt_stride=%lld < max_blocks=%d", who, static_cast<long long>(a->bt_stride),
+                a->max_blocks);
+  if (!lists) return fail(SSA_ERR_INVALID, "%s: lists is NULL", who);
+  if (!lists->idx || !lists->cnt) return fail(SSA_ERR_INVALID, "%s: lists idx/cnt must be non-NULL", who);
+  if (!aligned(lists->idx, 4) || !aligned(lists->cnt, 4))
+    return fail(SSA_ERR_INVALID, "%s: lists idx/cnt must be 4-byte aligned", who);
+  if (lists->W < 1 || lists->W > 64) return fail(SSA_ERR_INVALID, "%s: list width W=%d not in [1, 64]", who, lists->W);
+  if (lists->n_qblocks < a->max_blocks)
+    return fail(SSA_ERR_INVALID, "%s: lists hold %d rows per head, max_blocks=%d needs as many", who,
+                lists->n_qblocks, a->max_blocks);
+  if (lists->idx_sb < 0 || lists->idx_sh < 0 || lists->cnt_sb < 0 || lists->cnt_sh < 0)
+    return fail(SSA_ERR_INVALID, "%s: list strides must be >= 0", who);
+  if (!(a->dtype == SSA_DTYPE_BF16 && a->Dqk == 128 && a->Dv == 128))
+    return fail(SSA_ERR_UNSUPPORTED, "%s: no kernel for dtype=%d Dqk=%d Dv=%d (BF16, 128, 128 only)", who, a->dtype,
+                a->Dqk, a->Dv);
+  // rows of a page are addressed with 32-bit offsets from the page base
+  const int64_t row_span = 2 * (127 * std::max(a->k_stride[2], a->v_stride[2]) + a->Dqk);
+  if (row_span > INT32_MAX)
+    return fail(SSA_ERR_UNSUPPORTED, "%s: slot strides (%lld, %lld) put a page's rows beyond 2^31 bytes", who,
+                static_cast<long long>(a->k_stride[2]), static_cast<long long>(a->v_stride[2]));
+  ssa::ChunkParams p{};
+  p.q = a->q;
+  p.k = a->k_pages;
+  p.v = a->v_pages;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.qs_b = a->q_stride[0];
+  p.qs_l = a->q_stride[1];
+  p.qs_h = a->q_stride[2];
+  p.ks_b = a->k_stride[0];
+  p.ks_h = a->k_stride[1];
+  p.ks_l = a->k_stride[2];
+  p.vs_b = a->v_stride[0];
+  p.vs_h = a->v_stride[1];
+  p.vs_l = a->v_stride[2];
+  p.os_b = a->o_stride[0];
+  p.os_l = a->o_stride[1];
+  p.os_h = a->o_stride[2];
+  p.B = a->B;
+  p.L = 0;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.group = a->Hq / a->Hkv;
+  p.nqb = static_cast<int32_t>(ceil_div(a->T, 128) + 1);  // query-block tiles a chunk can touch
+  p.scale = a->scale;
+  p.c1 = static_cast<float>(static_cast<double>(a->scale) * 1.4426950408889634);
+  p.idx = lists->idx;
+  p.cnt = lists->cnt;
+  p.W = lists->W;
+  p.dense = 0;
+  p.idx_sb = lists->idx_sb;
+  p.idx_sh = lists->idx_sh;
+  p.cnt_sb = lists->cnt_sb;
+  p.cnt_sh = lists->cnt_sh;
+  p.block_table = a->block_table;
+  p.seq_lens = a->seq_lens;
+  p.bt_stride = a->bt_stride;
+  p.T = a->T;
+  p.num_pages = a->num_pages;
+  p.max_len = a->max_blocks * 128;
+  return device_status(ssa::launch_prefill_chunk_d128(p, a->out_dtype == SSA_DTYPE_F32, as_stream(stream)), who);
+}
+
 size_t ssa_decode_workspace_size(const ssa_decode_args* a, const ssa_window* win) {
   if (!a || !win || a->B < 1 || a->Hq < 1 || win->n_global < 0 || win->n_local < 0) return 0;
   if (!(a->Dqk == 576 && a->Dv == 512)) return 0;

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <tuple>
+#include <type_traits>
 #include <utility>
 
 namespace ssa {
@@ -48,6 +49,16 @@ struct PrefillParams {
   int32_t W;
   int32_t dense;
   int64_t idx_sb, idx_sh, cnt_sb, cnt_sh;
+};
+
+// Chunked prefill over a paged cache: the k/v strides (ks_b, ks_h, ks_l) are
+// (page, head, slot); nqb counts query-block tiles per (b, h); the chunk of
+// sequence b is positions seq_lens[b] - T .. seq_lens[b] - 1; L is unused.
+struct ChunkParams : PrefillParams {
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int64_t bt_stride;
+  int32_t T, num_pages, max_len;
 };
 
 struct DecodeParams {
@@ -102,6 +113,8 @@ hipError_t launch_prefill_wide(const PrefillParams& p, int dqk, int dv, bool out
 // bf16, Dqk = Dv = 128: 32 queries per wave, two waves per SIMD
 bool prefill_d128_supports(const PrefillParams& p, int dqk, int dv);
 hipError_t launch_prefill_d128(const PrefillParams& p, bool out_f32, hipStream_t stream);
+// chunked prefill over a paged cache, bf16, Dqk = Dv = 128
+hipError_t launch_prefill_chunk_d128(const ChunkParams& p, bool out_f32, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeParams& p, int dqk, int dv, hipStream_t stream);
 

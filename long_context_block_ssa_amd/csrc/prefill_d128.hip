@@ -165,9 +165,17 @@ __device__ __forceinline__ void store4<__bf16>(__bf16* dst, f32x4 v) {
   *reinterpret_cast<bf16x4*>(dst) = __builtin_convertvector(v, bf16x4);
 }
 
-template <typename OutT, bool DENSE>
+// PAGED: chunked prefill over a paged cache.  The workgroup's tile is query
+// block q0/128 + tile of the chunk q0 .. n-1 (q0 = n - T); a key block lives
+// in page block_table[b][block]; queries and outputs are indexed by position
+// - q0.  Everything else is the kernel above with L = n.
+template <bool PAGED>
+using KernelParams = std::conditional_t<PAGED, ChunkParams, PrefillParams>;
+
+template <typename OutT, bool DENSE, bool PAGED>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_d128_kernel(PrefillParams p) {
+void prefill_d128_kernel(KernelParams<PAGED> p) {
+  static_assert(!(DENSE && PAGED), "no dense layer over a paged cache");
   __shared__ u32x4 ring[kSlots * kSlotBytes / 16];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -177,15 +185,43 @@ void prefill_d128_kernel(PrefillParams p) {
   // tile order: query blocks last to first (the dense layer's longest rows
   // first), then batch, heads fastest
   const int bh_count = p.B * p.Hq;
-  const int qb = p.nqb - 1 - static_cast<int>(blockIdx.x) / bh_count;
+  const int tile = p.nqb - 1 - static_cast<int>(blockIdx.x) / bh_count;
   const int bh = static_cast<int>(blockIdx.x) % bh_count;
   const int b = bh / p.Hq, h = bh % p.Hq;
   const int hk = h / p.group;
   const int qoff = wave * 32;  // this wave's first query inside the block
 
+  // a chunk row that cannot be computed: NaN output and lse
+  auto nan_row = [&](int t) {
+    if constexpr (PAGED) {
+      OutT* obase = static_cast<OutT*>(p.o) + b * p.os_b + h * p.os_h;
+      const float nan = __builtin_nanf("");
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          store4<OutT>(obase + t * p.os_l + 32 * dt + 8 * k + 4 * h32, f32x4{nan, nan, nan, nan});
+      if (p.lse && h32 == 0) p.lse[(static_cast<int64_t>(b) * p.Hq + h) * p.T + t] = nan;
+    }
+  };
+  int L = p.L, q0 = 0, qb = tile, nkb = p.nqb;  // keys [0, L); first query q0; key blocks [0, nkb)
+  if constexpr (PAGED) {
+    const int n = p.seq_lens[b];
+    if (n < p.T || n > p.max_len) {  // no valid chunk: NaN rows tile*128 .. of this (b, h)
+      const int t = tile * kBlk + qoff + c32;
+      if (t < p.T) nan_row(t);
+      return;
+    }
+    L = n;
+    q0 = n - p.T;
+    qb = q0 / kBlk + tile;
+    nkb = (n + kBlk - 1) / kBlk;
+    if (qb >= nkb) return;  // past the chunk's last block
+  }
+
   const __bf16* qbase = static_cast<const __bf16*>(p.q) + b * p.qs_b + h * p.qs_h;
-  const __bf16* kbase = static_cast<const __bf16*>(p.k) + b * p.ks_b + hk * p.ks_h;
-  const __bf16* vbase = static_cast<const __bf16*>(p.v) + b * p.vs_b + hk * p.vs_h;
+  const __bf16* kbase = static_cast<const __bf16*>(p.k) + (PAGED ? 0 : b * p.ks_b) + hk * p.ks_h;
+  const __bf16* vbase = static_cast<const __bf16*>(p.v) + (PAGED ? 0 : b * p.vs_b) + hk * p.vs_h;
 
   // ---- the block list, read once into registers (entry i on lane i of
   // every wave, fetched with readlane): a global read inside the stage loop
@@ -197,7 +233,22 @@ void prefill_d128_kernel(PrefillParams p) {
     nblk = min(p.cnt[b * p.cnt_sb + h * p.cnt_sh + qb], p.W);
     const int32_t* list = p.idx + b * p.idx_sb + h * p.idx_sh + static_cast<int64_t>(qb) * p.W;
     const int kb = lane < nblk ? list[lane] : -1;
-    blane = (kb < 0 || kb > qb || kb >= p.nqb) ? -1 : kb;
+    blane = (kb < 0 || kb > qb || kb >= nkb) ? -1 : kb;
+  }
+  // PAGED: page of list entry i on lane i (block 0's page for a skipped
+  // entry, which stages rows nobody reads); a listed page or block 0's page
+  // outside the pool makes every row of the tile NaN
+  int plane = 0, page0 = 0;
+  if constexpr (PAGED) {
+    const int32_t* bt = p.block_table + b * p.bt_stride;
+    page0 = bt[0];
+    plane = blane >= 0 ? bt[blane] : page0;
+    const bool bad = plane < 0 || plane >= p.num_pages || page0 < 0 || page0 >= p.num_pages;
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+      const int row = qb * kBlk + qoff + c32;
+      if (row >= q0 && row < L) nan_row(row - q0);
+      return;
+    }
   }
   const int nst = nblk * (kBlk / kSK);
   // block of stage s; -1 for a skipped list entry and for stages past the end
@@ -245,7 +296,7 @@ void prefill_d128_kernel(PrefillParams p) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       u32x4 v = {0, 0, 0, 0};
-      if (row < p.L) v = *reinterpret_cast<const u32x4*>(qbase + row * p.qs_l + c * 16 + h32 * 8);
+      if (row >= q0 && row < L) v = *reinterpret_cast<const u32x4*>(qbase + (row - q0) * p.qs_l + c * 16 + h32 * 8);
       qf[c] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -257,26 +308,52 @@ void prefill_d128_kernel(PrefillParams p) {
 
   // ---- staging: this wave's four loads of stage s into ring slot `slot` ---
   auto issue = [&](int s, int slot) {
-    const int kb = max(stage_block(s), 0);  // skipped entries stage block 0 (unused)
-    const int key0 = kb * kBlk + (s & 3) * kSK;
     SSA_LDS u32x4* kd = (SSA_LDS u32x4*)(ring) + slot * (kSlotBytes / 16) + wave * 64;
     SSA_LDS u32x4* vd = kd + kSlab;
 #define SSA_DMA(src, dst) \
   __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(src), (SSA_LDS void*)(dst), 16, 0, 0)
-    if (key0 + kSK <= p.L) {
-      const __bf16* ks = kbase + static_cast<int64_t>(key0) * p.ks_l + koff;
-      const __bf16* vs = vbase + static_cast<int64_t>(key0) * p.vs_l + voff;
-      SSA_DMA(ks, kd);
-      SSA_DMA(ks + k16, kd + 256);
-      SSA_DMA(vs, vd);
-      SSA_DMA(vs + v16, vd + 256);
+    if constexpr (PAGED) {
+      // block kb lives in its page: rows r0 .. r0+31 of the page
+      const int sb = stage_block(s);
+      const int kb = max(sb, 0);  // skipped entries stage block 0 (unused)
+      const int pg = sb >= 0 ? __builtin_amdgcn_readlane(plane, s >> 2) : page0;
+      const __bf16* kpg = kbase + static_cast<int64_t>(pg) * p.ks_b;
+      const __bf16* vpg = vbase + static_cast<int64_t>(pg) * p.vs_b;
+      const int r0 = (s & 3) * kSK;
+      if (kb * kBlk + r0 + kSK <= L) {
+        const __bf16* ks = kpg + static_cast<int64_t>(r0) * p.ks_l + koff;
+        const __bf16* vs = vpg + static_cast<int64_t>(r0) * p.vs_l + voff;
+        SSA_DMA(ks, kd);
+        SSA_DMA(ks + k16, kd + 256);
+        SSA_DMA(vs, vd);
+        SSA_DMA(vs + v16, vd + 256);
+      } else {
+        // the sequence's last block: rows at or past n repeat row n-1
+        const int last = L - 1 - kb * kBlk;
+        const int64_t ra = min(r0 + drow, last), rb = min(r0 + drow + 16, last);
+        SSA_DMA(kpg + ra * p.ks_l + dunit * 8, kd);
+        SSA_DMA(kpg + rb * p.ks_l + dunit * 8, kd + 256);
+        SSA_DMA(vpg + ra * p.vs_l + dunit * 8, vd);
+        SSA_DMA(vpg + rb * p.vs_l + dunit * 8, vd + 256);
+      }
     } else {
-      // last block of a ragged L: rows at or past L repeat row L-1 (finite, masked later)
-      const int64_t r0 = min(key0 + drow, p.L - 1), r1 = min(key0 + drow + 16, p.L - 1);
-      SSA_DMA(kbase + r0 * p.ks_l + dunit * 8, kd);
-      SSA_DMA(kbase + r1 * p.ks_l + dunit * 8, kd + 256);
-      SSA_DMA(vbase + r0 * p.vs_l + dunit * 8, vd);
-      SSA_DMA(vbase + r1 * p.vs_l + dunit * 8, vd + 256);
+      const int kb = max(stage_block(s), 0);  // skipped entries stage block 0 (unused)
+      const int key0 = kb * kBlk + (s & 3) * kSK;
+      if (key0 + kSK <= p.L) {
+        const __bf16* ks = kbase + static_cast<int64_t>(key0) * p.ks_l + koff;
+        const __bf16* vs = vbase + static_cast<int64_t>(key0) * p.vs_l + voff;
+        SSA_DMA(ks, kd);
+        SSA_DMA(ks + k16, kd + 256);
+        SSA_DMA(vs, vd);
+        SSA_DMA(vs + v16, vd + 256);
+      } else {
+        // last block of a ragged L: rows at or past L repeat row L-1 (finite, masked later)
+        const int64_t r0 = min(key0 + drow, p.L - 1), r1 = min(key0 + drow + 16, p.L - 1);
+        SSA_DMA(kbase + r0 * p.ks_l + dunit * 8, kd);
+        SSA_DMA(kbase + r1 * p.ks_l + dunit * 8, kd + 256);
+        SSA_DMA(vbase + r0 * p.vs_l + dunit * 8, vd);
+        SSA_DMA(vbase + r1 * p.vs_l + dunit * 8, vd + 256);
+      }
     }
 #undef SSA_DMA
   };
@@ -289,7 +366,7 @@ void prefill_d128_kernel(PrefillParams p) {
     const int kb = stage_block(s);
     const int sub = s & 3;
     const int key0 = kb * kBlk + sub * kSK;
-    const bool need = kb >= 0 && key0 < p.L && !(kb == qb && sub * kSK > qoff + 31);
+    const bool need = kb >= 0 && key0 < L && !(kb == qb && sub * kSK > qoff + 31);
     if (ns < nst) issue(ns, nslot);
     if (!need) return;
     // S^T = K Q^T: 32 keys x 32 queries
@@ -307,9 +384,9 @@ void prefill_d128_kernel(PrefillParams p) {
     u32x2 vraw[16];
     lds_read_vt16<OFF>(vaddr, vraw);
     // own block: key > query; keys at or past L
-    if (kb == qb || key0 + kSK > p.L) {
+    if (kb == qb || key0 + kSK > L) {
       const int qi = qb * kBlk + qoff + c32;
-      const int lim = min(qi, p.L - 1) - key0 - 4 * h32;  // last valid key offset
+      const int lim = min(qi, L - 1) - key0 - 4 * h32;  // last valid key offset
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (8 * (i >> 2) + (i & 3) > lim) sc[i] = kNegInf;
@@ -427,25 +504,28 @@ void prefill_d128_kernel(PrefillParams p) {
   OutT* obase = static_cast<OutT*>(p.o) + b * p.os_b + h * p.os_h;
   const float lt = pair_sum(l);
   const int row = qb * kBlk + qoff + c32;
-  if (row >= p.L) return;
+  if (row < q0 || row >= L) return;
+  const int t = row - q0;  // output row (the position itself unless PAGED)
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const f32x4 v = {acc[dt][4 * k], acc[dt][4 * k + 1], acc[dt][4 * k + 2], acc[dt][4 * k + 3]};
-      store4<OutT>(obase + row * p.os_l + 32 * dt + 8 * k + 4 * h32, v * inv);
+      store4<OutT>(obase + t * p.os_l + 32 * dt + 8 * k + 4 * h32, v * inv);
     }
   if (p.lse && h32 == 0) {
     const float v = lt > 0.f ? m * p.scale + __builtin_amdgcn_logf(lt) * kLn2 : kNegInf;
-    p.lse[(static_cast<int64_t>(b) * p.Hq + h) * p.L + row] = v;
+    int64_t rows = p.L;  // lse row length: L, or the chunk length T
+    if constexpr (PAGED) rows = p.T;
+    p.lse[(static_cast<int64_t>(b) * p.Hq + h) * rows + t] = v;
   }
 }
 
-template <typename OutT, bool DENSE>
-hipError_t launch_d128(const PrefillParams& p, hipStream_t stream) {
+template <typename OutT, bool DENSE, bool PAGED = false>
+hipError_t launch_d128(const KernelParams<PAGED>& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.nqb) * p.B * p.Hq);
-  return launch_kernel(prefill_d128_kernel<OutT, DENSE>, grid, dim3(kWaves * 64), 0, stream, p);
+  return launch_kernel(prefill_d128_kernel<OutT, DENSE, PAGED>, grid, dim3(kWaves * 64), 0, stream, p);
 }
 
 }  // namespace
@@ -457,6 +537,11 @@ bool prefill_d128_supports(const PrefillParams& p, int dqk, int dv) {
 hipError_t launch_prefill_d128(const PrefillParams& p, bool out_f32, hipStream_t stream) {
   if (p.dense) return out_f32 ? launch_d128<float, true>(p, stream) : launch_d128<__bf16, true>(p, stream);
   return out_f32 ? launch_d128<float, false>(p, stream) : launch_d128<__bf16, false>(p, stream);
+}
+
+hipError_t launch_prefill_chunk_d128(const ChunkParams& p, bool out_f32, hipStream_t stream) {
+  if (p.W > kMaxW) return hipErrorNotSupported;
+  return out_f32 ? launch_d128<float, false, true>(p, stream) : launch_d128<__bf16, false, true>(p, stream);
 }
 
 }  // namespace ssa

@@ -223,7 +223,7 @@ def chunk_prefill(q, k_pages, v_pages, block_table, seq_lens, scale, win: Window
     b (n = seq_lens[b], which counts the chunk; the chunk's keys and values are
     already in the cache); k_pages / v_pages / block_table as for ``decode``.
     Each query i reads the window of its own block and keys j <= i: the same
-    rule as ``ssa_attention``, applied to the cached sequence.
+    rule as ``ssa_rows``, with the keys gathered from the pages.
     Returns o [B, T, Hq, Dv], lse [B, Hq, T] (rows of ``batches`` only, if given).
     """
     B, T, Hq, _ = q.shape
@@ -233,28 +233,23 @@ def chunk_prefill(q, k_pages, v_pages, block_table, seq_lens, scale, win: Window
     batches = range(B) if batches is None else batches
     o = np.full((B, T, Hq, v_pages.shape[3]), np.nan)
     lse = np.full((B, Hq, T), np.nan)
-    heads = list(range(Hq))
     for b in batches:
         n = int(seq_lens[b])
         q0 = n - T
-        # the cached sequence [n, Hkv, D], gathered page by page (blocks the
-        # chunk cannot read stay NaN)
-        nblk = (n + bs - 1) // bs
-        need = sorted({t for qb in range(q0 // bs, nblk) for t in window_blocks(qb, win)})
-        k_seq = np.full((n, Hkv, k_pages.shape[3]), np.nan)
-        v_seq = np.full((n, Hkv, v_pages.shape[3]), np.nan)
-        for t in need:
-            page = int(block_table[b, t])
-            r0, r1 = t * bs, min((t + 1) * bs, n)
-            k_seq[r0:r1] = np.asarray(k_pages[page, :, :r1 - r0], np.float64).transpose(1, 0, 2)
-            v_seq[r0:r1] = np.asarray(v_pages[page, :, :r1 - r0], np.float64).transpose(1, 0, 2)
-        for r0 in range(q0, n):
-            if r0 != q0 and r0 % bs != 0:
-                continue
-            r1 = min((r0 // bs + 1) * bs, n)
-            ob, lb = ssa_rows(q[b, r0 - q0:r1 - q0], r0, k_seq, v_seq, scale, heads, Hq, win)
-            o[b, r0 - q0:r1 - q0] = ob
-            lse[b, :, r0 - q0:r1 - q0] = lb.T
+        for qb in range(q0 // bs, (n - 1) // bs + 1):
+            r0, r1 = max(q0, qb * bs), min(n, (qb + 1) * bs)  # the chunk's rows in this block
+            blocks = window_blocks(qb, win)
+            pos = np.concatenate([np.arange(t * bs, min((t + 1) * bs, n)) for t in blocks])
+            allowed = pos[None, :] <= np.arange(r0, r1)[:, None]
+            for h in range(Hq):
+                g = _kv_head(h, Hq, Hkv)
+                kr = np.concatenate([np.asarray(k_pages[int(block_table[b, t]), g, :min(bs, n - t * bs)], np.float64)
+                                     for t in blocks])
+                vr = np.concatenate([np.asarray(v_pages[int(block_table[b, t]), g, :min(bs, n - t * bs)], np.float64)
+                                     for t in blocks])
+                ob, lb = _attend(np.asarray(q[b, r0 - q0:r1 - q0, h], np.float64), kr, vr, allowed, scale)
+                o[b, r0 - q0:r1 - q0, h] = ob
+                lse[b, h, r0 - q0:r1 - q0] = lb
     return o, lse
 
 

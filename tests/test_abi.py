@@ -174,6 +174,57 @@ def mla_decode_args(**over):
     return decode_args(**base)
 
 
+def chunk_args(**over):
+    a = ssa.CChunkArgs()
+    a.dtype = a.out_dtype = ssa.DTYPE_BF16
+    a.B, a.T, a.Hq, a.Hkv, a.Dqk, a.Dv = 2, 300, 4, 2, 128, 128
+    a.page_size, a.num_pages, a.max_blocks = 128, 40, 16
+    a.scale = 0.088
+    a.q = a.k_pages = a.v_pages = FAKE
+    a.o = FAKE + 4096
+    a.block_table = a.seq_lens = FAKE
+    a.q_stride = (ctypes.c_int64 * 3)(300 * 4 * 128, 4 * 128, 128)
+    a.k_stride = (ctypes.c_int64 * 3)(2 * 128 * 128, 128 * 128, 128)
+    a.v_stride = (ctypes.c_int64 * 3)(2 * 128 * 128, 128 * 128, 128)
+    a.o_stride = (ctypes.c_int64 * 3)(300 * 4 * 128, 4 * 128, 128)
+    a.bt_stride = 16
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a
+
+
+def chunk_lists(**over):
+    ls = ssa.CBlockLists()
+    ls.idx, ls.cnt, ls.W, ls.n_qblocks = FAKE, FAKE, 8, 16
+    for key, val in over.items():
+        setattr(ls, key, val)
+    return ls
+
+
+@pytest.mark.parametrize("over,lover,code", [
+    (dict(T=0), {}, ssa.SSA_ERR_INVALID),
+    (dict(T=16 * 128 + 1), {}, ssa.SSA_ERR_INVALID),      # longer than any cached sequence
+    (dict(page_size=64), {}, ssa.SSA_ERR_INVALID),
+    (dict(Hq=5), {}, ssa.SSA_ERR_INVALID),
+    (dict(bt_stride=15), {}, ssa.SSA_ERR_INVALID),
+    (dict(seq_lens=None), {}, ssa.SSA_ERR_INVALID),
+    (dict(scale=float("nan")), {}, ssa.SSA_ERR_INVALID),
+    (dict(q=FAKE + 8), {}, ssa.SSA_ERR_INVALID),           # alignment
+    ({}, dict(n_qblocks=15), ssa.SSA_ERR_INVALID),          # rows must cover every block of max_blocks
+    ({}, dict(W=65), ssa.SSA_ERR_INVALID),
+    ({}, dict(idx=None), ssa.SSA_ERR_INVALID),
+    (dict(Dqk=64, Dv=64), {}, ssa.SSA_ERR_UNSUPPORTED),
+    (dict(dtype=ssa.DTYPE_F32, out_dtype=ssa.DTYPE_F32), {}, ssa.SSA_ERR_UNSUPPORTED),
+    (dict(k_stride=(ctypes.c_int64 * 3)(128 << 24, 128, 1 << 24)), {}, ssa.SSA_ERR_UNSUPPORTED),
+])
+def test_prefill_chunk_rejects(lib, over, lover, code):
+    a = chunk_args(**over)
+    assert lib.ssa_prefill_chunk(ctypes.byref(a), ctypes.byref(chunk_lists(**lover)), None) == code
+    assert lib.ssa_last_error().decode() != ""
+    assert lib.ssa_prefill_chunk(None, ctypes.byref(chunk_lists()), None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_prefill_chunk(ctypes.byref(chunk_args()), None, None) == ssa.SSA_ERR_INVALID
+
+
 def test_decode_workspace_size(lib):
     w = ssa.CWindow(128, 1, 7)
     a = mla_decode_args()
