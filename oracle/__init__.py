@@ -19,6 +19,10 @@ against the sources by eye:
   section 2.1, equations (1) and (2); section 2.2.1 for the causal rule j <= i),
   computed with the row maximum subtracted before exp (CSA/HCA tutorial page,
   section 7.1, stable softmax).
+* ``ssa_backward`` -- gradients of ``ssa_attention`` with respect to q, k and v,
+  written out by the chain rule through o = P v and the softmax (the sparse
+  operator has a custom deterministic backward in training: LongCat sparse
+  attention article, section 4).
 * ``dense_causal_rows`` / ``dense_causal`` -- the full causal attention used as
   the comparison layer; written on its own, without the window code, so that
   "SSA equals dense when L <= 1024" is a real check.
@@ -34,7 +38,8 @@ against the sources by eye:
 Parity status: every function here is pinned by the CPU tests (brute force on
 tiny inputs, the dense special case against torch's own attention routine,
 closed-form key counts, structural one-hot outputs, decode == last prefill row,
-chunked prefill == brute force over the cached sequence,
+chunked prefill == brute force over the cached sequence, gradients == central
+finite differences of the forward and == torch autograd with an explicit mask,
 exact rational re-scoring of page selections).  No function is "parity
 unpinned".
 """
@@ -46,6 +51,7 @@ from .ssa import (  # noqa: F401
     block_index_seq,
     ssa_rows,
     ssa_attention,
+    ssa_backward,
     dense_causal_rows,
     dense_causal,
     decode,

@@ -176,6 +176,48 @@ def dense_causal(q, k, v, scale, chunk: int = 128):
     return o, lse
 
 
+def ssa_backward(q, k, v, do, scale, win: Window = DEFAULT_WINDOW):
+    """Gradients of the SSA output with respect to q, k and v.
+
+    For one query block and head, with P = softmax of the masked scaled scores
+    (the forward above) and dO the incoming gradient of its output rows:
+      dV += P^T dO ;  dP = dO V^T ;  dS = P * (dP - rowsum(P * dP)) ;
+      dQ  = scale * dS K ;  dK += scale * dS^T Q
+    -- the chain rule through o = P v and the softmax (whose Jacobian is
+    diag(p) - p p^T).  Keys are summed over every query block and query head
+    that reads them (the window's inverse map; a kv head serves Hq / Hkv query
+    heads).  The sparse operator is part of training (LongCat sparse attention
+    article, section 4: a custom, deterministic forward and backward).
+    Returns dq [B, L, Hq, Dqk], dk [B, L, Hkv, Dqk], dv [B, L, Hkv, Dv].
+    """
+    B, L, Hq, Dqk = q.shape
+    Hkv, Dv = k.shape[2], v.shape[3]
+    bs = win.block_size
+    dq = np.zeros((B, L, Hq, Dqk))
+    dk = np.zeros((B, L, Hkv, Dqk))
+    dv = np.zeros((B, L, Hkv, Dv))
+    for b in range(B):
+        for r0 in range(0, L, bs):
+            r1 = min(r0 + bs, L)
+            pos = np.concatenate([np.arange(t * bs, min((t + 1) * bs, L)) for t in window_blocks(r0 // bs, win)])
+            allowed = pos[None, :] <= np.arange(r0, r1)[:, None]
+            for h in range(Hq):
+                g = _kv_head(h, Hq, Hkv)
+                qr = np.asarray(q[b, r0:r1, h], np.float64)
+                kr = np.asarray(k[b, pos, g], np.float64)
+                vr = np.asarray(v[b, pos, g], np.float64)
+                dor = np.asarray(do[b, r0:r1, h], np.float64)
+                s = np.where(allowed, scale * (qr @ kr.T), -np.inf)
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                dp = dor @ vr.T
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[b, r0:r1, h] = scale * (ds @ kr)
+                np.add.at(dk[b, :, g], pos, scale * (ds.T @ qr))
+                np.add.at(dv[b, :, g], pos, p.T @ dor)
+    return dq, dk, dv
+
+
 # ---------------------------------------------------------------------------
 # decode over a paged cache
 # ---------------------------------------------------------------------------

@@ -9,6 +9,8 @@
 * structural outputs: one-hot values per block, constant values, the first row;
 * decode of a sequence of length n == row n - 1 of the prefill on the same data;
 * a chunk of queries over a paged cache == brute force over the cached sequence;
+* gradients == central finite differences of the forward on tiny inputs, and ==
+  torch's autograd through an explicitly masked softmax at the real window;
 * page selection re-decided with exact rationals on tiny inputs.
 """
 import math
@@ -332,6 +334,67 @@ def test_chunk_prefill_bruteforce_real_geometry():
     for (b, h, i), (ob, lb) in ref.items():
         np.testing.assert_allclose(o[b, i - (n - T), h], ob, rtol=1e-11, atol=1e-12)
         assert abs(lse[b, h, i - (n - T)] - lb) < 1e-11
+
+
+# ---------------------------------------------------------------------------
+# backward: central finite differences of the (pinned) forward, and torch's
+# autograd through an explicitly masked softmax attention
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("L,bs,ng,nl,Hq,Hkv", [
+    (13, 4, 1, 3, 2, 1),   # ragged, GQA 2:1: a kv head sums both query heads
+    (16, 4, 2, 2, 1, 1),   # two global blocks
+])
+def test_backward_finite_differences(L, bs, ng, nl, Hq, Hkv):
+    rng = np.random.default_rng(500 + L)
+    D, Dv, scale = 3, 2, 0.6
+    win = Window(bs, ng, nl)
+    q = rng.standard_normal((1, L, Hq, D))
+    k = rng.standard_normal((1, L, Hkv, D))
+    v = rng.standard_normal((1, L, Hkv, Dv))
+    g = rng.standard_normal((1, L, Hq, Dv))  # loss = sum(o * g), so dO = g
+
+    def loss(q_, k_, v_):
+        return float((oracle.ssa_attention(q_, k_, v_, scale, win)[0] * g).sum())
+
+    dq, dk, dv = oracle.ssa_backward(q, k, v, g, scale, win)
+    eps = 1e-6
+    for x, grad, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - grad[idx]) < 1e-7 * max(1.0, abs(fd)), (which, idx, fd, grad[idx])
+
+
+def test_backward_matches_torch_autograd_walked_mask():
+    """Real window at L = 1300 (block 0 read by every query block, local blocks
+    by the next 7), GQA 2:1, against torch autograd in float64."""
+    L, D, Hq, Hkv = 1300, 8, 2, 1
+    rng = np.random.default_rng(901)
+    q = rng.standard_normal((1, L, Hq, D))
+    k = rng.standard_normal((1, L, Hkv, D))
+    v = rng.standard_normal((1, L, Hkv, D))
+    g = rng.standard_normal((1, L, Hq, D))
+    mask = np.zeros((L, L), bool)
+    for i in range(L):
+        mask[i, brute_window_keys(i, 128, 1, 7)] = True
+    tq, tk, tv = (torch.tensor(x[0], dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    m = torch.tensor(mask)
+    out = []
+    for h in range(Hq):
+        s = (tq[:, h] @ tk[:, 0].T) * 0.3
+        p = torch.softmax(s.masked_fill(~m, float("-inf")), dim=-1)
+        out.append(p @ tv[:, 0])
+    (torch.stack(out, dim=1) * torch.tensor(g[0])).sum().backward()
+    dq, dk, dv = oracle.ssa_backward(q, k, v, g, 0.3)
+    np.testing.assert_allclose(dq[0], tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk[0], tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv[0], tv.grad.numpy(), rtol=1e-10, atol=1e-12)
 
 
 # ---------------------------------------------------------------------------
