@@ -13,6 +13,8 @@ One step = one pass over every row of the path on resident synthetic inputs:
   a8  page-selected prefill  over those lists
   f1  chunked prefill        16 sequences at context ~ U[65536, 131072], the last 2048
                              tokens of each as one chunk over the paged cache, H=16/16, d=128
+  f3  SSA backward           dq, dk, dv of the a2 prefill (its output and lse computed once
+                             outside the timed region; dout ~ N(0,1))
 
 The headline value is the SSA prefill throughput (algorithmic TFLOP/s: 4*d per
 (query, key) pair the window admits) at the L=32768 workload; the decode GB/s
@@ -94,6 +96,11 @@ def page_flops(L, H, D, M, B=1):
 def chunk_flops(lens, T, H, D):
     """4*d per admitted pair over the last T positions of every sequence."""
     return 4 * D * H * sum(keys_ssa(i) for n in lens for i in range(int(n) - T, int(n)))
+
+
+def bwd_flops(L, H, D, B=1):
+    """5 products of 2*d flops per admitted pair: S recomputed, dP, dV, dQ, dK."""
+    return 10 * D * pairs(L, keys_ssa) * H * B
 
 
 def decode_bytes(lens, Hq, Hkv, Dqk, Dv):
@@ -310,7 +317,7 @@ def main():
     ap.add_argument("--rotations", type=int, default=2, help="independent decode page sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=25.0)
-    ap.add_argument("--only", default="", help="comma list of rows to run (prefill,decode,dense,page,mla,chunk); "
+    ap.add_argument("--only", default="", help="comma list of rows to run (prefill,decode,dense,page,mla,chunk,bwd); "
                     "for profiling one kernel -- the JSON line is printed only for a full run")
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="summarise two rocprofv3 --pmc runs into a traffic file and exit")
@@ -346,14 +353,14 @@ def main():
         return t.to(dev)
 
     only = set(x for x in args.only.split(",") if x)
-    run = {name: (not only) or (name in only) for name in ("prefill", "decode", "dense", "page", "mla", "chunk")}
+    run = {name: (not only) or (name in only) for name in ("prefill", "decode", "dense", "page", "mla", "chunk", "bwd")}
     run["copy"] = "copy" in only  # calibration copy for the traffic counters, only on request
 
     print("[bench] generating inputs", flush=True)
     # a2 / a5 inputs
     L2, H2, D2, s2 = W2["L"], W2["H"], W2["D"], W2["seed"]
     nqb2 = L2 // 128
-    if run["prefill"] or run["dense"]:
+    if run["prefill"] or run["dense"] or run["bwd"]:
         q2, k2, v2 = (up(synth.seq_tensor(s2, t, 1, L2, H2, D2)) for t in (synth.Q, synth.K, synth.V))
         o2 = torch.empty((1, H2, L2, D2), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
         od = torch.empty_like(o2)
@@ -437,10 +444,18 @@ def main():
         bt6d, sl6 = torch.from_numpy(bt6).to(dev), torch.from_numpy(lens6).to(dev)
         idx6, cnt6 = ssa.block_index(bt6.shape[1], device=dev)
         lists6 = ssa.lists_from_index(idx6, cnt6)
+    # f3 inputs: the a2 forward's output and lse, an incoming gradient
+    if run["bwd"]:
+        lists2 = ssa.lists_from_index(*ssa.block_index(nqb2, device=dev))
+        ob, lseb = ssa.prefill(q2, k2, v2, lists2, with_lse=True)
+        gb = up(synth.seq_tensor(s2, 90, 1, L2, H2, D2))
+        dqb, dkb, dvb = (torch.empty((1, H2, L2, D2), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
+                         for _ in range(3))
+        wsb = torch.empty((ssa.prefill_backward_workspace_size(q2, k2) + 256,), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     rows = ["a1 block_index", "a2 ssa_prefill", "a3 ssa_decode", "a5 dense_causal", "a6-a7 page_select",
-            "a8 page_prefill", "a4 mla_prefill", "a4 mla_decode", "f1 chunk_prefill"]
+            "a8 page_prefill", "a4 mla_prefill", "a4 mla_decode", "f1 chunk_prefill", "f3 ssa_backward"]
     nev = len(rows) + 1
 
     if run["copy"]:
@@ -481,6 +496,9 @@ def main():
         if run["chunk"]:
             ssa.prefill_chunk(q6, kp6, vp6, bt6d, sl6, lists6, out=o6)
         mark(9)
+        if run["bwd"]:
+            ssa.prefill_backward(q2, k2, v2, ob, gb, lseb, dq=dqb, dk=dkb, dv=dvb, workspace=wsb)
+        mark(10)
         if run["copy"]:
             cp_dst.copy_(cp_src)
 
@@ -504,7 +522,7 @@ def main():
     if only:
         return
     for t, name in ((o2, "ssa"), (o3, "decode"), (od, "dense"), (o5, "page"), (o4[0, -128:], "mla"),
-                    (o4d, "mla decode"), (o6, "chunk")):
+                    (o4d, "mla decode"), (o6, "chunk"), (dqb, "dq"), (dkb, "dk"), (dvb, "dv")):
         if not torch.isfinite(t.float()).all():
             raise RuntimeError(f"non-finite {name} output")
 
@@ -548,6 +566,11 @@ def main():
                                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                 "frac": f6 / (per_row[8] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                 "us": per_row[8] * 1e3, "work": f6}
+    fb = bwd_flops(L2, H2, D2)
+    kernels["ssa_backward"] = {"bound": "mfma", "achieved": fb / (per_row[9] * 1e-3) / 1e12,
+                               "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                               "frac": fb / (per_row[9] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                               "us": per_row[9] * 1e3, "work": fb}
     out = {
         "metric": "SSA prefill TFLOP/s (frac MFMA peak) + decode GB/s (frac HBM) at 128K ctx",
         "value": tf2,
@@ -566,7 +589,7 @@ def main():
                         "ctx U[65536,131072] bf16 (decode) + dense causal (same shape) + page selection "
                         "L=131072 H=16 d=128 M=8 + latent-shared 576/512 x 128 heads: prefill L=262144, "
                         "decode batch 8 at 1048576 + chunked prefill of the last 2048 tokens of 16 sequences "
-                        "at ctx U[65536,131072] over a paged cache",
+                        "at ctx U[65536,131072] over a paged cache + SSA backward of the prefill workload",
             "prefill_tokens_per_s": L2 / t2,
             "decode_gbps": gb3,
             "decode_frac_hbm": gb3 / PEAK_HBM_GBS,

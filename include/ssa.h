@@ -195,6 +195,58 @@ int ssa_decode(const ssa_decode_args* a, const ssa_window* win, void* stream);
 size_t ssa_decode_workspace_size(const ssa_decode_args* a, const ssa_window* win);
 
 /* ---------------------------------------------------------------------------
+ * ssa_prefill_backward -- gradients of the SSA prefill output with respect to
+ * q, k and v, for training: LoZA converts layers in mid-training (QbitAI
+ * report on LongCat LoZA), and the sparse operator needs its own
+ * deterministic backward (LongCat sparse attention article, section 4).
+ * With P the masked softmax of the forward (recomputed from its lse) and dO
+ * the incoming gradient of o:
+ *   dV = P^T dO,  dP = dO V^T,  dS = P (dP - rowsum(dO * O)),
+ *   dQ = scale dS K,  dK = scale dS^T Q,
+ * summed over every query block and query head that reads a key (the
+ * window's inverse map).  Bitwise deterministic (no atomics).
+ *
+ * Operands (logical [B, L, H, D], strides for (b, l, h), channels contiguous):
+ *   q, k, v: the forward's inputs; o: its output; dout: the gradient of o
+ *   (same shape and strides rules as o); lse: the forward's lse, fp32,
+ *   contiguous [B, Hq, L] (ssa_prefill with lse != NULL);
+ *   dq, dk, dv: written in grad_dtype, shaped like q, k, v (no overlap with
+ *   any input).
+ * The window is the one the forward used (block_size 128).  workspace: device
+ * memory of at least ssa_prefill_backward_workspace_size bytes, 256-byte
+ * aligned, contents on entry ignored.
+ * Supported: dtype BF16 (q, k, v, o, dout), Dqk = Dv = 128, grad_dtype BF16 or
+ * F32, Hq a multiple of Hkv, window width <= 64.
+ * ------------------------------------------------------------------------- */
+typedef struct ssa_bwd_args {
+  int32_t dtype;      /* of q, k, v, o, dout: BF16 */
+  int32_t grad_dtype; /* of dq, dk, dv: BF16 or F32 */
+  int32_t B, L, Hq, Hkv, Dqk, Dv;
+  float scale; /* the forward's */
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3], do_stride[3];
+  int64_t dq_stride[3], dk_stride[3], dv_stride[3];
+  void* workspace;
+  size_t workspace_bytes;
+} ssa_bwd_args;
+
+int ssa_prefill_backward(const ssa_bwd_args* a, const ssa_window* win, void* stream);
+
+/* Bytes of workspace ssa_prefill_backward needs: per (b, query head, 32
+ * rows) 256 bytes of lse / delta records, plus fp32 partial dk, dv of the
+ * global blocks (128 KB per global block, batch, kv head and group of
+ * n_local query blocks that reads it).  0 for NULL arguments. */
+size_t ssa_prefill_backward_workspace_size(const ssa_bwd_args* a, const ssa_window* win);
+
+/* ---------------------------------------------------------------------------
  * ssa_prefill_chunk -- chunked prefill over a paged cache: T new queries per
  * sequence, at positions n_b - T .. n_b - 1, each reading the key blocks its
  * row lists (row = the query's absolute block, position / 128) and keys

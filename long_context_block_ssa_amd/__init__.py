@@ -28,7 +28,8 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 
 # every symbol include/ssa.h declares
 EXPORTS = (
-    "ssa_block_index", "ssa_block_index_seq", "ssa_prefill", "ssa_dense_causal", "ssa_prefill_chunk", "ssa_decode",
+    "ssa_block_index", "ssa_block_index_seq", "ssa_prefill", "ssa_dense_causal", "ssa_prefill_chunk", "ssa_prefill_backward", "ssa_prefill_backward",
+    "ssa_prefill_backward_workspace_size", "ssa_decode",
     "ssa_decode_workspace_size", "ssa_page_select", "ssa_page_select_workspace_size", "ssa_last_error", "ssa_version",
 )
 
@@ -102,6 +103,22 @@ class CChunkArgs(ctypes.Structure):
     ]
 
 
+class CBwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("L", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("Dqk", ctypes.c_int32), ("Dv", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("dout", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3), ("v_stride", ctypes.c_int64 * 3),
+        ("o_stride", ctypes.c_int64 * 3), ("do_stride", ctypes.c_int64 * 3),
+        ("dq_stride", ctypes.c_int64 * 3), ("dk_stride", ctypes.c_int64 * 3), ("dv_stride", ctypes.c_int64 * 3),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 @dataclass(frozen=True)
 class Window:
     """Window geometry; defaults = 1 global + 7 local blocks of 128 tokens."""
@@ -137,6 +154,9 @@ def load(path: str = LIB_PATH):
     lib.ssa_prefill.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CBlockLists), vp]
     lib.ssa_dense_causal.argtypes = [ctypes.POINTER(CAttnArgs), vp]
     lib.ssa_prefill_chunk.argtypes = [ctypes.POINTER(CChunkArgs), ctypes.POINTER(CBlockLists), vp]
+    lib.ssa_prefill_backward.argtypes = [ctypes.POINTER(CBwdArgs), ctypes.POINTER(CWindow), vp]
+    lib.ssa_prefill_backward_workspace_size.argtypes = [ctypes.POINTER(CBwdArgs), ctypes.POINTER(CWindow)]
+    lib.ssa_prefill_backward_workspace_size.restype = ctypes.c_size_t
     lib.ssa_decode.argtypes = [ctypes.POINTER(CDecodeArgs), ctypes.POINTER(CWindow), vp]
     lib.ssa_decode_workspace_size.argtypes = [ctypes.POINTER(CDecodeArgs), ctypes.POINTER(CWindow)]
     lib.ssa_decode_workspace_size.restype = ctypes.c_size_t
@@ -321,6 +341,52 @@ def prefill_chunk(q, k_pages, v_pages, block_table, seq_lens, lists: CBlockLists
     a.bt_stride = block_table.stride(0)
     _check(lib.ssa_prefill_chunk(ctypes.byref(a), ctypes.byref(lists), _stream(stream)))
     return out, lse
+
+
+def _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, scale) -> CBwdArgs:
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if t.dim() != 4 or t.stride(-1) != 1:
+            raise SSAError(SSA_ERR_INVALID, f"{name} must be [B, L, H, D] with a contiguous channel dimension")
+    a = CBwdArgs()
+    a.dtype, a.grad_dtype = _dtype_code(q.dtype), _dtype_code(dq.dtype)
+    a.B, a.L, a.Hq, a.Dqk = q.shape
+    a.Hkv, a.Dv = k.shape[2], v.shape[3]
+    a.scale = float(1.0 / math.sqrt(a.Dqk) if scale is None else scale)
+    a.q, a.k, a.v, a.o, a.dout, a.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse)
+    a.dq, a.dk, a.dv = _ptr(dq), _ptr(dk), _ptr(dv)
+    for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", o), ("do_stride", dout),
+                    ("dq_stride", dq), ("dk_stride", dk), ("dv_stride", dv)):
+        setattr(a, name, (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2)))
+    return a
+
+
+def prefill_backward_workspace_size(q, k, window: Window = DEFAULT_WINDOW) -> int:
+    a = CBwdArgs()
+    a.B, a.L, a.Hq, _ = q.shape
+    a.Hkv = k.shape[2]
+    w = window.c()
+    return int(load().ssa_prefill_backward_workspace_size(ctypes.byref(a), ctypes.byref(w)))
+
+
+def prefill_backward(q, k, v, o, dout, lse, scale=None, window: Window = DEFAULT_WINDOW, grad_dtype=None,
+                     dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """ssa_prefill_backward: (dq, dk, dv) of the SSA prefill whose output o and
+    lse [B, Hq, L] (fp32) the forward returned; dout is the gradient of o."""
+    lib = load()
+    gd = grad_dtype or q.dtype
+    dq = torch.empty(q.shape, dtype=gd, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=gd, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=gd, device=q.device) if dv is None else dv
+    a = _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, scale)
+    w = window.c()
+    need = int(lib.ssa_prefill_backward_workspace_size(ctypes.byref(a), ctypes.byref(w)))
+    if workspace is None:
+        workspace = torch.empty((need + 256,), dtype=torch.uint8, device=q.device)
+    base = workspace.data_ptr()
+    off = (-base) % 256
+    a.workspace, a.workspace_bytes = base + off, max(workspace.numel() - off, 0)
+    _check(lib.ssa_prefill_backward(ctypes.byref(a), ctypes.byref(w), _stream(stream)))
+    return dq, dk, dv
 
 
 def decode_workspace_size(B: int, Hq: int, Dqk: int, Dv: int, window: Window = DEFAULT_WINDOW) -> int:

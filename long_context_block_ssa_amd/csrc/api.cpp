@@ -203,6 +203,88 @@ int ssa_dense_causal(const ssa_attn_args* a, void* stream) {
   return device_status(e, who);
 }
 
+size_t ssa_prefill_backward_workspace_size(const ssa_bwd_args* a, const ssa_window* win) {
+  if (!a || !win || a->B < 1 || a->L < 1 || a->Hq < 1 || a->Hkv < 1 || win->n_global < 0 || win->n_local < 1)
+    return 0;
+  return (ssa::prefill_backward_workspace_bytes(a->B, a->L, a->Hq, a->Hkv, win->n_global, win->n_local) + 255) / 256 *
+         256;
+}
+
+int ssa_prefill_backward(const ssa_bwd_args* a, const ssa_window* win, void* stream) {
+  const char* who = "ssa_prefill_backward";
+  if (!a) return fail(SSA_ERR_INVALID, "%s: args is NULL", who);
+  if (!valid_window(win, who, 64)) return SSA_ERR_INVALID;
+  if (a->dtype != SSA_DTYPE_F32 && a->dtype != SSA_DTYPE_BF16)
+    return fail(SSA_ERR_INVALID, "%s: dtype %d is not an ssa_dtype", who, a->dtype);
+  if (a->grad_dtype != SSA_DTYPE_F32 && a->grad_dtype != SSA_DTYPE_BF16)
+    return fail(SSA_ERR_INVALID, "%s: grad_dtype %d is not an ssa_dtype", who, a->grad_dtype);
+  if (a->B < 1 || a->L < 1 || a->Hq < 1 || a->Hkv < 1 || a->Dqk < 1 || a->Dv < 1)
+    return fail(SSA_ERR_INVALID, "%s: sizes B=%d L=%d Hq=%d Hkv=%d Dqk=%d Dv=%d must be >= 1", who, a->B, a->L,
+                a->Hq, a->Hkv, a->Dqk, a->Dv);
+  if (a->Hq % a->Hkv != 0) return fail(SSA_ERR_INVALID, "%s: Hq=%d is not a multiple of Hkv=%d", who, a->Hq, a->Hkv);
+  if (!(std::isfinite(a->scale) && a->scale > 0.f))
+    return fail(SSA_ERR_INVALID, "%s: scale %g must be finite and > 0", who, static_cast<double>(a->scale));
+  if (!a->q || !a->k || !a->v || !a->o || !a->dout || !a->lse || !a->dq || !a->dk || !a->dv)
+    return fail(SSA_ERR_INVALID, "%s: q, k, v, o, dout, lse, dq, dk and dv must be non-NULL", who);
+  const void* p16[] = {a->q, a->k, a->v, a->o, a->dout, a->dq, a->dk, a->dv};
+  for (const void* ptr : p16)
+    if (!aligned(ptr, 16)) return fail(SSA_ERR_INVALID, "%s: tensor pointers must be 16-byte aligned", who);
+  if (!aligned(a->lse, 4)) return fail(SSA_ERR_INVALID, "%s: lse must be 4-byte aligned", who);
+  const size_t es = elem_size(a->dtype), eg = elem_size(a->grad_dtype);
+  if (!valid_strides(a->q_stride, es, who, "q") || !valid_strides(a->k_stride, es, who, "k") ||
+      !valid_strides(a->v_stride, es, who, "v") || !valid_strides(a->o_stride, es, who, "o") ||
+      !valid_strides(a->do_stride, es, who, "dout") || !valid_strides(a->dq_stride, eg, who, "dq") ||
+      !valid_strides(a->dk_stride, eg, who, "dk") || !valid_strides(a->dv_stride, eg, who, "dv"))
+    return SSA_ERR_INVALID;
+  if (win->block_size != 128) return fail(SSA_ERR_UNSUPPORTED, "%s: block_size must be 128", who);
+  if (!(a->dtype == SSA_DTYPE_BF16 && a->Dqk == 128 && a->Dv == 128))
+    return fail(SSA_ERR_UNSUPPORTED, "%s: no kernel for dtype=%d Dqk=%d Dv=%d (BF16, 128, 128 only)", who, a->dtype,
+                a->Dqk, a->Dv);
+  // the row strides of q, k, v and dout enter 32-bit staging offsets (16 rows)
+  const int64_t* rs[] = {&a->q_stride[1], &a->k_stride[1], &a->v_stride[1], &a->do_stride[1]};
+  for (const int64_t* r : rs)
+    if (*r >= (int64_t{1} << 26))
+      return fail(SSA_ERR_UNSUPPORTED, "%s: row stride %lld must be below 2^26 elements", who,
+                  static_cast<long long>(*r));
+  const size_t need = ssa_prefill_backward_workspace_size(a, win);
+  if (!a->workspace || a->workspace_bytes < need)
+    return fail(SSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
+                a->workspace ? a->workspace_bytes : static_cast<size_t>(0));
+  if (!aligned(a->workspace, 256)) return fail(SSA_ERR_INVALID, "%s: workspace must be 256-byte aligned", who);
+  ssa::BwdParams p{};
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.o = a->o;
+  p.dout = a->dout;
+  p.lse = a->lse;
+  p.dq = a->dq;
+  p.dk = a->dk;
+  p.dv = a->dv;
+  const int64_t* src[] = {a->q_stride, a->k_stride, a->v_stride, a->o_stride, a->do_stride,
+                          a->dq_stride, a->dk_stride, a->dv_stride};
+  int64_t* dst[][3] = {{&p.qs_b, &p.qs_l, &p.qs_h},    {&p.ks_b, &p.ks_l, &p.ks_h},    {&p.vs_b, &p.vs_l, &p.vs_h},
+                       {&p.os_b, &p.os_l, &p.os_h},    {&p.dos_b, &p.dos_l, &p.dos_h}, {&p.dqs_b, &p.dqs_l, &p.dqs_h},
+                       {&p.dks_b, &p.dks_l, &p.dks_h}, {&p.dvs_b, &p.dvs_l, &p.dvs_h}};
+  for (int t = 0; t < 8; ++t)
+    for (int i = 0; i < 3; ++i) *dst[t][i] = src[t][i];
+  p.B = a->B;
+  p.L = a->L;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.group = a->Hq / a->Hkv;
+  p.nqb = static_cast<int32_t>(ceil_div(a->L, 128));
+  p.n_global = win->n_global;
+  p.n_local = win->n_local;
+  p.nparts = static_cast<int32_t>(ceil_div(p.nqb, win->n_local));
+  p.scale = a->scale;
+  p.c1 = static_cast<float>(static_cast<double>(a->scale) * 1.4426950408889634);
+  const int64_t rec_bytes = static_cast<int64_t>(a->B) * a->Hq * p.nqb * 4 * 64 * 4;
+  p.rec = static_cast<float*>(a->workspace);
+  p.part = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + (rec_bytes + 255) / 256 * 256);
+  return device_status(ssa::launch_prefill_backward_d128(p, a->grad_dtype == SSA_DTYPE_F32, as_stream(stream)), who);
+}
+
 int ssa_prefill_chunk(const ssa_chunk_args* a, const ssa_block_lists* lists, void* stream) {
   const char* who = "ssa_prefill_chunk";
   if (!a) return fail(SSA_ERR_INVALID, "%s: args is NULL", who);

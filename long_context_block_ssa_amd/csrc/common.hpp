@@ -61,6 +61,39 @@ struct ChunkParams : PrefillParams {
   int32_t T, num_pages, max_len;
 };
 
+// SSA backward, bf16, Dqk = Dv = 128.  lse is the forward's natural-log sum
+// of exponentials [B, Hq, L]; the workspace holds, per (b, query head, stage
+// of 32 queries), a 64-float record: lse * log2(e) of the 32 rows, then
+// delta = rowsum(dout * o) of the 32 rows (rows past L: 0), and after the
+// records the fp32 partial dk / dv of the global blocks.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t qs_b, qs_l, qs_h;
+  int64_t ks_b, ks_l, ks_h;
+  int64_t vs_b, vs_l, vs_h;
+  int64_t os_b, os_l, os_h;
+  int64_t dos_b, dos_l, dos_h;
+  int64_t dqs_b, dqs_l, dqs_h;
+  int64_t dks_b, dks_l, dks_h;
+  int64_t dvs_b, dvs_l, dvs_h;
+  int32_t B, L, Hq, Hkv, group;
+  int32_t nqb;               // ceil(L / 128)
+  int32_t n_global, n_local; // the window
+  int32_t nparts;            // query-block parts of global block 0 (ceil(nqb / n_local))
+  float c1;                  // scale * log2(e)
+  float scale;
+  float* rec;                // [B, Hq, nqb * 4, 64] stage records
+  float* part;               // [n_global, nparts, B, Hkv, 2, 128, 128] global-block partials
+};
+
 struct DecodeParams {
   const void* q;
   const void* k;
@@ -115,6 +148,12 @@ bool prefill_d128_supports(const PrefillParams& p, int dqk, int dv);
 hipError_t launch_prefill_d128(const PrefillParams& p, bool out_f32, hipStream_t stream);
 // chunked prefill over a paged cache, bf16, Dqk = Dv = 128
 hipError_t launch_prefill_chunk_d128(const ChunkParams& p, bool out_f32, hipStream_t stream);
+
+// SSA backward (bf16, d = 128): delta / records, dq, dk and dv of the local
+// blocks, the global blocks' partials and their reduction
+hipError_t launch_prefill_backward_d128(const BwdParams& p, bool grad_f32, hipStream_t stream);
+size_t prefill_backward_workspace_bytes(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t n_global,
+                                        int32_t n_local);
 
 hipError_t launch_decode(const DecodeParams& p, int dqk, int dv, hipStream_t stream);
 

@@ -1,0 +1,657 @@
+// SSA backward on gfx950, bf16, Dqk = Dv = 128: the gradients of the
+// block-sparse causal attention with respect to q, k and v.  The sparse
+// operator needs a custom, deterministic backward for training (LongCat
+// sparse attention article, section 4); LoZA converts its layers in
+// mid-training (QbitAI report on LongCat LoZA).  With P the softmax of the
+// masked scaled scores, recomputed from the forward's lse, and dO the
+// incoming gradient of the output, the chain rule through o = P v and the
+// softmax gives
+//   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - delta),   delta_i = sum_c dO_ic O_ic,
+//   dQ = scale dS K,   dK = scale dS^T Q.
+//
+// Kernels (one stream, in this order):
+//   - records: per (b, head, 32-row stage) a 64-float record: the stage's
+//     lse * log2(e), then its delta (rows past L: 0);
+//   - dq: one workgroup per (query block, b, head), laid out like the
+//     forward: the window's K and V stream through the LDS ring, S^T = K Q^T
+//     and dP^T = V dO^T on 32x32x16 MFMAs with Q and dO in registers (one
+//     query per lane), dQ^T += K^T dS^T with K^T read transposed
+//     (ds_read_b64_tr_b16);
+//   - dkdv: one workgroup per (key block, b, kv head) for the local blocks
+//     and per (global block, part of its readers, b, kv head): each wave
+//     keeps its 32 keys' K and V rows in registers, and the query stages
+//     that read the key block -- the window's inverse map: the next n_local
+//     query blocks, or every later block for a global block -- stream their
+//     Q and dO rows and records through the ring, for every query head of
+//     the kv head.  S = Q K^T and dP = dO V^T put one key per lane, so P and
+//     dS are directly the B operands of dV^T += dO^T P and dK^T += Q^T dS
+//     (dO^T and Q^T read transposed);
+//   - reduce: a global block's partials summed in part order.
+// No atomics: the result is bitwise deterministic.
+#include "attn_d128.hpp"
+
+#include <algorithm>
+
+namespace ssa {
+namespace {
+
+using namespace d128;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kRec = 64;               // floats per stage record
+constexpr int kRingBytes = kSlots * kSlotBytes;  // 64 KB of Q/dO (or K/V) slabs
+constexpr int kRecRegion = 1024;       // per wave and slot: the record, then 3 copies of it
+constexpr int kDkdvLds = kRingBytes + kSlots * kWaves * kRecRegion;  // 80 KB
+
+// vmcnt(5 k) alone: all but this wave's loads of the last k stages have
+// landed (5 loads a stage: 4 row slabs and the record)
+__device__ __forceinline__ void wait_stages5(int k) {
+  if (k >= 2)
+    __builtin_amdgcn_s_waitcnt(0x0F7A);
+  else if (k == 1)
+    __builtin_amdgcn_s_waitcnt(0x0F75);
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// the stage record's lse*log2(e) and delta of the 16 query rows a lane holds
+// (rows 8j + 4h .. +3 for j = 0..3): 8 reads at the wave's record region
+template <int SLOT>
+__device__ __forceinline__ void lds_read_rec(uint32_t a, f32x4 (&ls)[4], f32x4 (&dl)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%9\n"
+      "ds_read_b128 %1, %8 offset:%10\n"
+      "ds_read_b128 %2, %8 offset:%11\n"
+      "ds_read_b128 %3, %8 offset:%12\n"
+      "ds_read_b128 %4, %8 offset:%13\n"
+      "ds_read_b128 %5, %8 offset:%14\n"
+      "ds_read_b128 %6, %8 offset:%15\n"
+      "ds_read_b128 %7, %8 offset:%16\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(ls[0]), "=&v"(ls[1]), "=&v"(ls[2]), "=&v"(ls[3]), "=&v"(dl[0]), "=&v"(dl[1]), "=&v"(dl[2]),
+        "=&v"(dl[3])
+      : "v"(a), "i"(SLOT * kWaves * kRecRegion), "i"(SLOT * kWaves * kRecRegion + 32),
+        "i"(SLOT * kWaves * kRecRegion + 64), "i"(SLOT * kWaves * kRecRegion + 96),
+        "i"(SLOT * kWaves * kRecRegion + 128), "i"(SLOT * kWaves * kRecRegion + 160),
+        "i"(SLOT * kWaves * kRecRegion + 192), "i"(SLOT * kWaves * kRecRegion + 224)
+      : "memory");
+}
+
+#define SSA_DMA(src, dst) \
+  __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(src), (SSA_LDS void*)(dst), 16, 0, 0)
+
+// ---------------------------------------------------------------------------
+// records: one 16-lane group per (b, head, row < nqb*128), 8 channels a lane
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_records_kernel(BwdParams p) {
+  const int64_t Lp = static_cast<int64_t>(p.nqb) * kBlk;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);  // (b*Hq + h) * Lp + i
+  const int c = threadIdx.x & 15;
+  if (gid >= static_cast<int64_t>(p.B) * p.Hq * Lp) return;  // whole 16-lane groups
+  const int i = static_cast<int>(gid % Lp);
+  const int64_t bh = gid / Lp;
+  const int h = static_cast<int>(bh % p.Hq), b = static_cast<int>(bh / p.Hq);
+  float acc = 0.f, lse2 = 0.f;
+  if (i < p.L) {
+    const u32x4 ov = *reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.o) + b * p.os_b +
+                                                     static_cast<int64_t>(i) * p.os_l + h * p.os_h + c * 8);
+    const u32x4 dv = *reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.dout) + b * p.dos_b +
+                                                     static_cast<int64_t>(i) * p.dos_l + h * p.dos_h + c * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = __builtin_fmaf(__builtin_bit_cast(float, ov[w] << 16), __builtin_bit_cast(float, dv[w] << 16), acc);
+      acc = __builtin_fmaf(__builtin_bit_cast(float, ov[w] & 0xFFFF0000u), __builtin_bit_cast(float, dv[w] & 0xFFFF0000u),
+                           acc);
+    }
+    const float l = p.lse[bh * p.L + i];
+    // a row that admitted no key (lse = -inf) must give P = 0
+    lse2 = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e;
+  }
+  acc += __shfl_xor(acc, 8);
+  acc += __shfl_xor(acc, 4);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 1);
+  if (c == 0) {
+    float* r = p.rec + (bh * (p.nqb * 4) + i / kSK) * kRec;
+    r[i % kSK] = lse2;
+    r[kSK + i % kSK] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dq: one workgroup per (query block, b, head), 4 waves x 32 queries
+// ---------------------------------------------------------------------------
+template <typename GradT>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdParams p) {
+  __shared__ u32x4 ring[kRingBytes / 16];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h32 = lane >> 5, c32 = lane & 31;
+  const int bh_count = p.B * p.Hq;
+  const int qb = p.nqb - 1 - static_cast<int>(blockIdx.x) / bh_count;
+  const int bh = static_cast<int>(blockIdx.x) % bh_count;
+  const int b = bh / p.Hq, h = bh % p.Hq, hk = h / p.group;
+  const int qoff = wave * 32;
+  const int L = p.L;
+
+  const __bf16* qbase = static_cast<const __bf16*>(p.q) + b * p.qs_b + h * p.qs_h;
+  const __bf16* dobase = static_cast<const __bf16*>(p.dout) + b * p.dos_b + h * p.dos_h;
+  const __bf16* kbase = static_cast<const __bf16*>(p.k) + b * p.ks_b + hk * p.ks_h;
+  const __bf16* vbase = static_cast<const __bf16*>(p.v) + b * p.vs_b + hk * p.vs_h;
+
+  // the window of qb in ascending order, entry i on lane i
+  const int g_end = min(p.n_global, qb + 1);
+  const int l_begin = max(g_end, qb - p.n_local + 1);
+  const int nblk = g_end + qb - l_begin + 1;
+  const int blane = lane < g_end ? lane : (lane < nblk ? l_begin + lane - g_end : -1);
+  const int nst = nblk * (kBlk / kSK);
+  auto stage_block = [&](int s) -> int { return s < nst ? __builtin_amdgcn_readlane(blane, s >> 2) : -1; };
+
+  // staging (the forward's): slab instruction j covers rows 4j .. 4j+3; wave
+  // w issues j = w and j = w + 4 of the K slab and of the V slab
+  const int drow = 4 * wave + (lane >> 4);
+  const int dunit = (lane & 15) ^ swz(drow);
+  const uint32_t koff = static_cast<uint32_t>(drow * p.ks_l + dunit * 8);
+  const uint32_t voff = static_cast<uint32_t>(drow * p.vs_l + dunit * 8);
+  const int64_t k16 = 16 * p.ks_l, v16 = 16 * p.vs_l;
+  const uint32_t ring0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SSA_LDS u32x4*)(ring)));
+  // row fragment c (A operand): row c32, logical unit 2c + h32
+  uint32_t faddr[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) faddr[c] = ring0 + (c32 * kUnits + ((2 * c + h32) ^ swz(c32))) * 16;
+  // transposed fragment (dim tile dt, read e) of a slab: lane i of 16-lane
+  // group g points at row 8e + 4(g/2) + i/4 (+16 for the second 16 rows),
+  // channels 32dt + 16(g%2) + 4(i%4) .. +3
+  uint32_t taddr[2][4];
+  {
+    const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int row = 8 * e + 4 * (g >> 1) + (i >> 2);
+        const int ch = 32 * dt + 16 * (g & 1) + 4 * (i & 3);
+        taddr[e][dt] = ring0 + (row * kUnits + ((ch >> 3) ^ swz(row))) * 16 + (ch & 7) * 2;
+      }
+  }
+
+  // this lane's query column: Q and dO rows (B operands), lse and delta
+  const int row = qb * kBlk + qoff + c32;
+  bf16x8 qf[8], dof[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    u32x4 a = {0, 0, 0, 0}, d = {0, 0, 0, 0};
+    if (row < L) {
+      a = *reinterpret_cast<const u32x4*>(qbase + static_cast<int64_t>(row) * p.qs_l + c * 16 + h32 * 8);
+      d = *reinterpret_cast<const u32x4*>(dobase + static_cast<int64_t>(row) * p.dos_l + c * 16 + h32 * 8);
+    }
+    qf[c] = __builtin_bit_cast(bf16x8, a);
+    dof[c] = __builtin_bit_cast(bf16x8, d);
+  }
+  float lse2 = 0.f, delta = 0.f;
+  if (row < L) {
+    const float* rec = p.rec + (static_cast<int64_t>(bh) * (p.nqb * 4) + row / kSK) * kRec;
+    lse2 = rec[row % kSK];
+    delta = rec[kSK + row % kSK];
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+
+  auto issue = [&](int s, int slot) {
+    const int kb = max(stage_block(s), 0);  // past the end: rows of block 0 nobody reads
+    const int key0 = kb * kBlk + (s & 3) * kSK;
+    SSA_LDS u32x4* kd = (SSA_LDS u32x4*)(ring) + slot * (kSlotBytes / 16) + wave * 64;
+    SSA_LDS u32x4* vd = kd + kSlab;
+    if (key0 + kSK <= L) {
+      const __bf16* ks = kbase + static_cast<int64_t>(key0) * p.ks_l + koff;
+      const __bf16* vs = vbase + static_cast<int64_t>(key0) * p.vs_l + voff;
+      SSA_DMA(ks, kd);
+      SSA_DMA(ks + k16, kd + 256);
+      SSA_DMA(vs, vd);
+      SSA_DMA(vs + v16, vd + 256);
+    } else {
+      const int64_t r0 = min(key0 + drow, L - 1), r1 = min(key0 + drow + 16, L - 1);
+      SSA_DMA(kbase + r0 * p.ks_l + dunit * 8, kd);
+      SSA_DMA(kbase + r1 * p.ks_l + dunit * 8, kd + 256);
+      SSA_DMA(vbase + r0 * p.vs_l + dunit * 8, vd);
+      SSA_DMA(vbase + r1 * p.vs_l + dunit * 8, vd + 256);
+    }
+  };
+
+  auto stage = [&](auto slot_tag, int s, int ns, int nslot) {
+    constexpr int SLOT = decltype(slot_tag)::value;
+    constexpr int OFF = SLOT * kSlotBytes;
+    const int kb = stage_block(s);
+    const int sub = s & 3;
+    const int key0 = kb * kBlk + sub * kSK;
+    const bool need = kb >= 0 && key0 < L && !(kb == qb && sub * kSK > qoff + 31);
+    if (ns < nst) issue(ns, nslot);
+    if (!need) return;
+    f32x16 sc, dp;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
+    {
+      u32x4 kraw[8];
+      lds_read_k8<OFF>(faddr, kraw);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kraw[c]), qf[c], sc, 0, 0, 0);
+    }
+    {
+      u32x4 vraw[8];
+      lds_read_k8<OFF + kSlab * 16>(faddr, vraw);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vraw[c]), dof[c], dp, 0, 0, 0);
+    }
+    u32x2 kt[16];
+    lds_read_vt16<OFF>(taddr, kt);  // K^T of the stage
+    if (kb == qb || key0 + kSK > L) {
+      const int lim = min(row, L - 1) - key0 - 4 * h32;  // last valid key offset
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + (i & 3) > lim) sc[i] = kNegInf;
+    }
+    // P^T = exp(scale s - lse), dS^T = P^T (dP^T - delta)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], p.c1, -lse2));
+      dp[i] = pe * (dp[i] - delta);
+    }
+    bf16x8 df[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16x4 a = __builtin_convertvector((f32x4){dp[8 * c], dp[8 * c + 1], dp[8 * c + 2], dp[8 * c + 3]}, bf16x4);
+      const bf16x4 bq =
+          __builtin_convertvector((f32x4){dp[8 * c + 4], dp[8 * c + 5], dp[8 * c + 6], dp[8 * c + 7]}, bf16x4);
+      df[c] = bf16x8{a[0], a[1], a[2], a[3], bq[0], bq[1], bq[2], bq[3]};
+    }
+    // dQ^T += K^T dS^T: chunk c = keys 16c .. 16c+15 in the dS^T register order
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const bf16x4 t0 = __builtin_bit_cast(bf16x4, kt[c * 4 + dt]);
+        const bf16x4 t1 = __builtin_bit_cast(bf16x4, kt[8 + c * 4 + dt]);
+        const bf16x8 tf = bf16x8{t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf, df[c], acc[dt], 0, 0, 0);
+      }
+  };
+
+  auto settle = [&](int s) {
+    const int last = max(kSlots - 2, min(s + kSlots - 1, nst - 1));  // last stage issued
+    wait_stages(last - (s + 1));
+    stage_barrier();
+  };
+
+#pragma unroll
+  for (int i = 0; i < kSlots - 1; ++i) issue(i, i);
+  wait_stages(kSlots - 2);
+  stage_barrier();
+  const int nst_pad = (nst + kSlots - 1) & ~(kSlots - 1);
+  for (int s0 = 0; s0 < nst_pad; s0 += kSlots) {
+#define SSA_STAGE(k)                                                                                        \
+  {                                                                                                         \
+    const int s = s0 + (k);                                                                                 \
+    if (s < nst) stage(std::integral_constant<int, (k)>{}, s, s + kSlots - 1, ((k) + kSlots - 1) % kSlots); \
+    settle(s);                                                                                              \
+  }
+    SSA_STAGE(0)
+    SSA_STAGE(1)
+    SSA_STAGE(2)
+    SSA_STAGE(3)
+#undef SSA_STAGE
+  }
+
+  if (row >= L) return;
+  GradT* dqb = static_cast<GradT*>(p.dq) + b * p.dqs_b + h * p.dqs_h + static_cast<int64_t>(row) * p.dqs_l;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x4 v = {acc[dt][4 * k], acc[dt][4 * k + 1], acc[dt][4 * k + 2], acc[dt][4 * k + 3]};
+      store4<GradT>(dqb + 32 * dt + 8 * k + 4 * h32, v * p.scale);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dk, dv: one workgroup per (key block[, part], b, kv head), 4 waves x 32 keys
+// ---------------------------------------------------------------------------
+template <typename GradT, bool PARTIAL>
+__global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p) {
+  extern __shared__ u32x4 ring[];  // kDkdvLds bytes: the slab ring, then the record regions
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h32 = lane >> 5, c32 = lane & 31;
+  const int bh_count = p.B * p.Hkv;
+  const int bh = static_cast<int>(blockIdx.x) % bh_count;
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const int L = p.L;
+  // the key block and the query blocks [q_begin, q_end) that read it
+  int kb, part = 0, q_begin, q_end;
+  if constexpr (PARTIAL) {
+    const int rest = static_cast<int>(blockIdx.x) / bh_count;
+    part = rest % p.nparts;
+    kb = rest / p.nparts;
+    q_begin = kb + part * p.n_local;
+    q_end = min(q_begin + p.n_local, p.nqb);
+    if (q_begin >= q_end) return;  // a part past the last query block
+  } else {
+    kb = p.n_global + static_cast<int>(blockIdx.x) / bh_count;
+    q_begin = kb;
+    q_end = min(kb + p.n_local, p.nqb);
+  }
+  const int nq = q_end - q_begin;
+  const int nst = p.group * nq * (kBlk / kSK);  // (query head of the group, query block, quarter)
+  const int key = kb * kBlk + wave * 32 + c32;  // this lane's key (B-operand column)
+  const bool wave_keys = kb * kBlk + wave * 32 < L;
+
+  // K and V rows of this lane's key (B operands of S = Q K^T and dP = dO V^T)
+  bf16x8 kf[8], vf[8];
+  {
+    const __bf16* kr = static_cast<const __bf16*>(p.k) + b * p.ks_b + hk * p.ks_h + static_cast<int64_t>(key) * p.ks_l;
+    const __bf16* vr = static_cast<const __bf16*>(p.v) + b * p.vs_b + hk * p.vs_h + static_cast<int64_t>(key) * p.vs_l;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      u32x4 a = {0, 0, 0, 0}, d = {0, 0, 0, 0};
+      if (key < L) {
+        a = *reinterpret_cast<const u32x4*>(kr + c * 16 + h32 * 8);
+        d = *reinterpret_cast<const u32x4*>(vr + c * 16 + h32 * 8);
+      }
+      kf[c] = __builtin_bit_cast(bf16x8, a);
+      vf[c] = __builtin_bit_cast(bf16x8, d);
+    }
+  }
+
+  // stage s -> query head, first query row
+  auto stage_rows = [&](int s, int& hq, int& q0) {
+    const int ss = s < nst ? s : 0;  // past the end: stage 0 again (rows nobody reads)
+    const int gi = ss / (nq * 4);
+    const int qbi = (ss >> 2) % nq;
+    hq = hk * p.group + gi;
+    q0 = (q_begin + qbi) * kBlk + (ss & 3) * kSK;
+  };
+
+  const int drow = 4 * wave + (lane >> 4);
+  const int dunit = (lane & 15) ^ swz(drow);
+  const uint32_t qoffs = static_cast<uint32_t>(drow * p.qs_l + dunit * 8);
+  const uint32_t dooffs = static_cast<uint32_t>(drow * p.dos_l + dunit * 8);
+  const int64_t q16 = 16 * p.qs_l, do16 = 16 * p.dos_l;
+  const uint32_t ring0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SSA_LDS u32x4*)(ring)));
+  uint32_t faddr[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) faddr[c] = ring0 + (c32 * kUnits + ((2 * c + h32) ^ swz(c32))) * 16;
+  uint32_t taddr[2][4];
+  {
+    const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int row = 8 * e + 4 * (g >> 1) + (i >> 2);
+        const int ch = 32 * dt + 16 * (g & 1) + 4 * (i & 3);
+        taddr[e][dt] = ring0 + (row * kUnits + ((ch >> 3) ^ swz(row))) * 16 + (ch & 7) * 2;
+      }
+  }
+  // this wave's record region of slot 0; the rows of lane half h32 start 16 h32 bytes in
+  const uint32_t raddr = ring0 + kRingBytes + wave * kRecRegion + 16 * h32;
+
+  f32x16 dka[4], dva[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dka[dt][i] = dva[dt][i] = 0.f;
+
+  auto issue = [&](int s, int slot) {
+    int hq, q0;
+    stage_rows(s, hq, q0);
+    const __bf16* qs = static_cast<const __bf16*>(p.q) + b * p.qs_b + hq * p.qs_h;
+    const __bf16* ds = static_cast<const __bf16*>(p.dout) + b * p.dos_b + hq * p.dos_h;
+    SSA_LDS u32x4* qd = (SSA_LDS u32x4*)(ring) + slot * (kSlotBytes / 16) + wave * 64;
+    SSA_LDS u32x4* dd = qd + kSlab;
+    SSA_LDS u32x4* rd = (SSA_LDS u32x4*)(ring) + (kRingBytes + (slot * kWaves + wave) * kRecRegion) / 16;
+    if (q0 + kSK <= L) {
+      const __bf16* a = qs + static_cast<int64_t>(q0) * p.qs_l + qoffs;
+      const __bf16* d = ds + static_cast<int64_t>(q0) * p.dos_l + dooffs;
+      SSA_DMA(a, qd);
+      SSA_DMA(a + q16, qd + 256);
+      SSA_DMA(d, dd);
+      SSA_DMA(d + do16, dd + 256);
+    } else {
+      // rows at or past L repeat row L-1 (finite, masked later)
+      const int64_t r0 = min(q0 + drow, L - 1), r1 = min(q0 + drow + 16, L - 1);
+      SSA_DMA(qs + r0 * p.qs_l + dunit * 8, qd);
+      SSA_DMA(qs + r1 * p.qs_l + dunit * 8, qd + 256);
+      SSA_DMA(ds + r0 * p.dos_l + dunit * 8, dd);
+      SSA_DMA(ds + r1 * p.dos_l + dunit * 8, dd + 256);
+    }
+    // the record: 16 lanes cover its 256 bytes, the other lanes repeat them
+    const float* rec = p.rec + (static_cast<int64_t>(b * p.Hq + hq) * (p.nqb * 4) + q0 / kSK) * kRec + (lane & 15) * 4;
+    SSA_DMA(rec, rd);
+  };
+
+  auto stage = [&](auto slot_tag, int s, int ns, int nslot) {
+    constexpr int SLOT = decltype(slot_tag)::value;
+    constexpr int OFF = SLOT * kSlotBytes;
+    int hq, q0;
+    stage_rows(s, hq, q0);
+    const int qb = q0 / kBlk;
+    // nothing to do: no query of the stage reaches this wave's keys, or they do not exist
+    const bool need = q0 < L && wave_keys && !(qb == kb && q0 + kSK - 1 < kb * kBlk + wave * 32);
+    if (ns < nst) issue(ns, nslot);
+    if (!need) return;
+    // S = Q K^T and dP = dO V^T: 32 queries x this wave's 32 keys, one key per lane
+    f32x16 sc, dp;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
+    {
+      u32x4 qr[8];
+      lds_read_k8<OFF>(faddr, qr);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qr[c]), kf[c], sc, 0, 0, 0);
+    }
+    {
+      u32x4 dr[8];
+      lds_read_k8<OFF + kSlab * 16>(faddr, dr);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, dr[c]), vf[c], dp, 0, 0, 0);
+    }
+    f32x4 ls[4], dl[4];
+    lds_read_rec<SLOT>(raddr, ls, dl);
+    // register i holds query q0 + 8(i/4) + 4 h32 + (i%4): it must not precede the key and must exist
+    if (qb == kb || q0 + kSK > L) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qi = q0 + 8 * (i >> 2) + 4 * h32 + (i & 3);
+        if (qi < key || qi >= L) sc[i] = kNegInf;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sc[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], p.c1, -ls[i >> 2][i & 3]));  // P
+      dp[i] = sc[i] * (dp[i] - dl[i >> 2][i & 3]);                                       // dS
+    }
+    bf16x8 pf[2], df[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16x4 a = __builtin_convertvector((f32x4){sc[8 * c], sc[8 * c + 1], sc[8 * c + 2], sc[8 * c + 3]}, bf16x4);
+      const bf16x4 a2 =
+          __builtin_convertvector((f32x4){sc[8 * c + 4], sc[8 * c + 5], sc[8 * c + 6], sc[8 * c + 7]}, bf16x4);
+      pf[c] = bf16x8{a[0], a[1], a[2], a[3], a2[0], a2[1], a2[2], a2[3]};
+      const bf16x4 d = __builtin_convertvector((f32x4){dp[8 * c], dp[8 * c + 1], dp[8 * c + 2], dp[8 * c + 3]}, bf16x4);
+      const bf16x4 d2 =
+          __builtin_convertvector((f32x4){dp[8 * c + 4], dp[8 * c + 5], dp[8 * c + 6], dp[8 * c + 7]}, bf16x4);
+      df[c] = bf16x8{d[0], d[1], d[2], d[3], d2[0], d2[1], d2[2], d2[3]};
+    }
+    // dV^T += dO^T P, then dK^T += Q^T dS: chunk c = queries 16c .. 16c+15 in the register order
+    {
+      u32x2 t[16];
+      lds_read_vt16<OFF + kSlab * 16>(taddr, t);  // dO^T
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const bf16x4 t0 = __builtin_bit_cast(bf16x4, t[c * 4 + dt]);
+          const bf16x4 t1 = __builtin_bit_cast(bf16x4, t[8 + c * 4 + dt]);
+          const bf16x8 tf = bf16x8{t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+          dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf, pf[c], dva[dt], 0, 0, 0);
+        }
+    }
+    {
+      u32x2 t[16];
+      lds_read_vt16<OFF>(taddr, t);  // Q^T
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const bf16x4 t0 = __builtin_bit_cast(bf16x4, t[c * 4 + dt]);
+          const bf16x4 t1 = __builtin_bit_cast(bf16x4, t[8 + c * 4 + dt]);
+          const bf16x8 tf = bf16x8{t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+          dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf, df[c], dka[dt], 0, 0, 0);
+        }
+    }
+  };
+
+  auto settle = [&](int s) {
+    const int last = max(kSlots - 2, min(s + kSlots - 1, nst - 1));
+    wait_stages5(last - (s + 1));
+    stage_barrier();
+  };
+
+#pragma unroll
+  for (int i = 0; i < kSlots - 1; ++i) issue(i, i);
+  wait_stages5(kSlots - 2);
+  stage_barrier();
+  const int nst_pad = (nst + kSlots - 1) & ~(kSlots - 1);
+  for (int s0 = 0; s0 < nst_pad; s0 += kSlots) {
+#define SSA_STAGE(k)                                                                                        \
+  {                                                                                                         \
+    const int s = s0 + (k);                                                                                 \
+    if (s < nst) stage(std::integral_constant<int, (k)>{}, s, s + kSlots - 1, ((k) + kSlots - 1) % kSlots); \
+    settle(s);                                                                                              \
+  }
+    SSA_STAGE(0)
+    SSA_STAGE(1)
+    SSA_STAGE(2)
+    SSA_STAGE(3)
+#undef SSA_STAGE
+  }
+
+  if (key >= L) return;
+  // accumulators: lane = key, register i of tile dt = channel 32dt + 8(i/4) + 4 h32 + (i%4)
+  if constexpr (PARTIAL) {
+    float* out = p.part + ((((static_cast<int64_t>(kb) * p.nparts + part) * p.B + b) * p.Hkv + hk) * 2) * kBlk * kD +
+                 static_cast<int64_t>(key - kb * kBlk) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 vk = {dka[dt][4 * k], dka[dt][4 * k + 1], dka[dt][4 * k + 2], dka[dt][4 * k + 3]};
+        const f32x4 vv = {dva[dt][4 * k], dva[dt][4 * k + 1], dva[dt][4 * k + 2], dva[dt][4 * k + 3]};
+        *reinterpret_cast<f32x4*>(out + 32 * dt + 8 * k + 4 * h32) = vk * p.scale;
+        *reinterpret_cast<f32x4*>(out + kBlk * kD + 32 * dt + 8 * k + 4 * h32) = vv;
+      }
+  } else {
+    GradT* dkr = static_cast<GradT*>(p.dk) + b * p.dks_b + hk * p.dks_h + static_cast<int64_t>(key) * p.dks_l;
+    GradT* dvr = static_cast<GradT*>(p.dv) + b * p.dvs_b + hk * p.dvs_h + static_cast<int64_t>(key) * p.dvs_l;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 vk = {dka[dt][4 * k], dka[dt][4 * k + 1], dka[dt][4 * k + 2], dka[dt][4 * k + 3]};
+        const f32x4 vv = {dva[dt][4 * k], dva[dt][4 * k + 1], dva[dt][4 * k + 2], dva[dt][4 * k + 3]};
+        store4<GradT>(dkr + 32 * dt + 8 * k + 4 * h32, vk * p.scale);
+        store4<GradT>(dvr + 32 * dt + 8 * k + 4 * h32, vv);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// reduce: dk / dv of the global blocks = the sum of their parts, in order;
+// one thread per (global block, b, kv head, dk|dv, key row, 4 channels)
+// ---------------------------------------------------------------------------
+template <typename GradT>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int n_glob) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int quad = static_cast<int>(gid % 32);
+  const int r = static_cast<int>((gid / 32) % kBlk);
+  const int which = static_cast<int>((gid / (32 * kBlk)) % 2);
+  const int64_t rest = gid / (64 * kBlk);
+  const int bh = static_cast<int>(rest % (p.B * p.Hkv));
+  const int kb = static_cast<int>(rest / (p.B * p.Hkv));
+  if (kb >= n_glob) return;
+  const int key = kb * kBlk + r;
+  if (key >= p.L) return;
+  const int b = bh / p.Hkv, hk = bh % p.Hkv;
+  const int np = min(p.nparts, (p.nqb - kb + p.n_local - 1) / p.n_local);  // parts that have readers
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int part = 0; part < np; ++part) {
+    const float* src = p.part + ((((static_cast<int64_t>(kb) * p.nparts + part) * p.B + b) * p.Hkv + hk) * 2 + which) *
+                                    kBlk * kD +
+                       r * kD + quad * 4;
+    s += *reinterpret_cast<const f32x4*>(src);
+  }
+  GradT* dst = which == 0 ? static_cast<GradT*>(p.dk) + b * p.dks_b + hk * p.dks_h + static_cast<int64_t>(key) * p.dks_l
+                          : static_cast<GradT*>(p.dv) + b * p.dvs_b + hk * p.dvs_h + static_cast<int64_t>(key) * p.dvs_l;
+  store4<GradT>(dst + quad * 4, s);
+}
+
+#undef SSA_DMA
+
+template <typename GradT>
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
+  const int64_t Lp = static_cast<int64_t>(p.nqb) * kBlk;
+  const int64_t rows = static_cast<int64_t>(p.B) * p.Hq * Lp;
+  hipError_t e = launch_kernel(bwd_records_kernel, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, stream, p);
+  if (e != hipSuccess) return e;
+  e = launch_kernel(bwd_dq_kernel<GradT>, dim3(static_cast<unsigned>(p.nqb) * p.B * p.Hq), dim3(kWaves * 64), 0, stream,
+                    p);
+  if (e != hipSuccess) return e;
+  const int n_glob = min(p.n_global, p.nqb);
+  const unsigned bh = static_cast<unsigned>(p.B) * p.Hkv;
+  if (p.nqb > n_glob) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dkdv_kernel<GradT, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kDkdvLds);
+    if (e != hipSuccess) return e;
+    e = launch_kernel(bwd_dkdv_kernel<GradT, false>, dim3(static_cast<unsigned>(p.nqb - n_glob) * bh), dim3(kWaves * 64),
+                      kDkdvLds, stream, p);
+    if (e != hipSuccess) return e;
+  }
+  if (n_glob > 0) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dkdv_kernel<GradT, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kDkdvLds);
+    if (e != hipSuccess) return e;
+    e = launch_kernel(bwd_dkdv_kernel<GradT, true>, dim3(static_cast<unsigned>(n_glob * p.nparts) * bh),
+                      dim3(kWaves * 64), kDkdvLds, stream, p);
+    if (e != hipSuccess) return e;
+    const int64_t threads = static_cast<int64_t>(n_glob) * bh * 2 * kBlk * 32;
+    e = launch_kernel(bwd_reduce_kernel<GradT>, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
+                      stream, p, n_glob);
+  }
+  return e;
+}
+
+}  // namespace
+
+size_t prefill_backward_workspace_bytes(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t n_global,
+                                        int32_t n_local) {
+  const int64_t nqb = (static_cast<int64_t>(L) + kBlk - 1) / kBlk;
+  const int64_t rec = static_cast<int64_t>(B) * Hq * nqb * 4 * kRec * sizeof(float);
+  const int64_t n_glob = std::min<int64_t>(n_global, nqb);
+  const int64_t nparts = (nqb + n_local - 1) / n_local;
+  const int64_t part = n_glob * nparts * B * Hkv * 2 * kBlk * kD * static_cast<int64_t>(sizeof(float));
+  return static_cast<size_t>((rec + 255) / 256 * 256 + part);
+}
+
+hipError_t launch_prefill_backward_d128(const BwdParams& p, bool grad_f32, hipStream_t stream) {
+  return grad_f32 ? launch_bwd<float>(p, stream) : launch_bwd<__bf16>(p, stream);
+}
+
+}  // namespace ssa

@@ -225,6 +225,64 @@ def test_prefill_chunk_rejects(lib, over, lover, code):
     assert lib.ssa_prefill_chunk(ctypes.byref(chunk_args()), None, None) == ssa.SSA_ERR_INVALID
 
 
+def bwd_args(**over):
+    a = ssa.CBwdArgs()
+    a.dtype = ssa.DTYPE_BF16
+    a.grad_dtype = ssa.DTYPE_F32
+    a.B, a.L, a.Hq, a.Hkv, a.Dqk, a.Dv = 2, 3000, 4, 2, 128, 128
+    a.scale = 0.088
+    a.q = a.k = a.v = a.o = a.dout = FAKE
+    a.lse = FAKE
+    a.dq, a.dk, a.dv = FAKE + 4096, FAKE + 8192, FAKE + 12288
+    for n, h in (("q_stride", 4), ("o_stride", 4), ("do_stride", 4), ("dq_stride", 4), ("k_stride", 2), ("v_stride", 2),
+                 ("dk_stride", 2), ("dv_stride", 2)):
+        setattr(a, n, (ctypes.c_int64 * 3)(3000 * h * 128, h * 128, 128))
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a
+
+
+def test_backward_workspace_size(lib):
+    w = ssa.CWindow(128, 1, 7)
+    a = bwd_args()
+    nqb = (3000 + 127) // 128
+    rec = 2 * 4 * nqb * 4 * 64 * 4
+    part = 1 * ((nqb + 6) // 7) * 2 * 2 * 2 * 128 * 128 * 4  # one global block, parts of 7 query blocks
+    assert lib.ssa_prefill_backward_workspace_size(ctypes.byref(a), ctypes.byref(w)) == \
+        ((rec + 255) // 256 * 256 + part + 255) // 256 * 256
+    assert lib.ssa_prefill_backward_workspace_size(None, ctypes.byref(w)) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(lse=None), ssa.SSA_ERR_INVALID),
+    (dict(dout=None), ssa.SSA_ERR_INVALID),
+    (dict(Hq=3), ssa.SSA_ERR_INVALID),
+    (dict(scale=0.0), ssa.SSA_ERR_INVALID),
+    (dict(dq=FAKE + 8), ssa.SSA_ERR_INVALID),
+    (dict(grad_dtype=7), ssa.SSA_ERR_INVALID),
+    (dict(Dqk=64, Dv=64), ssa.SSA_ERR_UNSUPPORTED),
+    (dict(dtype=ssa.DTYPE_F32), ssa.SSA_ERR_UNSUPPORTED),
+    (dict(q_stride=(ctypes.c_int64 * 3)(0, 1 << 26, 128)), ssa.SSA_ERR_UNSUPPORTED),
+])
+def test_backward_rejects(lib, over, code):
+    w = ssa.CWindow(128, 1, 7)
+    a = bwd_args(workspace=FAKE, workspace_bytes=1 << 40, **over)
+    assert lib.ssa_prefill_backward(ctypes.byref(a), ctypes.byref(w), None) == code
+    assert lib.ssa_last_error().decode() != ""
+
+
+def test_backward_workspace_rules(lib):
+    w = ssa.CWindow(128, 1, 7)
+    a = bwd_args()
+    need = lib.ssa_prefill_backward_workspace_size(ctypes.byref(a), ctypes.byref(w))
+    assert lib.ssa_prefill_backward(ctypes.byref(a), ctypes.byref(w), None) == ssa.SSA_ERR_WORKSPACE
+    a = bwd_args(workspace=FAKE, workspace_bytes=need - 1)
+    assert lib.ssa_prefill_backward(ctypes.byref(a), ctypes.byref(w), None) == ssa.SSA_ERR_WORKSPACE
+    a = bwd_args(workspace=FAKE + 16, workspace_bytes=need)
+    assert lib.ssa_prefill_backward(ctypes.byref(a), ctypes.byref(w), None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_prefill_backward(ctypes.byref(a), None, None) == ssa.SSA_ERR_INVALID
+
+
 def test_decode_workspace_size(lib):
     w = ssa.CWindow(128, 1, 7)
     a = mla_decode_args()
