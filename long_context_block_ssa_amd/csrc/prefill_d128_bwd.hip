@@ -319,10 +319,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 }
 
 // ---------------------------------------------------------------------------
-// dk, dv: one workgroup per (key block[, part], b, kv head), 4 waves x 32 keys
+// dk, dv: one workgroup per (key block[, part], b, kv head), 4 waves x 32 keys.
+// The grid holds the global blocks' parts first (n_part_items workgroups,
+// fp32 partials), then the local blocks, so one launch keeps every CU busy.
 // ---------------------------------------------------------------------------
-template <typename GradT, bool PARTIAL>
-__global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p) {
+template <typename GradT>
+__global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p, int n_part_items) {
   extern __shared__ u32x4 ring[];  // kDkdvLds bytes: the slab ring, then the record regions
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -333,8 +335,9 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p) {
   const int b = bh / p.Hkv, hk = bh % p.Hkv;
   const int L = p.L;
   // the key block and the query blocks [q_begin, q_end) that read it
+  const bool partial = static_cast<int>(blockIdx.x) < n_part_items;
   int kb, part = 0, q_begin, q_end;
-  if constexpr (PARTIAL) {
+  if (partial) {
     const int rest = static_cast<int>(blockIdx.x) / bh_count;
     part = rest % p.nparts;
     kb = rest / p.nparts;
@@ -342,7 +345,7 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p) {
     q_end = min(q_begin + p.n_local, p.nqb);
     if (q_begin >= q_end) return;  // a part past the last query block
   } else {
-    kb = p.n_global + static_cast<int>(blockIdx.x) / bh_count;
+    kb = p.n_global + (static_cast<int>(blockIdx.x) - n_part_items) / bh_count;
     q_begin = kb;
     q_end = min(kb + p.n_local, p.nqb);
   }
@@ -546,7 +549,7 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p) {
 
   if (key >= L) return;
   // accumulators: lane = key, register i of tile dt = channel 32dt + 8(i/4) + 4 h32 + (i%4)
-  if constexpr (PARTIAL) {
+  if (partial) {
     float* out = p.part + ((((static_cast<int64_t>(kb) * p.nparts + part) * p.B + b) * p.Hkv + hk) * 2) * kBlk * kD +
                  static_cast<int64_t>(key - kb * kBlk) * kD;
 #pragma unroll
@@ -616,21 +619,14 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int n_glob = min(p.n_global, p.nqb);
   const unsigned bh = static_cast<unsigned>(p.B) * p.Hkv;
-  if (p.nqb > n_glob) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dkdv_kernel<GradT, false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kDkdvLds);
-    if (e != hipSuccess) return e;
-    e = launch_kernel(bwd_dkdv_kernel<GradT, false>, dim3(static_cast<unsigned>(p.nqb - n_glob) * bh), dim3(kWaves * 64),
-                      kDkdvLds, stream, p);
-    if (e != hipSuccess) return e;
-  }
+  const int n_part_items = n_glob * p.nparts * static_cast<int>(bh);
+  const unsigned items = static_cast<unsigned>(n_part_items) + static_cast<unsigned>(p.nqb - n_glob) * bh;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dkdv_kernel<GradT>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kDkdvLds);
+  if (e != hipSuccess) return e;
+  e = launch_kernel(bwd_dkdv_kernel<GradT>, dim3(items), dim3(kWaves * 64), kDkdvLds, stream, p, n_part_items);
+  if (e != hipSuccess) return e;
   if (n_glob > 0) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dkdv_kernel<GradT, true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kDkdvLds);
-    if (e != hipSuccess) return e;
-    e = launch_kernel(bwd_dkdv_kernel<GradT, true>, dim3(static_cast<unsigned>(n_glob * p.nparts) * bh),
-                      dim3(kWaves * 64), kDkdvLds, stream, p);
-    if (e != hipSuccess) return e;
     const int64_t threads = static_cast<int64_t>(n_glob) * bh * 2 * kBlk * 32;
     e = launch_kernel(bwd_reduce_kernel<GradT>, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
                       stream, p, n_glob);
