@@ -255,8 +255,9 @@ def write_traffic(fetch_dir: str, write_dir: str, out_path: str):
 
 def short_kernel_name(name: str) -> str:
     """'void ssa::(anonymous namespace)::k<128, 128, false, 2, __bf16>(ssa::P)' -> 'k<128, 128, false, 2, __bf16>'."""
-    # the profiler's own demangler prints the template arguments <__bf16, true> as <bool _Accum, bool, E>
-    name = name.replace("<bool _Accum, bool, E>", "<__bf16, true>")
+    # the profiler's own demangler prints the leading template arguments <__bf16, true, ...> of the
+    # dense-layer instantiation as <bool _Accum, bool, E, ...>
+    name = name.replace("<bool _Accum, bool, E", "<__bf16, true")
     n = name.replace("void ", "").replace("ssa::(anonymous namespace)::", "").replace("ssa::", "")
     depth = 0
     for i, ch in enumerate(n):  # cut at the argument list (the first '(' outside template brackets)
