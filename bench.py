@@ -173,6 +173,104 @@ def cpu_baseline(budget_s: float = 25.0):
     }
 
 
+def cpu_rows_baseline():
+    """The float64 oracle on a small sample of every other row's workload, one
+    process and one BLAS thread, each reported in that row's unit (the work of
+    the sample over its wall time).  Inputs are synthetic of the same shapes;
+    the 576-wide rows use generator draws instead of the benchmark's
+    device-side ones (the values do not change the time)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(1)
+    except Exception:
+        limit = None
+    out = {}
+
+    def timed(name, unit, work, sample, fn):
+        t0 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t0
+        out[name] = {"value": work / dt / (1e12 if unit == "TFLOP/s" else 1e9), "unit": unit, "cores": 1,
+                     "kind": "oracle", "sample": sample, "seconds": dt}
+
+    f64 = lambda bits: synth.bf16_bits_to_f32(bits).astype(np.float64)
+    # a3 decode: 4 of the 64 sequences
+    B3, H3, D3, s3 = W3["B"], W3["H"], W3["D"], W3["seed"]
+    nd = 16
+    lens = synth.decode_seq_lens(s3, B3, W3["lo"], W3["hi"])[:nd]
+    fill = synth.decode_fill_blocks(lens, 128, 1, 7)
+    bt = np.full((nd, int(lens.max()) // 128 + 1), -1, np.int32)
+    kh, vh = [], []
+    for b, blocks in enumerate(fill):
+        for t in blocks:
+            bt[b, t] = len(kh)
+            kh.append(synth.page_chunk(s3, synth.K, b, t, H3, D3))
+            vh.append(synth.page_chunk(s3, synth.V, b, t, H3, D3))
+    kp, vp = f64(np.stack(kh)), f64(np.stack(vh))
+    q3 = f64(synth.decode_query(s3, nd, H3, D3))
+    timed("a3 ssa_decode", "GB/s", decode_bytes(lens, H3, H3, D3, D3),
+          f"{nd} of the 64 sequences of the decode workload",
+          lambda: oracle.decode(q3, kp, vp, bt, lens, 1 / math.sqrt(D3)))
+    # a2 inputs serve the dense, backward rows (two heads)
+    L2, H2, D2, s2 = W2["L"], W2["H"], W2["D"], W2["seed"]
+    q2 = f64(synth.seq_tensor(s2, synth.Q, 1, L2, H2, D2)[:, :, :2])
+    k2 = f64(synth.seq_tensor(s2, synth.K, 1, L2, H2, D2)[:, :, :2])
+    v2 = f64(synth.seq_tensor(s2, synth.V, 1, L2, H2, D2)[:, :, :2])
+    qb = L2 // 128 - 1
+    timed("a5 dense_causal", "TFLOP/s", 4 * D2 * sum(range(qb * 128 + 1, L2 + 1)) * 2,
+          "dense causal rows of the last query block, 2 of the 16 heads",
+          lambda: oracle.dense_causal_rows(q2[0, qb * 128:], qb * 128, k2[0], v2[0], 1 / math.sqrt(D2), [0, 1], 2))
+    g2 = f64(synth.seq_tensor(s2, 90, 1, L2, H2, D2)[:, :, :1])
+    timed("f3 ssa_backward", "TFLOP/s", bwd_flops(L2, 1, D2),
+          "whole backward of 1 of the 16 heads of the prefill workload",
+          lambda: oracle.ssa_backward(q2[:, :, :1], k2[:, :, :1], v2[:, :, :1], g2, 1 / math.sqrt(D2)))
+    # a6-a8 page selection: head 0 of the L=131072 workload
+    L5, H5, D5, M5, s5 = W5["L"], W5["H"], W5["D"], W5["M"], W5["seed"]
+    q5 = synth.bf16_bits_to_f32(synth.seq_tensor(s5, synth.Q, 1, L5, H5, D5)[:, :, :1])
+    k5 = synth.bf16_bits_to_f32(synth.seq_tensor(s5, synth.K, 1, L5, H5, D5)[:, :, :1])
+    sel = {}
+    timed("a6-a7 page_select", "GB/s", 2 * L5 * D5 * 2, "block sums, scores and top-8 lists of 1 of the 16 heads",
+          lambda: sel.update(r=oracle.page_select(q5, k5, top_m=M5)))
+    v5 = synth.bf16_bits_to_f32(synth.seq_tensor(s5, synth.V, 1, L5, H5, D5)[:, :, :1])
+    idx, cnt = sel["r"][:2]
+    qbs = list(range(L5 // 128 - 16, L5 // 128))
+    timed("a8 page_prefill", "TFLOP/s", 4 * D5 * sum(keys_page(i, M5) for qb_ in qbs for i in range(qb_ * 128, qb_ * 128 + 128)),
+          "rows of the last 16 query blocks, 1 of the 16 heads",
+          lambda: [oracle.block_list_rows(q5[0, qb_ * 128:(qb_ + 1) * 128].astype(np.float64), qb_ * 128, k5[0], v5[0],
+                                          1 / math.sqrt(D5), [0], 1, [list(idx[0, 0, qb_, :cnt[0, 0, qb_]])])
+                   for qb_ in qbs])
+    # a4: the 576-wide shape (one query block x 16 of the 128 heads; one decode sequence)
+    H4, DQ4, DV4 = W4["H"], W4["DQK"], W4["DV"]
+    L4s = 2048
+    c4 = f64(synth.seq_tensor(W4["seed"], synth.K, 1, L4s, 1, DQ4, mul=1 / 24))
+    q4 = f64(synth.seq_tensor(W4["seed"], synth.Q, 1, 128, 16, DQ4, mul=1 / 24))
+    timed("a4 mla_prefill", "TFLOP/s", 2 * (DQ4 + DV4) * sum(keys_ssa(i) for i in range(L4s - 128, L4s)) * 16,
+          "one query block at position 1920..2047 (a full window), 16 of the 128 heads",
+          lambda: oracle.ssa_rows(q4[0], L4s - 128, c4[0], c4[0, :, :, :DV4], 1 / 24, list(range(16)), 16))
+    pages = c4[0].reshape(L4s // 128, 128, 1, DQ4).transpose(0, 2, 1, 3)
+    q4d = f64(synth.decode_query(W4["seed"], 1, H4, DQ4, mul=1 / 24))
+    timed("a4 mla_decode", "GB/s", mla_decode_bytes([L4s], H4, DQ4, DV4), "one sequence of 2048 keys (a full window), 128 heads",
+          lambda: oracle.decode(q4d, pages, pages[..., :DV4], np.arange(L4s // 128, dtype=np.int32)[None],
+                                np.array([L4s]), 1 / 24))
+    # f1: one sequence's 2048-token chunk, 2 of the 16 heads
+    B6, T6, H6, D6, s6 = W6["B"], W6["T"], W6["H"], W6["D"], W6["seed"]
+    n6 = int(synth.decode_seq_lens(s6, B6, W6["lo"], W6["hi"])[0])
+    need = sorted({0} | set(range((n6 - T6) // 128 - 6, (n6 + 127) // 128)))
+    bt6 = np.full((1, (n6 + 127) // 128), -1, np.int32)
+    kh6, vh6 = [], []
+    for t in need:
+        bt6[0, t] = len(kh6)
+        kh6.append(synth.page_chunk(s6, synth.K, 0, t, H6, D6)[:2])
+        vh6.append(synth.page_chunk(s6, synth.V, 0, t, H6, D6)[:2])
+    q6 = f64(synth.seq_tensor(s6, synth.Q, 1, T6, H6, D6)[:, :, :2])
+    timed("f1 chunk_prefill", "TFLOP/s", chunk_flops([n6], T6, 2, D6), "the 2048-token chunk of 1 of the 16 sequences, 2 of the 16 heads",
+          lambda: oracle.chunk_prefill(q6, f64(np.stack(kh6)), f64(np.stack(vh6)), bt6, np.array([n6]), 1 / math.sqrt(D6)))
+    if limit is not None:
+        limit.unregister() if hasattr(limit, "unregister") else None
+    return out
+
+
 # ----------------------------------------------------------------------------
 # GPU part
 # ----------------------------------------------------------------------------
@@ -339,6 +437,11 @@ def main():
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_budget)
     if cpu:
         print(f"[bench] cpu baseline: {cpu['value']:.4f} TFLOP/s ({cpu['sample']})", flush=True)
+    cpu_rows = None if args.no_cpu_baseline else cpu_rows_baseline()
+    if cpu_rows:
+        for name, r in cpu_rows.items():
+            print(f"[bench] cpu baseline {name:20s} {r['value']:10.4f} {r['unit']:8s} ({r['seconds']:.1f} s: {r['sample']})",
+                  flush=True)
 
     import torch
     import long_context_block_ssa_amd as ssa
@@ -601,6 +704,7 @@ def main():
         "roofline_decode": kernels["ssa_decode"],
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "cpu_baseline_rows": cpu_rows,
     }
     print(json.dumps(out), flush=True)
 
