@@ -24,6 +24,7 @@ fraction of the MI355X peak (bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s).  Kernel
 times come from HIP events recorded on the stream the kernels run on.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py --zigzag     # f4: dense/SSA layer-stack prefill timing at 128K and 256K
 """
 from __future__ import annotations
 
@@ -414,6 +415,62 @@ def write_trace_summary(stats_csv: str, out_path: str, command: str):
     print("\n".join(lines))
 
 
+def zigzag(dev, ssa, torch):
+    """Layer-stack timing (timing only, synthetic weights): a decoder layer =
+    QKV projection, attention, output projection with residual, SwiGLU MLP with
+    residual (hidden 2048 = 16 heads x 128, MLP 5632; norms left out), its
+    attention either dense causal or SSA.  LoZA keeps half the layers dense
+    and makes the other half SSA, alternating (the ZigZag layout, "LoZA:
+    ZigZag sparse attention" page / QbitAI report), so a 50/50 stack costs
+    (t_dense + t_ssa) per layer pair against 2 t_dense for the all-dense model."""
+    H, D, FFN = 16, 128, 5632
+    hid = H * D
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    mk = lambda *shape: (torch.randn(*shape, device=dev, generator=g, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    w_qkv, w_o, w_13, w_2 = mk(hid, 3 * hid), mk(hid, hid), mk(hid, 2 * FFN), mk(FFN, hid)
+    res = {}
+    for L in (131072, 262144):
+        x0 = mk(L, hid)
+        o = torch.empty((1, L, H, D), dtype=torch.bfloat16, device=dev)
+        idx, cnt = ssa.block_index(L // 128, device=dev)
+        lists = ssa.lists_from_index(idx, cnt)
+
+        def layer(x, dense):
+            qkv = x @ w_qkv
+            q, k, v = (qkv[:, i * hid:(i + 1) * hid].view(1, L, H, D) for i in range(3))
+            if dense:
+                ssa.dense_causal(q, k, v, out=o)
+            else:
+                ssa.prefill(q, k, v, lists, out=o)
+            x = x + o.view(L, hid) @ w_o
+            h = x @ w_13
+            return x + (torch.nn.functional.silu(h[:, :FFN]) * h[:, FFN:]) @ w_2
+
+        times = {}
+        for dense in (False, True):
+            layer(x0, dense)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 2
+            e0.record()
+            for _ in range(reps):
+                layer(x0, dense)
+            e1.record()
+            torch.cuda.synchronize()
+            times["dense" if dense else "ssa"] = e0.elapsed_time(e1) / reps
+        td, ts = times["dense"], times["ssa"]
+        res[f"L{L}"] = {"dense_layer_ms": td, "ssa_layer_ms": ts, "layer_ratio": td / ts,
+                        "zigzag_50_50_prefill_speedup": 2 * td / (td + ts)}
+        print(f"[zigzag] L={L}: dense layer {td:.1f} ms, SSA layer {ts:.2f} ms, "
+              f"50/50 stack vs all-dense: {2 * td / (td + ts):.2f}x", flush=True)
+        del x0, o
+        torch.cuda.empty_cache()
+    print(json.dumps({"zigzag_prefill": res, "layer": {"hidden": hid, "heads": H, "head_dim": D, "mlp": FFN,
+                                                       "dtype": "bf16", "weights": "synthetic N(0, 0.02^2)"}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -426,6 +483,7 @@ def main():
                     "for profiling one kernel -- the JSON line is printed only for a full run")
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="summarise two rocprofv3 --pmc runs into a traffic file and exit")
+    ap.add_argument("--zigzag", action="store_true", help="f4: dense/SSA layer-stack prefill timing and exit")
     ap.add_argument("--trace-summary", nargs=3, metavar=("KERNEL_STATS_CSV", "OUT", "COMMAND"),
                     help="summarise a rocprofv3 --kernel-trace --stats run into a short text file and exit")
     args = ap.parse_args()
@@ -455,6 +513,9 @@ def main():
     ssa.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.zigzag:
+        zigzag(dev, ssa, torch)
+        return
 
     def up(bits, head_major=True):
         t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
