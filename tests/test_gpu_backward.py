@@ -57,6 +57,8 @@ def run_case(lib, name, B, L, Hq, Hkv, win=(128, 1, 7), layout="blhd", grad_dtyp
     ("L2100-bhld-bf16", 2, 2100, 2, 2, (128, 1, 7), "bhld", None),      # ragged end, bf16 gradients
     ("L2500-2g3l", 1, 2500, 2, 1, (128, 2, 3), "blhd", torch.float32),   # two global blocks, 3 local
     ("L1", 1, 1, 1, 1, (128, 1, 7), "blhd", torch.float32),
+    ("L1700-0g6l", 1, 1700, 2, 2, (128, 0, 6), "blhd", torch.float32),  # no global block: no partials
+    ("L1500-1l", 1, 1500, 2, 2, (128, 1, 1), "blhd", torch.float32),    # block 0 and the own block only
     ("L129", 1, 129, 1, 1, (128, 1, 7), "blhd", torch.float32),
 ])
 def test_backward_parity(lib, name, B, L, Hq, Hkv, win, layout, gd):

@@ -83,6 +83,25 @@ def test_chunk_small_nan_poisoned(lib, T, lens, Hq, Hkv, out_f32):
     check_close(to_f64(lse), rl, f"{name} lse")
 
 
+@pytest.mark.parametrize("win,T,lens", [
+    ((128, 2, 3), 300, [300, 1100, 2600]),   # two global blocks, three local
+    ((128, 0, 6), 200, [200, 900, 1999]),    # no global block
+    ((128, 4, 12), 700, [700, 3000]),        # 16-block window
+])
+def test_chunk_other_windows(lib, win, T, lens):
+    name = f"ssa_prefill_chunk window={win} T={T} lens={lens}"
+    say(name)
+    dev, host = build_chunk_case(71 + T, lens, T, 2, 2)
+    idx, cnt = lib.block_index(dev["bt"].shape[1], lib.Window(*win))
+    o, lse = lib.prefill_chunk(dev["q"], dev["k"], dev["v"], dev["bt"], dev["sl"], lib.lists_from_index(idx, cnt),
+                               with_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.chunk_prefill(host["q"], host["k"], host["v"], host["bt"], host["sl"], 1 / math.sqrt(128),
+                                  oracle.Window(*win))
+    check_close(to_f64(o), ro, f"{name} o")
+    check_close(to_f64(lse), rl, f"{name} lse")
+
+
 def test_chunk_invalid_rows_are_nan(lib):
     """A sequence shorter than the chunk gets NaN rows; a page outside the pool
     turns the rows of the query blocks whose window lists it into NaN (block 0's
