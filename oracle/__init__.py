@@ -27,6 +27,8 @@ against the sources by eye:
   the comparison layer; written on its own, without the window code, so that
   "SSA equals dense when L <= 1024" is a real check.
 * ``decode`` -- one new query per sequence over a paged cache.
+* ``dense_decode`` -- one new query per sequence over every cached key (the
+  decode step of the dense layers, for the layer-stack comparison).
 * ``chunk_prefill`` -- a chunk of T new queries per sequence over a paged
   cache, each with the window of its own block (the step between prefill and
   decode: a long prompt prefilled in pieces).
@@ -38,7 +40,8 @@ against the sources by eye:
 Parity status: every function here is pinned by the CPU tests (brute force on
 tiny inputs, the dense special case against torch's own attention routine,
 closed-form key counts, structural one-hot outputs, decode == last prefill row,
-chunked prefill == brute force over the cached sequence, gradients == central
+chunked prefill == brute force over the cached sequence, dense decode == the
+last row of the (torch-pinned) dense causal attention, gradients == central
 finite differences of the forward and == torch autograd with an explicit mask,
 exact rational re-scoring of page selections).  No function is "parity
 unpinned".
@@ -55,6 +58,7 @@ from .ssa import (  # noqa: F401
     dense_causal_rows,
     dense_causal,
     decode,
+    dense_decode,
     chunk_prefill,
     block_sums,
     page_select,

@@ -257,6 +257,31 @@ def decode(q, k_pages, v_pages, block_table, seq_lens, scale, win: Window = DEFA
     return o, lse
 
 
+def dense_decode(q, k_pages, v_pages, block_table, seq_lens, scale, batches=None):
+    """Dense (full causal) attention of one new query per sequence over a paged
+    cache: every cached key 0 .. n-1 -- the decode step of the layers LoZA keeps
+    dense ("LoZA: ZigZag sparse attention" page, section 2.1, equation (1), with
+    the causal rule of section 2.2.1).  Layouts as for ``decode``."""
+    B, Hq, _ = q.shape
+    Hkv = k_pages.shape[1]
+    bs = k_pages.shape[2]
+    batches = range(B) if batches is None else batches
+    o = np.full((B, Hq, v_pages.shape[3]), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    for b in batches:
+        n = int(seq_lens[b])
+        blocks = range((n + bs - 1) // bs)
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            kr = np.concatenate([np.asarray(k_pages[int(block_table[b, t]), g, :min(bs, n - t * bs)], np.float64)
+                                 for t in blocks])
+            vr = np.concatenate([np.asarray(v_pages[int(block_table[b, t]), g, :min(bs, n - t * bs)], np.float64)
+                                 for t in blocks])
+            ob, lb = _attend(np.asarray(q[b, h], np.float64)[None, :], kr, vr, np.ones((1, kr.shape[0]), bool), scale)
+            o[b, h], lse[b, h] = ob[0], lb[0]
+    return o, lse
+
+
 def chunk_prefill(q, k_pages, v_pages, block_table, seq_lens, scale, win: Window = DEFAULT_WINDOW,
                   batches=None):
     """A chunk of T new queries per sequence over a paged cache (chunked prefill).

@@ -9,6 +9,7 @@
 * structural outputs: one-hot values per block, constant values, the first row;
 * decode of a sequence of length n == row n - 1 of the prefill on the same data;
 * a chunk of queries over a paged cache == brute force over the cached sequence;
+* dense decode over a paged cache == the last row of the dense causal attention;
 * gradients == central finite differences of the forward on tiny inputs, and ==
   torch's autograd through an explicitly masked softmax at the real window;
 * page selection re-decided with exact rationals on tiny inputs.
@@ -275,6 +276,22 @@ def test_decode_equals_prefill_last_row(n, Hq, Hkv):
     bt = np.full((1, 16), -1, np.int32)
     bt[0, :len(perm)] = perm
     o_d, lse_d = oracle.decode(q[:, n - 1], kp, vp, bt, np.array([n]), 0.3)
+    np.testing.assert_allclose(o_d[0], o_p[0, n - 1], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse_d[0], lse_p[0, :, n - 1], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("n,Hq,Hkv", [(1, 2, 2), (300, 4, 2), (1500, 2, 1)])
+def test_dense_decode_equals_dense_last_row(n, Hq, Hkv):
+    rng = np.random.default_rng(700 + n)
+    D, Dv = 8, 6
+    q = rng.standard_normal((1, n, Hq, D))
+    k = rng.standard_normal((1, n, Hkv, D))
+    v = rng.standard_normal((1, n, Hkv, Dv))
+    o_p, lse_p = oracle.dense_causal(q, k, v, 0.3)
+    kp, vp, perm = _paged_kv(k[0], v[0], 128, rng)
+    bt = np.full((1, 16), -1, np.int32)
+    bt[0, :len(perm)] = perm
+    o_d, lse_d = oracle.dense_decode(q[:, n - 1], kp, vp, bt, np.array([n]), 0.3)
     np.testing.assert_allclose(o_d[0], o_p[0, n - 1], rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(lse_d[0], lse_p[0, :, n - 1], rtol=1e-12, atol=1e-13)
 
