@@ -466,9 +466,50 @@ def zigzag(dev, ssa, torch):
               f"50/50 stack vs all-dense: {2 * td / (td + ts):.2f}x", flush=True)
         del x0, o
         torch.cuda.empty_cache()
-    print(json.dumps({"zigzag_prefill": res, "layer": {"hidden": hid, "heads": H, "head_dim": D, "mlp": FFN,
-                                                       "dtype": "bf16", "weights": "synthetic N(0, 0.02^2)"}}),
-          flush=True)
+    # decode side: the a3 batch (64 sequences at ~U[64K, 128K]) one token per sequence; the
+    # dense layer reads every cached key (ssa_decode_dense), the SSA layer its window
+    # (ssa_decode); the cache contents do not change the time (left uninitialised)
+    B3 = W3["B"]
+    lens = synth.decode_seq_lens(W3["seed"], B3, W3["lo"], W3["hi"])
+    bt, P = synth.decode_block_table(W3["seed"], lens, 128)
+    kp = torch.empty((P, H, 128, D), dtype=torch.bfloat16, device=dev)
+    vp = torch.empty_like(kp)
+    btd, sl = torch.from_numpy(bt).to(dev), torch.from_numpy(lens).to(dev)
+    od = torch.empty((B3, H, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((ssa.decode_workspace_size(B3, H, D, D) + 256,), dtype=torch.uint8, device=dev)
+    x0 = mk(B3, hid)
+
+    def dlayer(x, dense):
+        qkv = x @ w_qkv
+        q = qkv[:, :hid].view(B3, H, D)
+        if dense:
+            ssa.decode_dense(q, kp, vp, btd, sl, out=od)
+        else:
+            ssa.decode(q, kp, vp, btd, sl, out=od)
+        x = x + od.view(B3, hid) @ w_o
+        h = x @ w_13
+        return x + (torch.nn.functional.silu(h[:, :FFN]) * h[:, FFN:]) @ w_2
+
+    dt = {}
+    for dense in (False, True):
+        dlayer(x0, dense)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            dlayer(x0, dense)
+        e1.record()
+        torch.cuda.synchronize()
+        dt["dense" if dense else "ssa"] = e0.elapsed_time(e1) / reps
+    td, ts = dt["dense"], dt["ssa"]
+    dec = {"batch": B3, "mean_context": float(np.mean(lens)), "dense_layer_ms": td, "ssa_layer_ms": ts,
+           "layer_ratio": td / ts, "zigzag_50_50_decode_speedup": 2 * td / (td + ts)}
+    print(f"[zigzag] decode batch {B3} at mean context {np.mean(lens):.0f}: dense layer {td:.3f} ms, "
+          f"SSA layer {ts:.3f} ms, 50/50 stack vs all-dense: {2 * td / (td + ts):.2f}x", flush=True)
+    print(json.dumps({"zigzag_prefill": res, "zigzag_decode": dec,
+                      "layer": {"hidden": hid, "heads": H, "head_dim": D, "mlp": FFN, "dtype": "bf16",
+                                "weights": "synthetic N(0, 0.02^2)"}}), flush=True)
 
 
 def main():

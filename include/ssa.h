@@ -300,6 +300,25 @@ typedef struct ssa_chunk_args {
 int ssa_prefill_chunk(const ssa_chunk_args* a, const ssa_block_lists* lists, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * ssa_decode_dense -- the decode step of a dense layer over the same paged
+ * cache: the new query reads every cached key 0 .. n-1 (softmax attention of
+ * equation (1) of the ZigZag page with the causal rule of its section 2.2.1).
+ * LoZA keeps half of its layers dense (QbitAI report on LongCat LoZA), so a
+ * layer stack alternates this with ssa_decode.  Operands and the handling of
+ * bad lengths and pages as for ssa_decode (every block of the sequence is
+ * read, so any page of it outside the pool makes the row NaN).  Workspace: at
+ * least ssa_decode_dense_workspace_size bytes, 256-byte aligned (per
+ * sequence, query head and group of 16 blocks, an fp32 piece of D + 2
+ * values, merged exactly by a second kernel).
+ * Supported (dtype, Dqk, Dv): (BF16, 64, 64), (BF16, 128, 128), Hq/Hkv <= 16.
+ * ------------------------------------------------------------------------- */
+int ssa_decode_dense(const ssa_decode_args* a, void* stream);
+
+/* B * Hq * ceil(max_blocks / 16) * (Dv + 2) * 4 bytes, rounded up to 256; 0
+ * for NULL arguments or unsupported shapes. */
+size_t ssa_decode_dense_workspace_size(const ssa_decode_args* a);
+
+/* ---------------------------------------------------------------------------
  * ssa_page_select -- block lists for the page-selected variant (LongCat
  * sparse attention article, section 3: streaming-aware indexing keeps the
  * sink and the local window; hierarchical indexing scores 128-token pages

@@ -28,8 +28,8 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 
 # every symbol include/ssa.h declares
 EXPORTS = (
-    "ssa_block_index", "ssa_block_index_seq", "ssa_prefill", "ssa_dense_causal", "ssa_prefill_chunk", "ssa_prefill_backward", "ssa_prefill_backward",
-    "ssa_prefill_backward_workspace_size", "ssa_decode",
+    "ssa_block_index", "ssa_block_index_seq", "ssa_prefill", "ssa_dense_causal", "ssa_prefill_chunk", "ssa_prefill_backward", "ssa_decode_dense", "ssa_prefill_backward",
+    "ssa_prefill_backward_workspace_size", "ssa_decode", "ssa_decode_dense", "ssa_decode_dense_workspace_size",
     "ssa_decode_workspace_size", "ssa_page_select", "ssa_page_select_workspace_size", "ssa_last_error", "ssa_version",
 )
 
@@ -158,6 +158,9 @@ def load(path: str = LIB_PATH):
     lib.ssa_prefill_backward_workspace_size.argtypes = [ctypes.POINTER(CBwdArgs), ctypes.POINTER(CWindow)]
     lib.ssa_prefill_backward_workspace_size.restype = ctypes.c_size_t
     lib.ssa_decode.argtypes = [ctypes.POINTER(CDecodeArgs), ctypes.POINTER(CWindow), vp]
+    lib.ssa_decode_dense.argtypes = [ctypes.POINTER(CDecodeArgs), vp]
+    lib.ssa_decode_dense_workspace_size.argtypes = [ctypes.POINTER(CDecodeArgs)]
+    lib.ssa_decode_dense_workspace_size.restype = ctypes.c_size_t
     lib.ssa_decode_workspace_size.argtypes = [ctypes.POINTER(CDecodeArgs), ctypes.POINTER(CWindow)]
     lib.ssa_decode_workspace_size.restype = ctypes.c_size_t
     lib.ssa_page_select_workspace_size.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CWindow)]
@@ -435,6 +438,39 @@ def decode(q, k_pages, v_pages, block_table, seq_lens, scale=None, window: Windo
         off = (-base) % 256
         a.workspace, a.workspace_bytes = base + off, max(workspace.numel() - off, 0)
     _check(lib.ssa_decode(ctypes.byref(a), ctypes.byref(w), _stream(stream)))
+    return out, lse
+
+
+def decode_dense(q, k_pages, v_pages, block_table, seq_lens, scale=None, out=None, with_lse=False, lse=None,
+                 workspace=None, stream=None):
+    """ssa_decode_dense: the new query over every cached key.  Returns (o [B, Hq, Dv], lse or None)."""
+    lib = load()
+    B, Hq, Dqk = q.shape
+    P, Hkv, page, _ = k_pages.shape
+    Dv = v_pages.shape[3]
+    if out is None:
+        out = torch.empty((B, Hq, Dv), dtype=q.dtype, device=q.device)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    a = CDecodeArgs()
+    a.dtype = _dtype_code(q.dtype)
+    a.B, a.Hq, a.Hkv, a.Dqk, a.Dv = B, Hq, Hkv, Dqk, Dv
+    a.page_size, a.num_pages, a.max_blocks = page, P, block_table.shape[1]
+    a.scale = float(1.0 / math.sqrt(Dqk) if scale is None else scale)
+    a.q, a.k_pages, a.v_pages = _ptr(q), _ptr(k_pages), _ptr(v_pages)
+    a.block_table, a.seq_lens, a.o, a.lse = _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse)
+    a.q_stride = (ctypes.c_int64 * 2)(q.stride(0), q.stride(1))
+    a.k_stride = (ctypes.c_int64 * 3)(k_pages.stride(0), k_pages.stride(1), k_pages.stride(2))
+    a.v_stride = (ctypes.c_int64 * 3)(v_pages.stride(0), v_pages.stride(1), v_pages.stride(2))
+    a.o_stride = (ctypes.c_int64 * 2)(out.stride(0), out.stride(1))
+    a.bt_stride = block_table.stride(0)
+    need = int(lib.ssa_decode_dense_workspace_size(ctypes.byref(a)))
+    if workspace is None:
+        workspace = torch.empty((need + 256,), dtype=torch.uint8, device=q.device)
+    base = workspace.data_ptr()
+    off = (-base) % 256
+    a.workspace, a.workspace_bytes = base + off, max(workspace.numel() - off, 0)
+    _check(lib.ssa_decode_dense(ctypes.byref(a), _stream(stream)))
     return out, lse
 
 

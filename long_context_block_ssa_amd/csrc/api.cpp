@@ -384,8 +384,18 @@ size_t ssa_decode_workspace_size(const ssa_decode_args* a, const ssa_window* win
   return (ssa::decode_mla_workspace_bytes(a->B, a->Hq, win->n_global + win->n_local) + 255) / 256 * 256;
 }
 
-int ssa_decode(const ssa_decode_args* a, const ssa_window* win, void* stream) {
-  const char* who = "ssa_decode";
+size_t ssa_decode_dense_workspace_size(const ssa_decode_args* a) {
+  if (!a || a->B < 1 || a->Hq < 1 || a->max_blocks < 1) return 0;
+  if (!((a->Dqk == 64 && a->Dv == 64) || (a->Dqk == 128 && a->Dv == 128))) return 0;
+  return (ssa::decode_dense_workspace_bytes(a->B, a->Hq, a->max_blocks, a->Dqk) + 255) / 256 * 256;
+}
+
+// ssa_decode and ssa_decode_dense: shared validation and launch.  dense: every
+// cached block, through the workspace (the window is unused)
+static int decode_impl(const ssa_decode_args* a, const ssa_window* win, void* stream, bool dense) {
+  const char* who = dense ? "ssa_decode_dense" : "ssa_decode";
+  const ssa_window dense_win{128, 0, 1};
+  if (dense) win = &dense_win;
   if (!a) return fail(SSA_ERR_INVALID, "%s: args is NULL", who);
   if (!valid_window(win, who, 16)) return SSA_ERR_INVALID;
   if (a->dtype != SSA_DTYPE_BF16) return fail(SSA_ERR_UNSUPPORTED, "%s: only BF16 caches are supported", who);
@@ -416,7 +426,7 @@ int ssa_decode(const ssa_decode_args* a, const ssa_window* win, void* stream) {
                 a->max_blocks);
   const bool mha = (a->Dqk == 64 && a->Dv == 64) || (a->Dqk == 128 && a->Dv == 128);
   const bool mla = a->Dqk == 576 && a->Dv == 512 && a->Hkv == 1 && a->Hq % 16 == 0;
-  if (!(mha && a->Hq / a->Hkv <= 16) && !mla)
+  if (!(mha && a->Hq / a->Hkv <= 16) && !(mla && !dense))
     return fail(SSA_ERR_UNSUPPORTED, "%s: no kernel for Dqk=%d Dv=%d Hq=%d Hkv=%d", who, a->Dqk, a->Dv, a->Hq,
                 a->Hkv);
   if (win->block_size != 128) return fail(SSA_ERR_UNSUPPORTED, "%s: block_size must be 128", who);
@@ -426,7 +436,7 @@ int ssa_decode(const ssa_decode_args* a, const ssa_window* win, void* stream) {
   if (mha && row_span > INT32_MAX)
     return fail(SSA_ERR_UNSUPPORTED, "%s: slot strides (%lld, %lld) put a page's rows beyond 2^31 bytes", who,
                 static_cast<long long>(a->k_stride[2]), static_cast<long long>(a->v_stride[2]));
-  const size_t need = ssa_decode_workspace_size(a, win);
+  const size_t need = dense ? ssa_decode_dense_workspace_size(a) : ssa_decode_workspace_size(a, win);
   if (need > 0) {
     if (!a->workspace || a->workspace_bytes < need)
       return fail(SSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
@@ -463,10 +473,18 @@ int ssa_decode(const ssa_decode_args* a, const ssa_window* win, void* stream) {
   p.scale = a->scale;
   p.c1 = static_cast<float>(static_cast<double>(a->scale) * 1.4426950408889634);
   p.work = need > 0 ? static_cast<float*>(a->workspace) : nullptr;
-  hipError_t e = ssa::launch_decode(p, a->Dqk, a->Dv, as_stream(stream));
+  p.nsplit = static_cast<int32_t>(ceil_div(a->max_blocks, 16));
+  hipError_t e = dense ? ssa::launch_decode_dense(p, a->Dqk, as_stream(stream))
+                       : ssa::launch_decode(p, a->Dqk, a->Dv, as_stream(stream));
   if (e == hipErrorNotSupported) return fail(SSA_ERR_UNSUPPORTED, "%s: no kernel for Dqk=%d Dv=%d in this build", who, a->Dqk, a->Dv);
   return device_status(e, who);
 }
+
+int ssa_decode(const ssa_decode_args* a, const ssa_window* win, void* stream) {
+  return decode_impl(a, win, stream, false);
+}
+
+int ssa_decode_dense(const ssa_decode_args* a, void* stream) { return decode_impl(a, nullptr, stream, true); }
 
 size_t ssa_page_select_workspace_size(const ssa_attn_args* a, const ssa_window* win) {
   if (!a || !win || a->B < 1 || a->L < 1 || a->Hq < 1 || a->Hkv < 1 || a->Dqk < 1 || win->block_size < 1) return 0;

@@ -112,7 +112,8 @@ struct DecodeParams {
   int32_t n_global, n_local;
   float c1;
   float scale;
-  float* work;  // Dqk = 576 only: per-(sequence, head, window slot) partials
+  float* work;  // Dqk = 576, and dense decode: per-(sequence, head, slot) partials
+  int32_t nsplit;  // dense decode: block groups per sequence (the partials' slots)
 };
 
 struct PageSelectParams {
@@ -156,6 +157,11 @@ size_t prefill_backward_workspace_bytes(int32_t B, int32_t L, int32_t Hq, int32_
                                         int32_t n_local);
 
 hipError_t launch_decode(const DecodeParams& p, int dqk, int dv, hipStream_t stream);
+
+// Dense decode (every cached key), MHA/GQA d = 64/128: nsplit groups of 16
+// blocks per (sequence, kv head), partials in p.work, then a merge
+hipError_t launch_decode_dense(const DecodeParams& p, int d, hipStream_t stream);
+size_t decode_dense_workspace_bytes(int32_t B, int32_t Hq, int32_t max_blocks, int32_t d);
 
 // Dqk = 576, Dv = 512 with one kv head; called by launch_decode.  Needs
 // p.work of decode_mla_workspace_bytes(B, Hq, n_global + n_local) bytes.

@@ -103,7 +103,11 @@ __device__ __forceinline__ u32x4 ldg_stream(const char* base, uint32_t off) {
 // the compiler counts the loads in flight exactly instead of draining them
 // at every branch.  MAXT: the largest workgroup the instantiation serves; at
 // most 128 registers per wave, so two 8-wave workgroups share a CU.
-template <int D, int MAXT>
+// DENSE: every cached block, in groups of nwaves blocks: workgroup
+// (split, sequence, kv head) reads blocks split*nwaves + wave and writes its
+// merged (o unnormalised, m, l) per query head to p.work; a merge kernel
+// combines the groups.
+template <int D, int MAXT, bool DENSE = false>
 __global__ __launch_bounds__(MAXT) __attribute__((amdgpu_waves_per_eu(4))) void decode_mha_kernel(DecodeParams p) {
   constexpr int CPR = D / 8;      // lanes per key row (16 B each)
   constexpr int KPI = 64 / CPR;   // keys per wave-wide load
@@ -116,7 +120,9 @@ __global__ __launch_bounds__(MAXT) __attribute__((amdgpu_waves_per_eu(4))) void 
   const int lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kr = lane / CPR, cc = lane % CPR;
-  const int b = blockIdx.x / p.Hkv, hk = blockIdx.x % p.Hkv;
+  const int hk = blockIdx.x % p.Hkv;
+  const int b = DENSE ? (blockIdx.x / p.Hkv) % p.B : blockIdx.x / p.Hkv;
+  const int split = DENSE ? blockIdx.x / (p.Hkv * p.B) : 0;
   const int n = p.seq_lens[b];
   if (threadIdx.x == 0) bad = 0;
   __syncthreads();
@@ -125,11 +131,16 @@ __global__ __launch_bounds__(MAXT) __attribute__((amdgpu_waves_per_eu(4))) void 
   int blk = -1;
   const bool len_ok = n >= 1 && n <= p.max_blocks * kPage;
   if (len_ok) {
-    const int qb = (n - 1) / kPage;
-    const int g_end = min(p.n_global, qb + 1);
-    const int l_begin = max(g_end, qb - p.n_local + 1);
-    const int cntw = g_end + (qb - l_begin + 1);
-    if (wave < cntw) blk = wave < g_end ? wave : l_begin + (wave - g_end);
+    if constexpr (DENSE) {
+      const int cand = split * nwaves + wave;
+      if (cand < (n + kPage - 1) / kPage) blk = cand;
+    } else {
+      const int qb = (n - 1) / kPage;
+      const int g_end = min(p.n_global, qb + 1);
+      const int l_begin = max(g_end, qb - p.n_local + 1);
+      const int cntw = g_end + (qb - l_begin + 1);
+      if (wave < cntw) blk = wave < g_end ? wave : l_begin + (wave - g_end);
+    }
   } else if (threadIdx.x == 0) {
     bad = 1;
   }
@@ -240,17 +251,80 @@ __global__ __launch_bounds__(MAXT) __attribute__((amdgpu_waves_per_eu(4))) void 
         lsum = __builtin_fmaf(part[w][D + 1], sc, lsum);
       }
       const float nan = __builtin_nanf("");
-      const float out = all_bad ? nan : acc / lsum;
-      __bf16* op = static_cast<__bf16*>(p.o) + b * p.os_b + hq * p.os_h;
-      op[d] = static_cast<__bf16>(out);
-      if (d == 0 && p.lse)
-        p.lse[static_cast<int64_t>(b) * p.Hq + hq] = all_bad ? nan : M * p.scale + __builtin_amdgcn_logf(lsum) * kLn2;
+      if constexpr (DENSE) {
+        // this group's piece: o relative to M, then M and l (l = NaN marks a bad row)
+        float* w = p.work + ((static_cast<int64_t>(b) * p.Hq + hq) * p.nsplit + split) * (D + 2);
+        w[d] = acc;
+        if (d == 0) {
+          w[D] = M;
+          w[D + 1] = all_bad ? nan : lsum;
+        }
+      } else {
+        const float out = all_bad ? nan : acc / lsum;
+        __bf16* op = static_cast<__bf16*>(p.o) + b * p.os_b + hq * p.os_h;
+        op[d] = static_cast<__bf16>(out);
+        if (d == 0 && p.lse)
+          p.lse[static_cast<int64_t>(b) * p.Hq + hq] = all_bad ? nan : M * p.scale + __builtin_amdgcn_logf(lsum) * kLn2;
+      }
     }
     __syncthreads();
   }
 }
 
+// Dense decode merge: one wave per (sequence, query head) combines the
+// groups' pieces, M = max m_s, o = sum o_s e^(m_s - M) / sum l_s e^(m_s - M)
+// (the exact merge of max-subtracted softmax pieces, CSA/HCA tutorial page,
+// section 7.1); a NaN l in any group makes the row NaN.
+template <int D>
+__global__ __launch_bounds__(64) void decode_dense_merge_kernel(DecodeParams p) {
+  const int b = blockIdx.x / p.Hq, hq = blockIdx.x % p.Hq, lane = threadIdx.x;
+  const float* w = p.work + (static_cast<int64_t>(b) * p.Hq + hq) * p.nsplit * (D + 2);
+  float M = kNegInf;
+  bool bad = false;
+  for (int s = 0; s < p.nsplit; ++s) {
+    M = fmaxf(M, w[s * (D + 2) + D]);
+    bad |= __builtin_isnan(w[s * (D + 2) + D + 1]);
+  }
+  constexpr int PER = D / 64;
+  float acc[PER], lsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  for (int s = 0; s < p.nsplit; ++s) {
+    const float ms = w[s * (D + 2) + D];
+    if (ms == kNegInf) continue;  // a group with no key
+    const float sc = __builtin_amdgcn_exp2f((ms - M) * p.c1);
+    lsum = __builtin_fmaf(w[s * (D + 2) + D + 1], sc, lsum);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(w[s * (D + 2) + lane + 64 * i], sc, acc[i]);
+  }
+  const float nan = __builtin_nanf("");
+  __bf16* op = static_cast<__bf16*>(p.o) + b * p.os_b + hq * p.os_h;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) op[lane + 64 * i] = static_cast<__bf16>(bad ? nan : acc[i] / lsum);
+  if (lane == 0 && p.lse)
+    p.lse[static_cast<int64_t>(b) * p.Hq + hq] = bad ? nan : M * p.scale + __builtin_amdgcn_logf(lsum) * kLn2;
+}
+
 }  // namespace
+
+constexpr int kDenseGroup = 16;  // blocks per dense-decode workgroup (16 waves)
+
+size_t decode_dense_workspace_bytes(int32_t B, int32_t Hq, int32_t max_blocks, int32_t d) {
+  const int64_t nsplit = (static_cast<int64_t>(max_blocks) + kDenseGroup - 1) / kDenseGroup;
+  return static_cast<size_t>(static_cast<int64_t>(B) * Hq * nsplit * (d + 2) * sizeof(float));
+}
+
+hipError_t launch_decode_dense(const DecodeParams& p, int d, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(p.nsplit) * p.B * p.Hkv);
+  const dim3 block(64 * kDenseGroup);
+  hipError_t e = d == 128 ? launch_kernel(decode_mha_kernel<128, 1024, true>, grid, block, 0, stream, p)
+               : d == 64  ? launch_kernel(decode_mha_kernel<64, 1024, true>, grid, block, 0, stream, p)
+                          : hipErrorNotSupported;
+  if (e != hipSuccess) return e;
+  const dim3 mgrid(static_cast<unsigned>(p.B) * p.Hq);
+  return d == 128 ? launch_kernel(decode_dense_merge_kernel<128>, mgrid, dim3(64), 0, stream, p)
+                  : launch_kernel(decode_dense_merge_kernel<64>, mgrid, dim3(64), 0, stream, p);
+}
 
 hipError_t launch_decode(const DecodeParams& p, int dqk, int dv, hipStream_t stream) {
   if (dqk == 576 && dv == 512) return launch_decode_mla(p, stream);

@@ -283,6 +283,19 @@ def test_backward_workspace_rules(lib):
     assert lib.ssa_prefill_backward(ctypes.byref(a), None, None) == ssa.SSA_ERR_INVALID
 
 
+def test_decode_dense_rules(lib):
+    a = decode_args()  # B=2, Hq=4, 128/128, max_blocks 5
+    need = lib.ssa_decode_dense_workspace_size(ctypes.byref(a))
+    assert need == (2 * 4 * 1 * 130 * 4 + 255) // 256 * 256
+    assert lib.ssa_decode_dense_workspace_size(None) == 0
+    assert lib.ssa_decode_dense(ctypes.byref(a), None) == ssa.SSA_ERR_WORKSPACE
+    a = decode_args(workspace=FAKE + 16, workspace_bytes=need)
+    assert lib.ssa_decode_dense(ctypes.byref(a), None) == ssa.SSA_ERR_INVALID
+    a = mla_decode_args(workspace=FAKE, workspace_bytes=1 << 30)
+    assert lib.ssa_decode_dense(ctypes.byref(a), None) == ssa.SSA_ERR_UNSUPPORTED
+    assert "ssa_decode_dense" in lib.ssa_last_error().decode()
+
+
 def test_decode_workspace_size(lib):
     w = ssa.CWindow(128, 1, 7)
     a = mla_decode_args()

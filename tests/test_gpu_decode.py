@@ -177,3 +177,59 @@ def test_decode_structural_onehot(lib):
             c = (i % 128 + 1) if t == qb else (128 if (t == 0 or t >= qb - 6) else 0)
             want[t % D] += c / nk
         assert np.abs(o[b, 0] - want).max() <= 2 ** -8, b
+
+
+# ---------------------------------------------------------------------------
+# dense decode (every cached key; the dense layers of a layer stack)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 4, 2), (64, 2, 2)])
+def test_decode_dense_small(lib, D, Hq, Hkv):
+    lens = [1, 2, 127, 128, 129, 1000, 2049, 5000]
+    dev, host = build_case(31, len(lens), Hq, Hkv, D, lens, head=1, tail=64)  # every block filled
+    say(f"ssa_decode_dense D={D} Hq={Hq} Hkv={Hkv}")
+    o, lse = lib.decode_dense(dev["q"], dev["k"], dev["v"], dev["bt"], dev["sl"], with_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.dense_decode(host["q"], host["k"], host["v"], host["bt"], host["sl"], 1 / math.sqrt(D))
+    check_close(to_f64(o), ro, f"dense decode D={D} o")
+    check_close(to_f64(lse), rl, f"dense decode D={D} lse")
+
+
+def test_decode_dense_bad_rows(lib):
+    lens = [300, 0, 900]
+    dev, host = build_case(32, 3, 2, 2, 128, [300, 1, 900], head=1, tail=64)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    bt = dev["bt"].clone()
+    bt[2, 3] = 10 ** 6  # a page outside the pool in sequence 2
+    say("ssa_decode_dense bad rows")
+    o, lse = lib.decode_dense(dev["q"], dev["k"], dev["v"], bt, sl, with_lse=True)
+    torch.cuda.synchronize()
+    og = to_f64(o)
+    assert np.isnan(og[1]).all() and np.isnan(og[2]).all() and np.isnan(to_f64(lse)[[1, 2]]).all()
+    ro, rl = oracle.dense_decode(host["q"], host["k"], host["v"], host["bt"], np.array(lens), 1 / math.sqrt(128),
+                                 batches=[0])
+    check_close(og[0], ro[0], "dense decode bad-rows case, row 0")
+
+
+def test_decode_dense_long_contexts(lib):
+    """4 sequences at 60K-130K tokens (every block read: up to 1016 blocks, 64 groups of 16),
+    a device-drawn pool; the oracle checks sequence 1 (all 16 heads) on the pages copied back."""
+    lens = synth.decode_seq_lens(33, 4, 60000, 130000)
+    bt, P = synth.decode_block_table(33, lens, 128)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(33)
+    kp = torch.randn((P, 16, 128, 128), device="cuda", generator=g).to(torch.bfloat16)
+    vp = torch.randn((P, 16, 128, 128), device="cuda", generator=g).to(torch.bfloat16)
+    q = torch.randn((4, 16, 128), device="cuda", generator=g).to(torch.bfloat16)
+    say(f"ssa_decode_dense lens={list(lens)}")
+    o, lse = lib.decode_dense(q, kp, vp, torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda(), with_lse=True)
+    torch.cuda.synchronize()
+    b = 1
+    nb = (int(lens[b]) + 127) // 128
+    pages = torch.from_numpy(bt[b, :nb].astype(np.int64)).cuda()
+    kh = kp[pages].float().cpu().numpy()
+    vh = vp[pages].float().cpu().numpy()
+    bt_c = np.arange(nb, dtype=np.int32)[None]
+    ro, rl = oracle.dense_decode(q[b:b + 1].float().cpu().numpy(), kh, vh, bt_c, lens[b:b + 1], 1 / math.sqrt(128))
+    check_close(to_f64(o[b:b + 1]), ro, "dense decode long o")
+    check_close(to_f64(lse[b:b + 1]), rl, "dense decode long lse")
