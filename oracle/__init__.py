@@ -36,6 +36,10 @@ against the sources by eye:
   variant (LongCat sparse attention article, section 3: streaming-aware
   indexing keeps sink + local window, hierarchical indexing scores 128-token
   pages and keeps the top-M).
+* ``token_select`` / ``token_list_attention`` -- the second stage of
+  hierarchical indexing (same section: inside the recalled pages every token is
+  scored and the top K are kept) and attention over window blocks plus those
+  tokens.
 
 Parity status: every function here is pinned by the CPU tests (brute force on
 tiny inputs, the dense special case against torch's own attention routine,
@@ -43,7 +47,9 @@ closed-form key counts, structural one-hot outputs, decode == last prefill row,
 chunked prefill == brute force over the cached sequence, dense decode == the
 last row of the (torch-pinned) dense causal attention, gradients == central
 finite differences of the forward and == torch autograd with an explicit mask,
-exact rational re-scoring of page selections).  No function is "parity
+exact rational re-scoring of page and token selections, token lists that
+keep every candidate == the page-list attention, planted and duplicated
+tokens).  No function is "parity
 unpinned".
 """
 from .ssa import (  # noqa: F401
@@ -64,4 +70,6 @@ from .ssa import (  # noqa: F401
     page_select,
     block_list_rows,
     block_list_attention,
+    token_select,
+    token_list_attention,
 )

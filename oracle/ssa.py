@@ -444,3 +444,100 @@ def block_list_attention(q, k, v, scale, idx, cnt, block: int = 128):
             o[b, r0:r1] = ob
             lse[b, :, r0:r1] = lb.T
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# hierarchical indexing, second stage: single tokens inside the recalled pages
+# ---------------------------------------------------------------------------
+
+def token_select(q, k, page_idx, page_cnt, win: Window = DEFAULT_WINDOW, top_k: int = 512, heads=None):
+    """Second, fine-grained stage of hierarchical indexing (LongCat sparse
+    attention article, section 3, hierarchical indexing: the first stage recalls
+    the top-M pages, the second scores every token of those pages and keeps the
+    top K).
+
+    The pages leave the fine score to a trained indexer; the training-free
+    reading used here scores a token j with the same query-block sum as the
+    first stage:  score(j) = <sum of q over block qb, k_j>  (kv head of h).
+    Candidates are the tokens of the listed pages that lie outside the window of
+    qb (the window's pages are attended whole).  The K highest scores are kept,
+    equal scores preferring the lower token; with at most K candidates all are
+    kept.  Token lists are ascending and padded with -1 to width K.
+
+    Returns tok int32 [B, Hq, nqb, K], tok_cnt int32 [B, Hq, nqb] and near bool
+    [B, Hq, nqb] (rows whose float64 scores left the top-K boundary within
+    rounding error and were re-decided with exact rationals).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    B, L, Hq, D = q.shape
+    Hkv = k.shape[2]
+    bs = win.block_size
+    nqb = (L + bs - 1) // bs
+    K = top_k
+    tok = np.full((B, Hq, nqb, K), -1, np.int32)
+    tcnt = np.zeros((B, Hq, nqb), np.int32)
+    near = np.zeros((B, Hq, nqb), bool)
+    qs = block_sums(q, bs)
+    for b in range(B):
+        for h in (range(Hq) if heads is None else heads):
+            g = _kv_head(h, Hq, Hkv)
+            for qb in range(nqb):
+                inside = set(window_blocks(qb, win))
+                pages = sorted(int(c) for c in page_idx[b, h, qb, :page_cnt[b, h, qb]] if c >= 0 and c not in inside)
+                cand = [j for c in pages for j in range(c * bs, min((c + 1) * bs, L))]
+                if len(cand) <= K:
+                    chosen = cand
+                else:
+                    a = qs[b, qb, h]
+                    kc = k[b, cand, g]
+                    sc = kc @ a
+                    err = 1e-9 * (np.abs(kc) @ np.abs(a))
+                    order = np.lexsort((np.asarray(cand), -sc))  # descending score, then ascending token
+                    if K == 0 or sc[order[K - 1]] - sc[order[K]] > 2.0 * err.max():
+                        chosen = [cand[int(n)] for n in order[:K]]
+                    else:
+                        near[b, h, qb] = True
+                        rq = q[b, qb * bs:min((qb + 1) * bs, L), h]
+                        qsum_exact = [sum(Fraction(float(x)) for x in rq[:, d]) for d in range(D)]
+                        ex = [sum(qe * Fraction(float(x)) for qe, x in zip(qsum_exact, k[b, j, g])) for j in cand]
+                        order = sorted(range(len(cand)), key=lambda n: (-ex[n], cand[n]))
+                        chosen = [cand[n] for n in order[:K]]
+                chosen = sorted(chosen)
+                tok[b, h, qb, :len(chosen)] = chosen
+                tcnt[b, h, qb] = len(chosen)
+    return tok, tcnt, near
+
+
+def token_list_attention(q, k, v, scale, idx, cnt, tok, tok_cnt, block: int = 128, rows=None):
+    """Attention of each query over the listed blocks (causal, as in
+    ``block_list_attention``) together with the listed single tokens of its
+    query block; the tokens all precede the block, so no causal rule applies to
+    them.  ``rows`` (optional) restricts the work to some query blocks (other
+    rows of o / lse are left NaN).
+
+    Returns o [B, L, Hq, Dv] and lse [B, Hq, L].
+    """
+    q = np.asarray(q, np.float64)
+    B, L, Hq, _ = q.shape
+    Hkv = k.shape[2]
+    nqb = (L + block - 1) // block
+    o = np.full((B, L, Hq, v.shape[3]), np.nan)
+    lse = np.full((B, Hq, L), np.nan)
+    for b in range(B):
+        for qb in (range(nqb) if rows is None else rows):
+            r0, r1 = qb * block, min((qb + 1) * block, L)
+            qi = np.arange(r0, r1)
+            for h in range(Hq):
+                g = _kv_head(h, Hq, Hkv)
+                ids = [int(t) for t in idx[b, h, qb, :cnt[b, h, qb]] if t >= 0]
+                pos = [j for t in ids for j in range(t * block, min((t + 1) * block, L))]
+                toks = [int(t) for t in tok[b, h, qb, :tok_cnt[b, h, qb]]]
+                keys = np.asarray(pos + toks, np.int64)
+                allowed = np.concatenate([np.asarray(pos, np.int64)[None, :] <= qi[:, None],
+                                          np.ones((r1 - r0, len(toks)), bool)], axis=1)
+                oo, ll = _attend(q[b, r0:r1, h], np.asarray(k[b, keys, g], np.float64),
+                                 np.asarray(v[b, keys, g], np.float64), allowed, scale)
+                o[b, r0:r1, h] = oo
+                lse[b, h, r0:r1] = ll
+    return o, lse

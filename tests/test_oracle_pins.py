@@ -488,6 +488,135 @@ def test_block_list_attention_with_window_lists_is_ssa():
 
 
 # ---------------------------------------------------------------------------
+# hierarchical indexing, second stage (tokens inside the recalled pages)
+# ---------------------------------------------------------------------------
+
+def _tiny_token_case(seed=11, L=61, D=3, Hq=2):
+    rng = np.random.default_rng(seed)
+    q = np.round(rng.standard_normal((1, L, Hq, D)) * 8) / 8
+    k = np.round(rng.standard_normal((1, L, 1, D)) * 8) / 8
+    v = rng.standard_normal((1, L, 1, 2))
+    return q, k, v
+
+
+def _token_select_matches_brute(seed=11, before_select=None):
+    """Tiny geometry (block 4, 1 global, 2 local, top 2 pages, top 3 tokens): every
+    row re-decided by enumerating the candidate tokens with exact rational scores."""
+    win, M, K = Window(4, 1, 2), 2, 3
+    q, k, _ = _tiny_token_case(seed)
+    L, D = q.shape[1], q.shape[3]
+    pidx, pcnt, _ = oracle.page_select(q, k, win, top_m=M)
+    if before_select:
+        before_select()
+    tok, tcnt, _ = oracle.token_select(q, k, pidx, pcnt, win, top_k=K)
+    ok = True
+    for h in range(2):
+        for qb in range((L + 3) // 4):
+            inside = set(range(max(0, qb - 1), qb + 1)) | {0}
+            pages = [int(c) for c in pidx[0, h, qb, :pcnt[0, h, qb]] if c not in inside]
+            cand = [j for c in pages for j in range(4 * c, min(4 * c + 4, L))]
+            rows = range(4 * qb, min(4 * qb + 4, L))
+            qsum = [sum(Fraction(float(q[0, i, h, d])) for i in rows) for d in range(D)]
+            score = {j: sum(qsum[d] * Fraction(float(k[0, j, 0, d])) for d in range(D)) for j in cand}
+            want = sorted(sorted(cand, key=lambda j: (-score[j], j))[:K])
+            ok &= list(tok[0, h, qb, :tcnt[0, h, qb]]) == want
+            ok &= bool((tok[0, h, qb, tcnt[0, h, qb]:] == -1).all())
+    return ok
+
+
+def test_token_select_bruteforce_exact_tiny():
+    assert _token_select_matches_brute(11) and _token_select_matches_brute(21)
+
+
+def test_token_select_planted_mistake_is_caught(monkeypatch):
+    """Window pages wrongly counted as candidates (the global block dropped from
+    the window the second stage excludes) must fail the brute-force pin."""
+    import oracle.ssa as S
+    good_wb = S.window_blocks
+    assert _token_select_matches_brute(11)
+    no_global = lambda qb, win=S.DEFAULT_WINDOW: good_wb(qb, Window(win.block_size, 0, win.n_local))
+    assert not _token_select_matches_brute(11, lambda: monkeypatch.setattr(S, "window_blocks", no_global))
+
+
+def test_token_select_keeping_every_candidate_is_page_attention():
+    """With K at least the recalled pages' token count, window blocks + tokens is
+    the same key set as the page list: the attention outputs agree to rounding."""
+    rng = np.random.default_rng(12)
+    L, Hq = 128 * 20 + 37, 2
+    q = rng.standard_normal((1, L, Hq, 8))
+    k = rng.standard_normal((1, L, 1, 8))
+    v = rng.standard_normal((1, L, 1, 8))
+    pidx, pcnt, _ = oracle.page_select(q, k, top_m=3)
+    tok, tcnt, _ = oracle.token_select(q, k, pidx, pcnt, top_k=3 * 128)
+    widx, wcnt = oracle.block_index((L + 127) // 128)
+    nqb = widx.shape[0]
+    widx4 = np.broadcast_to(widx[None, None], (1, Hq, nqb, 8))
+    wcnt3 = np.broadcast_to(wcnt[None, None], (1, Hq, nqb))
+    o1, l1 = oracle.token_list_attention(q, k, v, 0.3, widx4, wcnt3, tok, tcnt)
+    o2, l2 = oracle.block_list_attention(q, k, v, 0.3, pidx, pcnt)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=1e-12, atol=1e-13)
+    # rows 16.. keep 3 pages = 384 tokens; shorter rows keep what they have
+    assert tcnt[0, 0, 19] == 384 and tcnt[0, 0, 8] == 128 and tcnt[0, 0, 7] == 0
+
+
+def test_token_select_planted_and_ties():
+    """Keys sharing a direction with the query block are selected; an exact
+    duplicate of the best key loses the tie to the lower token."""
+    rng = np.random.default_rng(13)
+    L, D = 128 * 30, 16
+    q = rng.standard_normal((1, L, 1, D))
+    k = rng.standard_normal((1, L, 1, D))
+    u = rng.standard_normal(D) * 3
+    qb = 29
+    q[0, qb * 128:(qb + 1) * 128, 0] += u
+    planted = [5 * 128 + 7, 5 * 128 + 90, 9 * 128 + 1]
+    for j in planted:
+        k[0, j, 0] += u
+    qsum = q[0, qb * 128:(qb + 1) * 128, 0].sum(axis=0)
+    weakest = min(planted, key=lambda j: k[0, j, 0] @ qsum)
+    k[0, 9 * 128 + 100, 0] = k[0, weakest, 0]          # exact duplicate of the weakest planted key
+    pidx = np.full((1, 1, 30, 10), -1, np.int32)
+    pcnt = np.zeros((1, 1, 30), np.int32)
+    row = sorted({0, 5, 9} | set(range(23, 30)))
+    pidx[0, 0, qb, :len(row)] = row
+    pcnt[0, 0, qb] = len(row)
+    tok, tcnt, _ = oracle.token_select(q, k, pidx, pcnt, top_k=3)
+    assert list(tok[0, 0, qb, :3]) == planted
+    tok4, _, _ = oracle.token_select(q, k, pidx, pcnt, top_k=4)
+    assert list(tok4[0, 0, qb, :4]) == sorted(planted + [9 * 128 + 100])
+
+
+def test_token_list_attention_bruteforce_tiny():
+    """Explicit per-query key sets (listed blocks causally, plus the tokens) with a
+    pure-Python softmax."""
+    win, M, K = Window(4, 1, 2), 2, 3
+    q, k, v = _tiny_token_case(seed=14)
+    L = q.shape[1]
+    pidx, pcnt, _ = oracle.page_select(q, k, win, top_m=M)
+    tok, tcnt, _ = oracle.token_select(q, k, pidx, pcnt, win, top_k=K)
+    nqb = (L + 3) // 4
+    widx = np.full((1, 2, nqb, 3), -1, np.int32)
+    wcnt = np.zeros((1, 2, nqb), np.int32)
+    for qb in range(nqb):
+        w = oracle.window_blocks(qb, win)
+        widx[0, :, qb, :len(w)] = w
+        wcnt[0, :, qb] = len(w)
+    o, lse = oracle.token_list_attention(q, k, v, 0.7, widx, wcnt, tok, tcnt, block=4)
+    for h in range(2):
+        for i in range(L):
+            qb = i // 4
+            keys = [j for t in oracle.window_blocks(qb, win) for j in range(4 * t, min(4 * t + 4, L)) if j <= i]
+            keys += [int(j) for j in tok[0, h, qb, :tcnt[0, h, qb]]]
+            s = [0.7 * sum(float(q[0, i, h, d]) * float(k[0, j, 0, d]) for d in range(3)) for j in keys]
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            ref = [sum(wi * float(v[0, j, 0, c]) for wi, j in zip(w, keys)) / sum(w) for c in range(2)]
+            assert np.allclose(o[0, i, h], ref, rtol=1e-12, atol=1e-13)
+            assert abs(lse[0, h, i] - (m + math.log(sum(w)))) < 1e-12
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: each must be caught by one of the pins above
 # ---------------------------------------------------------------------------
 
