@@ -53,7 +53,7 @@ PEAK_HBM_GBS = 8000.0
 
 W2 = dict(B=1, L=32768, H=16, D=128, seed=2)
 W3 = dict(B=64, H=16, D=128, lo=65536, hi=131072, seed=3)
-W5 = dict(B=1, L=131072, H=16, D=128, M=8, seed=5)
+W5 = dict(B=1, L=131072, H=16, D=128, M=8, K=512, seed=5)
 W4 = dict(L=262144, H=128, DQK=576, DV=512, seed=4, dec_B=8, dec_n=1048576, dec_rot=32)
 W6 = dict(B=16, T=2048, H=16, D=128, lo=65536, hi=131072, seed=6)
 
@@ -92,6 +92,18 @@ def dense_flops(L, H, D, B=1):
 
 def page_flops(L, H, D, M, B=1):
     return 4 * D * pairs(L, lambda i: keys_page(i, M)) * H * B
+
+
+def hi_tokens(qb: int, M: int, K: int) -> int:
+    """Tokens the second hierarchical stage keeps for query block qb: the
+    recalled pages outside the window are min(M, qb - 7) (all of them while
+    they number at most M), 128 tokens each, of which K at most."""
+    return min(K, 128 * min(M, max(qb - 7, 0)))
+
+
+def hi_flops(L, H, D, M, K, B=1):
+    """4d flops per (query, key) pair: the window's keys plus the block's tokens."""
+    return 4 * D * (pairs(L, keys_ssa) + sum(128 * hi_tokens(qb, M, K) for qb in range(L // 128))) * H * B
 
 
 def chunk_flops(lens, T, H, D):
@@ -247,6 +259,21 @@ def cpu_rows_baseline():
           lambda: [oracle.block_list_rows(q5[0, qb_ * 128:(qb_ + 1) * 128].astype(np.float64), qb_ * 128, k5[0], v5[0],
                                           1 / math.sqrt(D5), [0], 1, [list(idx[0, 0, qb_, :cnt[0, 0, qb_]])])
                    for qb_ in qbs])
+    # f2: the second hierarchical stage for head 0, attention of the last 16 query blocks
+    K5 = W5["K"]
+    tsel = {}
+    cand = sum(128 * min(M5, max(qb_ - 7, 0)) for qb_ in range(L5 // 128) if 128 * min(M5, max(qb_ - 7, 0)) > K5)
+    timed("f2 token_select", "GFLOP/s", 2 * D5 * cand, "top-512 token lists of every query block of 1 of the 16 heads",
+          lambda: tsel.update(r=oracle.token_select(q5, k5, idx, cnt, top_k=K5)))
+    tok, tcnt = tsel["r"][:2]
+    wi, wc = oracle.block_index(L5 // 128)
+    w4 = wi[None, None]
+    c3 = wc[None, None]
+    q5d = q5.astype(np.float64)
+    timed("f2 hi_prefill", "TFLOP/s",
+          4 * D5 * sum(keys_ssa(i) + hi_tokens(qb_, M5, K5) for qb_ in qbs for i in range(qb_ * 128, qb_ * 128 + 128)),
+          "rows of the last 16 query blocks, 1 of the 16 heads",
+          lambda: oracle.token_list_attention(q5d, k5, v5, 1 / math.sqrt(D5), w4, c3, tok, tcnt, rows=qbs))
     # a4: the 576-wide shape (one query block x 16 of the 128 heads; one decode sequence)
     H4, DQ4, DV4 = W4["H"], W4["DQK"], W4["DV"]
     L4s = 2048
@@ -520,7 +547,7 @@ def main():
     ap.add_argument("--rotations", type=int, default=2, help="independent decode page sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=25.0)
-    ap.add_argument("--only", default="", help="comma list of rows to run (prefill,decode,dense,page,mla,chunk,bwd); "
+    ap.add_argument("--only", default="", help="comma list of rows to run (prefill,decode,dense,page,mla,chunk,bwd,hi); "
                     "for profiling one kernel -- the JSON line is printed only for a full run")
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="summarise two rocprofv3 --pmc runs into a traffic file and exit")
@@ -565,7 +592,9 @@ def main():
         return t.to(dev)
 
     only = set(x for x in args.only.split(",") if x)
-    run = {name: (not only) or (name in only) for name in ("prefill", "decode", "dense", "page", "mla", "chunk", "bwd")}
+    run = {name: (not only) or (name in only) for name in ("prefill", "decode", "dense", "page", "mla", "chunk", "bwd",
+                                                          "hi")}
+    run["page"] = run["page"] or run["hi"]  # the token stage starts from the page lists
     run["copy"] = "copy" in only  # calibration copy for the traffic counters, only on request
 
     print("[bench] generating inputs", flush=True)
@@ -612,6 +641,10 @@ def main():
         idx5 = torch.empty((1, H5, nqb5, 8 + M5), dtype=torch.int32, device=dev)
         cnt5 = torch.empty((1, H5, nqb5), dtype=torch.int32, device=dev)
         ws5 = torch.empty((ssa.page_select_workspace_size(q5, k5) + 256,), dtype=torch.uint8, device=dev)
+    if run["hi"]:  # f2: the window's blocks plus K tokens of the recalled pages
+        K5 = W5["K"]
+        lists5w = ssa.lists_from_index(*ssa.block_index(nqb5, device=dev))
+        o5h = torch.empty((1, H5, L5, D5), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
     # a4 inputs: values N(0,1)/24, drawn on the device (the query is 38.6 GB)
     if run["mla"]:
         L4, H4, DQ4, DV4, s4 = W4["L"], W4["H"], W4["DQK"], W4["DV"], W4["seed"]
@@ -667,7 +700,8 @@ def main():
     torch.cuda.synchronize()
 
     rows = ["a1 block_index", "a2 ssa_prefill", "a3 ssa_decode", "a5 dense_causal", "a6-a7 page_select",
-            "a8 page_prefill", "a4 mla_prefill", "a4 mla_decode", "f1 chunk_prefill", "f3 ssa_backward"]
+            "a8 page_prefill", "a4 mla_prefill", "a4 mla_decode", "f1 chunk_prefill", "f3 ssa_backward",
+            "f2 token_select", "f2 hi_prefill"]
     nev = len(rows) + 1
 
     if run["copy"]:
@@ -711,6 +745,12 @@ def main():
         if run["bwd"]:
             ssa.prefill_backward(q2, k2, v2, ob, gb, lseb, dq=dqb, dk=dkb, dv=dvb, workspace=wsb)
         mark(10)
+        if run["hi"]:
+            t5, tc5 = ssa.token_select(q5, k5, i5, c5, ws5, top_m=M5, top_k=K5)
+        mark(11)
+        if run["hi"]:
+            ssa.prefill_tokens(q5, k5, v5, lists5w, ssa.token_lists(t5, tc5), out=o5h)
+        mark(12)
         if run["copy"]:
             cp_dst.copy_(cp_src)
 
@@ -734,7 +774,7 @@ def main():
     if only:
         return
     for t, name in ((o2, "ssa"), (o3, "decode"), (od, "dense"), (o5, "page"), (o4[0, -128:], "mla"),
-                    (o4d, "mla decode"), (o6, "chunk"), (dqb, "dq"), (dkb, "dk"), (dvb, "dv")):
+                    (o4d, "mla decode"), (o6, "chunk"), (dqb, "dq"), (dkb, "dk"), (dvb, "dv"), (o5h, "hi")):
         if not torch.isfinite(t.float()).all():
             raise RuntimeError(f"non-finite {name} output")
 
@@ -783,6 +823,17 @@ def main():
                                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                "frac": fb / (per_row[9] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                "us": per_row[9] * 1e3, "work": fb}
+    fh = hi_flops(L5, H5, D5, M5, K5)
+    # the second stage scores every recalled token: D fp64 FMAs on a key row
+    # (2D bytes, re-read from cache by neighbouring query blocks) per candidate
+    cand5 = H5 * sum(128 * min(M5, max(qb - 7, 0)) for qb in range(nqb5) if 128 * min(M5, max(qb - 7, 0)) > K5)
+    kernels["token_select"] = {"us": per_row[10] * 1e3, "candidates": cand5,
+                               "candidate_rows_per_s": cand5 / (per_row[10] * 1e-3),
+                               "fp64_gflops": 2 * D5 * cand5 / (per_row[10] * 1e-3) / 1e9}
+    kernels["hi_prefill"] = {"bound": "mfma", "achieved": fh / (per_row[11] * 1e-3) / 1e12,
+                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": fh / (per_row[11] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                             "us": per_row[11] * 1e3, "work": fh}
     out = {
         "metric": "SSA prefill TFLOP/s (frac MFMA peak) + decode GB/s (frac HBM) at 128K ctx",
         "value": tf2,
@@ -801,12 +852,15 @@ def main():
                         "ctx U[65536,131072] bf16 (decode) + dense causal (same shape) + page selection "
                         "L=131072 H=16 d=128 M=8 + latent-shared 576/512 x 128 heads: prefill L=262144, "
                         "decode batch 8 at 1048576 + chunked prefill of the last 2048 tokens of 16 sequences "
-                        "at ctx U[65536,131072] over a paged cache + SSA backward of the prefill workload",
+                        "at ctx U[65536,131072] over a paged cache + SSA backward of the prefill workload + "
+                        "hierarchical second stage (top-512 tokens of the 8 recalled pages) and attention over "
+                        "window + tokens at the page-selection shape",
             "prefill_tokens_per_s": L2 / t2,
             "decode_gbps": gb3,
             "decode_frac_hbm": gb3 / PEAK_HBM_GBS,
             "decode_tokens_per_s": B3 / t3,
             "page_select_index_share": per_row[4] / (per_row[4] + per_row[5]),
+            "hi_index_share": (per_row[4] + per_row[10]) / (per_row[4] + per_row[10] + per_row[11]),
         },
         "roofline": kernels["ssa_prefill"],
         "roofline_decode": kernels["ssa_decode"],

@@ -104,6 +104,23 @@ typedef struct ssa_block_lists {
   int64_t cnt_sb, cnt_sh;
 } ssa_block_lists;
 
+/* Per-query-block lists of single key tokens, as written by ssa_token_select
+ * (one list per batch and query head):
+ *   row (b, h, qb):  tok[b*tok_sb + h*tok_sh + qb*K + e], e < cnt[b*cnt_sb + h*cnt_sh + qb]
+ * (a count below 0 reads as 0, above K as K).  A row's entries must be
+ * strictly ascending, below qb*128 (every token precedes its query block, so
+ * no causal rule applies to them) and outside every block of the row's block
+ * list; a row that breaks this makes every output row of its query block NaN
+ * (lse NaN). */
+typedef struct ssa_token_lists {
+  const int32_t* tok;
+  const int32_t* cnt;
+  int32_t K;         /* list capacity, 0 .. 1024          */
+  int32_t n_qblocks; /* rows per (b, h); >= ceil(L/128)   */
+  int64_t tok_sb, tok_sh;
+  int64_t cnt_sb, cnt_sh;
+} ssa_token_lists;
+
 /* Paged decode operands.  One new query per sequence:
  *   q [B, Hq, Dqk]  -> o [B, Hq, Dv]   (strides for (b, h); channels contiguous)
  *   k_pages [num_pages, Hkv, page_size, Dqk], v_pages [num_pages, Hkv, page_size, Dv]
@@ -169,6 +186,22 @@ int ssa_block_index_seq(const ssa_window* win, const int32_t* seq_lens, int32_t 
  * accumulation; the softmax runs in fp32.
  * ------------------------------------------------------------------------- */
 int ssa_prefill(const ssa_attn_args* a, const ssa_block_lists* lists, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ssa_prefill_tokens -- ssa_prefill over the row's block list together with
+ * the row's single tokens (LongCat sparse attention article, section 3,
+ * hierarchical indexing: after the coarse page stage a fine stage keeps the
+ * best tokens inside the recalled pages; with the window's blocks as the
+ * block list and the lists of ssa_token_select as the tokens this is the
+ * attention of that variant).  The keys of query i in block qb are the keys
+ * j <= i of its listed blocks plus its block's listed tokens; the softmax is
+ * the masked softmax of equation (2) of the ZigZag page, section 2.1.
+ * Supported: BF16 with Dqk = Dv = 128 (else SSA_ERR_UNSUPPORTED); output BF16
+ * or F32; lse optional.  tokens->cnt must be non-NULL, tokens->tok too when
+ * K > 0.
+ * ------------------------------------------------------------------------- */
+int ssa_prefill_tokens(const ssa_attn_args* a, const ssa_block_lists* lists, const ssa_token_lists* tokens,
+                       void* stream);
 
 /* ssa_dense_causal -- the comparison layer: plain causal attention, key j <=
  * query i (equation (1) of the ZigZag page with the causal rule of its
@@ -339,6 +372,32 @@ size_t ssa_decode_dense_workspace_size(const ssa_decode_args* a);
 size_t ssa_page_select_workspace_size(const ssa_attn_args* a, const ssa_window* win);
 int ssa_page_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_m, int32_t* idx,
                     int32_t* cnt, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ssa_token_select -- the fine stage of hierarchical indexing (LongCat sparse
+ * attention article, section 3: inside the top-M recalled pages every token
+ * is scored and the top K are kept).  The article leaves the token score to
+ * a trained indexer; this library scores token j for query block qb with the
+ * page stage's query-block sum:
+ *      < sum of q over block qb , k_j >      (kv head of h, fp64)
+ * Candidates are the tokens of the pages c of row (b, h, qb) of page_idx /
+ * page_cnt with n_global <= c <= qb - n_local (the pages outside the window;
+ * a repeated page counts once; at most the 32 lowest such pages).  The top_k
+ * highest scores are kept, equal scores preferring the lower token; with at
+ * most top_k candidates all are kept.  Output lists are ascending, padded with
+ * -1:  tok [B, Hq, nqb, top_k],  tok_cnt [B, Hq, nqb]  (contiguous), ready for
+ * ssa_prefill_tokens with tok_sb = Hq*nqb*top_k, tok_sh = nqb*top_k,
+ * cnt_sb = Hq*nqb, cnt_sh = nqb.
+ * page_idx / page_cnt are the contiguous lists ssa_page_select wrote with the
+ * same a, win and top_m, and page_workspace is the workspace of that call
+ * (it holds the fp64 query-block sums), ordered before this call on the
+ * stream.  Uses a.k, its strides, a.dtype (BF16), B, L, Hq, Hkv, Dqk (64 or
+ * 128).  0 <= top_m <= 32; 0 <= top_k <= 1024 (tok may be NULL when
+ * top_k = 0; tok_cnt is then all 0).
+ * ------------------------------------------------------------------------- */
+int ssa_token_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_m, const int32_t* page_idx,
+                     const int32_t* page_cnt, const void* page_workspace, size_t page_workspace_bytes,
+                     int32_t top_k, int32_t* tok, int32_t* tok_cnt, void* stream);
 
 /* Text of the calling thread's last error ("" if none).  Valid until the
  * thread's next failing call. */

@@ -28,9 +28,10 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 
 # every symbol include/ssa.h declares
 EXPORTS = (
-    "ssa_block_index", "ssa_block_index_seq", "ssa_prefill", "ssa_dense_causal", "ssa_prefill_chunk", "ssa_prefill_backward", "ssa_decode_dense", "ssa_prefill_backward",
-    "ssa_prefill_backward_workspace_size", "ssa_decode", "ssa_decode_dense", "ssa_decode_dense_workspace_size",
-    "ssa_decode_workspace_size", "ssa_page_select", "ssa_page_select_workspace_size", "ssa_last_error", "ssa_version",
+    "ssa_block_index", "ssa_block_index_seq", "ssa_prefill", "ssa_prefill_tokens", "ssa_dense_causal",
+    "ssa_prefill_chunk", "ssa_prefill_backward", "ssa_prefill_backward_workspace_size", "ssa_decode",
+    "ssa_decode_dense", "ssa_decode_dense_workspace_size", "ssa_decode_workspace_size", "ssa_page_select",
+    "ssa_page_select_workspace_size", "ssa_token_select", "ssa_last_error", "ssa_version",
 )
 
 
@@ -66,6 +67,15 @@ class CBlockLists(ctypes.Structure):
         ("idx", ctypes.c_void_p), ("cnt", ctypes.c_void_p),
         ("W", ctypes.c_int32), ("n_qblocks", ctypes.c_int32),
         ("idx_sb", ctypes.c_int64), ("idx_sh", ctypes.c_int64),
+        ("cnt_sb", ctypes.c_int64), ("cnt_sh", ctypes.c_int64),
+    ]
+
+
+class CTokenLists(ctypes.Structure):
+    _fields_ = [
+        ("tok", ctypes.c_void_p), ("cnt", ctypes.c_void_p),
+        ("K", ctypes.c_int32), ("n_qblocks", ctypes.c_int32),
+        ("tok_sb", ctypes.c_int64), ("tok_sh", ctypes.c_int64),
         ("cnt_sb", ctypes.c_int64), ("cnt_sh", ctypes.c_int64),
     ]
 
@@ -152,6 +162,10 @@ def load(path: str = LIB_PATH):
     lib.ssa_block_index.argtypes = [ctypes.POINTER(CWindow), i32, vp, vp, vp]
     lib.ssa_block_index_seq.argtypes = [ctypes.POINTER(CWindow), vp, i32, vp, vp, vp]
     lib.ssa_prefill.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CBlockLists), vp]
+    lib.ssa_prefill_tokens.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CBlockLists),
+                                       ctypes.POINTER(CTokenLists), vp]
+    lib.ssa_token_select.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CWindow), i32, vp, vp, vp,
+                                     ctypes.c_size_t, i32, vp, vp, vp]
     lib.ssa_dense_causal.argtypes = [ctypes.POINTER(CAttnArgs), vp]
     lib.ssa_prefill_chunk.argtypes = [ctypes.POINTER(CChunkArgs), ctypes.POINTER(CBlockLists), vp]
     lib.ssa_prefill_backward.argtypes = [ctypes.POINTER(CBwdArgs), ctypes.POINTER(CWindow), vp]
@@ -500,6 +514,68 @@ def page_select(q, k, top_m: int = 8, window: Window = DEFAULT_WINDOW, workspace
     _check(lib.ssa_page_select(ctypes.byref(a), ctypes.byref(w), top_m, _ptr(idx), _ptr(cnt),
                                base + off, workspace.numel() - off, _stream(stream)))
     return idx, cnt
+
+
+def _aligned256(workspace):
+    base = workspace.data_ptr()
+    off = (-base) % 256
+    return base + off, workspace.numel() - off
+
+
+def token_lists(tok: torch.Tensor, tok_cnt: torch.Tensor) -> CTokenLists:
+    """Token lists per (batch, query head): tok [B, Hq, nqb, K], tok_cnt [B, Hq, nqb]."""
+    assert tok.is_contiguous() and tok_cnt.is_contiguous()
+    B, H, nqb, K = tok.shape
+    t = CTokenLists()
+    t.tok, t.cnt = _ptr(tok), _ptr(tok_cnt)
+    t.K, t.n_qblocks = K, nqb
+    t.tok_sb, t.tok_sh = H * nqb * K, nqb * K
+    t.cnt_sb, t.cnt_sh = H * nqb, nqb
+    return t
+
+
+def prefill_tokens(q, k, v, lists: CBlockLists, tokens: CTokenLists, scale=None, out=None, out_dtype=None,
+                   with_lse=False, lse=None, stream=None):
+    """ssa_prefill_tokens: attention over the block lists plus the token lists.  Returns (o, lse or None)."""
+    lib = load()
+    if out is None:
+        out, lse2 = _out(q, v, out_dtype, with_lse)
+        lse = lse if lse is not None else lse2
+    a = _attn_args(q, k, v, out, lse, scale)
+    _check(lib.ssa_prefill_tokens(ctypes.byref(a), ctypes.byref(lists), ctypes.byref(tokens), _stream(stream)))
+    return out, lse
+
+
+def token_select(q, k, page_idx, page_cnt, page_workspace, top_m: int = 8, top_k: int = 512,
+                 window: Window = DEFAULT_WINDOW, stream=None):
+    """ssa_token_select after page_select(q, k, top_m, window, workspace=page_workspace):
+    (tok int32 [B, Hq, nqb, top_k], tok_cnt int32 [B, Hq, nqb])."""
+    lib = load()
+    B, L, Hq, _ = q.shape
+    nqb = (L + window.block_size - 1) // window.block_size
+    tok = torch.empty((B, Hq, nqb, top_k), dtype=torch.int32, device=q.device)
+    tcnt = torch.empty((B, Hq, nqb), dtype=torch.int32, device=q.device)
+    a = _attn_args(q, k, k, q, None, 1.0)
+    w = window.c()
+    base, nbytes = _aligned256(page_workspace)
+    _check(lib.ssa_token_select(ctypes.byref(a), ctypes.byref(w), top_m, _ptr(page_idx), _ptr(page_cnt), base,
+                                nbytes, top_k, _ptr(tok), _ptr(tcnt), _stream(stream)))
+    return tok, tcnt
+
+
+def hi_attention(q, k, v, top_m: int = 8, top_k: int = 512, scale=None, window: Window = DEFAULT_WINDOW,
+                 out_dtype=None, with_lse=False, stream=None):
+    """Both stages of hierarchical indexing, then attention over the window blocks
+    plus the chosen tokens.  Returns (o, lse, tok, tok_cnt)."""
+    B, L, Hq, _ = q.shape
+    ws = torch.empty((page_select_workspace_size(q, k, window) + 256,), dtype=torch.uint8, device=q.device)
+    pidx, pcnt = page_select(q, k, top_m, window, workspace=ws, stream=stream)
+    tok, tcnt = token_select(q, k, pidx, pcnt, ws, top_m, top_k, window, stream=stream)
+    nqb = (L + window.block_size - 1) // window.block_size
+    widx, wcnt = block_index(nqb, window, device=q.device, stream=stream)
+    o, lse = prefill_tokens(q, k, v, lists_from_index(widx, wcnt), token_lists(tok, tcnt), scale=scale,
+                            out_dtype=out_dtype, with_lse=with_lse, stream=stream)
+    return o, lse, tok, tcnt
 
 
 def page_attention(q, k, v, top_m: int = 8, scale=None, window: Window = DEFAULT_WINDOW, out_dtype=None,

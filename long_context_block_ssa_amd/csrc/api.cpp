@@ -128,6 +128,32 @@ ssa::PrefillParams make_prefill(const ssa_attn_args* a) {
   return p;
 }
 
+int check_lists(const ssa_attn_args* a, const ssa_block_lists* lists, const char* who) {
+  if (!lists) return fail(SSA_ERR_INVALID, "%s: lists is NULL", who);
+  if (!lists->idx || !lists->cnt) return fail(SSA_ERR_INVALID, "%s: lists idx/cnt must be non-NULL", who);
+  if (!aligned(lists->idx, 4) || !aligned(lists->cnt, 4))
+    return fail(SSA_ERR_INVALID, "%s: lists idx/cnt must be 4-byte aligned", who);
+  if (lists->W < 1 || lists->W > 64) return fail(SSA_ERR_INVALID, "%s: list width W=%d not in [1, 64]", who, lists->W);
+  const int64_t nqb = ceil_div(a->L, 128);
+  if (lists->n_qblocks < nqb)
+    return fail(SSA_ERR_INVALID, "%s: lists hold %d rows per head, L=%d needs %lld", who, lists->n_qblocks, a->L,
+                static_cast<long long>(nqb));
+  if (lists->idx_sb < 0 || lists->idx_sh < 0 || lists->cnt_sb < 0 || lists->cnt_sh < 0)
+    return fail(SSA_ERR_INVALID, "%s: list strides must be >= 0", who);
+  return SSA_OK;
+}
+
+void set_lists(ssa::PrefillParams& p, const ssa_block_lists* lists) {
+  p.idx = lists->idx;
+  p.cnt = lists->cnt;
+  p.W = lists->W;
+  p.dense = 0;
+  p.idx_sb = lists->idx_sb;
+  p.idx_sh = lists->idx_sh;
+  p.cnt_sb = lists->cnt_sb;
+  p.cnt_sh = lists->cnt_sh;
+}
+
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
@@ -166,28 +192,50 @@ int ssa_prefill(const ssa_attn_args* a, const ssa_block_lists* lists, void* stre
   const char* who = "ssa_prefill";
   int rc = check_attn(a, who);
   if (rc != SSA_OK) return rc;
-  if (!lists) return fail(SSA_ERR_INVALID, "%s: lists is NULL", who);
-  if (!lists->idx || !lists->cnt) return fail(SSA_ERR_INVALID, "%s: lists idx/cnt must be non-NULL", who);
-  if (!aligned(lists->idx, 4) || !aligned(lists->cnt, 4))
-    return fail(SSA_ERR_INVALID, "%s: lists idx/cnt must be 4-byte aligned", who);
-  if (lists->W < 1 || lists->W > 64) return fail(SSA_ERR_INVALID, "%s: list width W=%d not in [1, 64]", who, lists->W);
-  const int64_t nqb = ceil_div(a->L, 128);
-  if (lists->n_qblocks < nqb)
-    return fail(SSA_ERR_INVALID, "%s: lists hold %d rows per head, L=%d needs %lld", who, lists->n_qblocks, a->L,
-                static_cast<long long>(nqb));
-  if (lists->idx_sb < 0 || lists->idx_sh < 0 || lists->cnt_sb < 0 || lists->cnt_sh < 0)
-    return fail(SSA_ERR_INVALID, "%s: list strides must be >= 0", who);
+  rc = check_lists(a, lists, who);
+  if (rc != SSA_OK) return rc;
   ssa::PrefillParams p = make_prefill(a);
-  p.idx = lists->idx;
-  p.cnt = lists->cnt;
-  p.W = lists->W;
-  p.dense = 0;
-  p.idx_sb = lists->idx_sb;
-  p.idx_sh = lists->idx_sh;
-  p.cnt_sb = lists->cnt_sb;
-  p.cnt_sh = lists->cnt_sh;
+  set_lists(p, lists);
   hipError_t e = ssa::launch_prefill(p, a->dtype, a->Dqk, a->Dv, a->out_dtype == SSA_DTYPE_F32, as_stream(stream));
   if (e == hipErrorNotSupported) return fail(SSA_ERR_UNSUPPORTED, "%s: no kernel for Dqk=%d Dv=%d in this build", who, a->Dqk, a->Dv);
+  return device_status(e, who);
+}
+
+int ssa_prefill_tokens(const ssa_attn_args* a, const ssa_block_lists* lists, const ssa_token_lists* tokens,
+                       void* stream) {
+  const char* who = "ssa_prefill_tokens";
+  int rc = check_attn(a, who);
+  if (rc != SSA_OK) return rc;
+  rc = check_lists(a, lists, who);
+  if (rc != SSA_OK) return rc;
+  if (!tokens) return fail(SSA_ERR_INVALID, "%s: tokens is NULL", who);
+  if (!(a->dtype == SSA_DTYPE_BF16 && a->Dqk == 128 && a->Dv == 128))
+    return fail(SSA_ERR_UNSUPPORTED, "%s: token lists need BF16 with Dqk = Dv = 128 (got dtype=%d Dqk=%d Dv=%d)", who,
+                a->dtype, a->Dqk, a->Dv);
+  if (tokens->K < 0 || tokens->K > 1024)
+    return fail(SSA_ERR_INVALID, "%s: token list width K=%d not in [0, 1024]", who, tokens->K);
+  if ((tokens->K > 0 && !tokens->tok) || !tokens->cnt)
+    return fail(SSA_ERR_INVALID, "%s: tokens cnt (and tok when K > 0) must be non-NULL", who);
+  if (!aligned(tokens->tok, 4) || !aligned(tokens->cnt, 4))
+    return fail(SSA_ERR_INVALID, "%s: tokens tok/cnt must be 4-byte aligned", who);
+  const int64_t nqb = ceil_div(a->L, 128);
+  if (tokens->n_qblocks < nqb)
+    return fail(SSA_ERR_INVALID, "%s: token lists hold %d rows per head, L=%d needs %lld", who, tokens->n_qblocks,
+                a->L, static_cast<long long>(nqb));
+  if (tokens->tok_sb < 0 || tokens->tok_sh < 0 || tokens->cnt_sb < 0 || tokens->cnt_sh < 0)
+    return fail(SSA_ERR_INVALID, "%s: token list strides must be >= 0", who);
+  ssa::TokenParams p{};
+  static_cast<ssa::PrefillParams&>(p) = make_prefill(a);
+  set_lists(p, lists);
+  p.tok = tokens->tok;
+  p.tcnt = tokens->cnt;
+  p.K = tokens->K;
+  p.tok_sb = tokens->tok_sb;
+  p.tok_sh = tokens->tok_sh;
+  p.tcnt_sb = tokens->cnt_sb;
+  p.tcnt_sh = tokens->cnt_sh;
+  hipError_t e = ssa::launch_prefill_tokens_d128(p, a->out_dtype == SSA_DTYPE_F32, as_stream(stream));
+  if (e == hipErrorNotSupported) return fail(SSA_ERR_UNSUPPORTED, "%s: list width W=%d exceeds the kernel's 64", who, lists->W);
   return device_status(e, who);
 }
 
@@ -544,6 +592,56 @@ int ssa_page_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_m
   p.idx = idx;
   p.cnt = cnt;
   return device_status(ssa::launch_page_select(p, as_stream(stream)), who);
+}
+
+int ssa_token_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_m, const int32_t* page_idx,
+                     const int32_t* page_cnt, const void* page_workspace, size_t page_workspace_bytes,
+                     int32_t top_k, int32_t* tok, int32_t* tok_cnt, void* stream) {
+  const char* who = "ssa_token_select";
+  if (!a) return fail(SSA_ERR_INVALID, "%s: args is NULL", who);
+  if (!valid_window(win, who, 64)) return SSA_ERR_INVALID;
+  if (a->dtype != SSA_DTYPE_BF16) return fail(SSA_ERR_UNSUPPORTED, "%s: only BF16 k is supported", who);
+  if (a->B < 1 || a->L < 1 || a->Hq < 1 || a->Hkv < 1)
+    return fail(SSA_ERR_INVALID, "%s: sizes B=%d L=%d Hq=%d Hkv=%d must be >= 1", who, a->B, a->L, a->Hq, a->Hkv);
+  if (a->Hq % a->Hkv != 0) return fail(SSA_ERR_INVALID, "%s: Hq=%d is not a multiple of Hkv=%d", who, a->Hq, a->Hkv);
+  if (a->Dqk != 64 && a->Dqk != 128) return fail(SSA_ERR_UNSUPPORTED, "%s: Dqk=%d (need 64 or 128)", who, a->Dqk);
+  if (top_m < 0 || top_m > 32) return fail(SSA_ERR_INVALID, "%s: top_m=%d not in [0, 32]", who, top_m);
+  if (win->n_global + win->n_local + top_m > 64)
+    return fail(SSA_ERR_INVALID, "%s: page list width %d exceeds 64", who, win->n_global + win->n_local + top_m);
+  if (top_k < 0 || top_k > 1024) return fail(SSA_ERR_INVALID, "%s: top_k=%d not in [0, 1024]", who, top_k);
+  if (win->block_size != 128) return fail(SSA_ERR_UNSUPPORTED, "%s: block_size must be 128", who);
+  if (ceil_div(a->L, 128) > 16384) return fail(SSA_ERR_UNSUPPORTED, "%s: L=%d exceeds 16384 blocks", who, a->L);
+  if (!a->k || !page_idx || !page_cnt || (top_k > 0 && !tok) || !tok_cnt)
+    return fail(SSA_ERR_INVALID, "%s: k, page_idx, page_cnt, tok_cnt (and tok when top_k > 0) must be non-NULL", who);
+  if (!aligned(a->k, 16) || !aligned(page_idx, 4) || !aligned(page_cnt, 4) || !aligned(tok, 4) || !aligned(tok_cnt, 4))
+    return fail(SSA_ERR_INVALID, "%s: k must be 16-byte and the lists 4-byte aligned", who);
+  if (!valid_strides(a->k_stride, 2, who, "k")) return SSA_ERR_INVALID;
+  const size_t need = ssa_page_select_workspace_size(a, win);
+  if (!page_workspace || page_workspace_bytes < need)
+    return fail(SSA_ERR_WORKSPACE, "%s: the page selection workspace of %zu bytes is needed, %zu given", who, need,
+                page_workspace ? page_workspace_bytes : static_cast<size_t>(0));
+  if (!aligned(page_workspace, 256)) return fail(SSA_ERR_INVALID, "%s: page_workspace must be 256-byte aligned", who);
+  ssa::TokenSelectParams p{};
+  p.k = a->k;
+  p.ks_b = a->k_stride[0];
+  p.ks_l = a->k_stride[1];
+  p.ks_h = a->k_stride[2];
+  p.qsum = static_cast<const double*>(page_workspace);
+  p.pidx = page_idx;
+  p.pcnt = page_cnt;
+  p.PW = win->n_global + win->n_local + top_m;
+  p.B = a->B;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.group = a->Hq / a->Hkv;
+  p.D = a->Dqk;
+  p.nqb = static_cast<int32_t>(ceil_div(a->L, 128));
+  p.n_global = win->n_global;
+  p.n_local = win->n_local;
+  p.K = top_k;
+  p.tok = tok;
+  p.tcnt = tok_cnt;
+  return device_status(ssa::launch_token_select(p, as_stream(stream)), who);
 }
 
 }  // extern "C"

@@ -61,6 +61,34 @@ struct ChunkParams : PrefillParams {
   int32_t T, num_pages, max_len;
 };
 
+// Attention over listed key blocks plus listed single tokens of each query
+// block (the second stage of hierarchical indexing): row (b, h, qb) of the
+// token list is tok[b*tok_sb + h*tok_sh + qb*K + e], e < tcnt[b*tcnt_sb +
+// h*tcnt_sh + qb].
+struct TokenParams : PrefillParams {
+  const int32_t* tok;
+  const int32_t* tcnt;
+  int32_t K;
+  int64_t tok_sb, tok_sh, tcnt_sb, tcnt_sh;
+};
+
+// Second stage of hierarchical indexing: page lists as page selection writes
+// them (contiguous [B, Hq, nqb, PW] and [B, Hq, nqb]), the fp64 query-block
+// sums of page selection, token lists out (contiguous [B, Hq, nqb, K] and
+// [B, Hq, nqb]).
+struct TokenSelectParams {
+  const void* k;
+  int64_t ks_b, ks_l, ks_h;
+  const double* qsum;  // [B, Hq, nqb, D]
+  const int32_t* pidx;
+  const int32_t* pcnt;
+  int32_t PW;
+  int32_t B, Hq, Hkv, group, D, nqb;
+  int32_t n_global, n_local, K;
+  int32_t* tok;
+  int32_t* tcnt;
+};
+
 // SSA backward, bf16, Dqk = Dv = 128.  lse is the forward's natural-log sum
 // of exponentials [B, Hq, L]; the workspace holds, per (b, query head, stage
 // of 32 queries), a 64-float record: lse * log2(e) of the 32 rows, then
@@ -148,6 +176,8 @@ hipError_t launch_prefill_wide(const PrefillParams& p, int dqk, int dv, bool out
 bool prefill_d128_supports(const PrefillParams& p, int dqk, int dv);
 hipError_t launch_prefill_d128(const PrefillParams& p, bool out_f32, hipStream_t stream);
 // chunked prefill over a paged cache, bf16, Dqk = Dv = 128
+hipError_t launch_prefill_tokens_d128(const TokenParams& p, bool out_f32, hipStream_t stream);
+hipError_t launch_token_select(const TokenSelectParams& p, hipStream_t stream);
 hipError_t launch_prefill_chunk_d128(const ChunkParams& p, bool out_f32, hipStream_t stream);
 
 // SSA backward (bf16, d = 128): delta / records, dq, dk and dv of the local

@@ -35,6 +35,12 @@
 //     tracking the true max, and once more with it as the reference if it
 //     ended more than 2^64 above the first.  Any fixed reference gives the
 //     same normalised result, so this is exact.
+//
+// TOKENS: after the listed blocks come single tokens of the query block's
+// token list (the second stage of hierarchical indexing), 32 per stage.  The
+// list is copied to LDS once; each token stage's rows are gathered by the
+// same direct-to-LDS loads, one row address per lane, and need no causal
+// mask (every listed token precedes the block).
 #include "attn_d128.hpp"
 
 namespace ssa {
@@ -43,19 +49,36 @@ namespace {
 using namespace d128;
 
 constexpr float kHeadroom = 64.f;  // log2 growth of the max over the reference before a rerun
+constexpr int kMaxTok = 1024;      // token-list capacity (TOKENS)
+
+// the two token-list entries a lane stages in a token stage (rows e and e+16
+// of the stage), read from the LDS copy of the list in an asm block that
+// waits for them (see lds_read_k8 for why slot-area reads are not left to
+// the compiler)
+__device__ __forceinline__ void lds_read_tok2(uint32_t a, int& t0, int& t1) {
+  asm volatile(
+      "ds_read_b32 %0, %2\n"
+      "ds_read_b32 %1, %2 offset:64\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(t0), "=&v"(t1)
+      : "v"(a)
+      : "memory");
+}
 
 // PAGED: chunked prefill over a paged cache.  The workgroup's tile is query
 // block q0/128 + tile of the chunk q0 .. n-1 (q0 = n - T); a key block lives
 // in page block_table[b][block]; queries and outputs are indexed by position
 // - q0.  Everything else is the kernel above with L = n.
-template <bool PAGED>
-using KernelParams = std::conditional_t<PAGED, ChunkParams, PrefillParams>;
+template <bool PAGED, bool TOKENS>
+using KernelParams = std::conditional_t<PAGED, ChunkParams, std::conditional_t<TOKENS, TokenParams, PrefillParams>>;
 
-template <typename OutT, bool DENSE, bool PAGED>
+template <typename OutT, bool DENSE, bool PAGED, bool TOKENS = false>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_d128_kernel(KernelParams<PAGED> p) {
+void prefill_d128_kernel(KernelParams<PAGED, TOKENS> p) {
   static_assert(!(DENSE && PAGED), "no dense layer over a paged cache");
+  static_assert(!(TOKENS && (DENSE || PAGED)), "token lists go with block lists over a plain sequence");
   __shared__ u32x4 ring[kSlots * kSlotBytes / 16];
+  extern __shared__ int32_t tokl[];  // TOKENS: the row's token list, padded to whole stages
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -70,10 +93,11 @@ void prefill_d128_kernel(KernelParams<PAGED> p) {
   const int hk = h / p.group;
   const int qoff = wave * 32;  // this wave's first query inside the block
 
-  // a chunk row that cannot be computed: NaN output and lse, stored as bit
-  // patterns (this file is compiled without NaN semantics)
+  // a row that cannot be computed (a chunk without a valid sequence or page,
+  // an invalid token list): NaN output and lse, stored as bit patterns (this
+  // file is compiled without NaN semantics)
   auto nan_row = [&](int t) {
-    if constexpr (PAGED) {
+    if constexpr (PAGED || TOKENS) {
       OutT* obase = static_cast<OutT*>(p.o) + b * p.os_b + h * p.os_h;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -85,8 +109,11 @@ void prefill_d128_kernel(KernelParams<PAGED> p) {
           else
             *reinterpret_cast<u32x2*>(dst) = u32x2{0x7FC07FC0u, 0x7FC07FC0u};
         }
-      if (p.lse && h32 == 0)
-        reinterpret_cast<uint32_t*>(p.lse)[(static_cast<int64_t>(b) * p.Hq + h) * p.T + t] = 0x7FC00000u;
+      if (p.lse && h32 == 0) {
+        int64_t rows = p.L;
+        if constexpr (PAGED) rows = p.T;
+        reinterpret_cast<uint32_t*>(p.lse)[(static_cast<int64_t>(b) * p.Hq + h) * rows + t] = 0x7FC00000u;
+      }
     }
   };
   int L = p.L, q0 = 0, qb = tile, nkb = p.nqb;  // keys [0, L); first query q0; key blocks [0, nkb)
@@ -135,10 +162,41 @@ void prefill_d128_kernel(KernelParams<PAGED> p) {
       return;
     }
   }
-  const int nst = nblk * (kBlk / kSK);
-  // block of stage s; -1 for a skipped list entry and for stages past the end
+  // TOKENS: the token list of the row, checked and copied to LDS.  Entries
+  // must be ascending, precede the query block and lie outside every listed
+  // block; otherwise every row of the tile is NaN.  Entries past the count up
+  // to the end of its last stage repeat the last token (staged, masked).
+  int ntok = 0;
+  if constexpr (TOKENS) {
+    ntok = min(max(p.tcnt[b * p.tcnt_sb + h * p.tcnt_sh + qb], 0), p.K);
+    const int32_t* tl = p.tok + b * p.tok_sb + h * p.tok_sh + static_cast<int64_t>(qb) * p.K;
+    const int npad = (ntok + kSK - 1) & ~(kSK - 1);
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < kMaxTok / (kWaves * 64); ++j) {
+      const int e = tid + kWaves * 64 * j;
+      if (e < ntok) {
+        const int t = tl[e];
+        const int prev = e > 0 ? tl[e - 1] : -1;
+        bad |= t <= prev || t >= qb * kBlk;
+        for (int i = 0; i < nblk; ++i) bad |= __builtin_amdgcn_readlane(blane, i) == (t >> 7);
+        tokl[e] = t;
+      } else if (e < npad) {
+        tokl[e] = tl[ntok - 1];
+      }
+    }
+    if (__syncthreads_or(bad)) {
+      const int row = qb * kBlk + qoff + c32;
+      if (row < L) nan_row(row);
+      return;
+    }
+  }
+  const int nbs = nblk * (kBlk / kSK);  // block stages; token stages follow
+  const int nst = nbs + (ntok + kSK - 1) / kSK;
+  // block of stage s; -1 for a skipped list entry, a token stage and stages
+  // past the end
   auto stage_block = [&](int s) -> int {
-    if (s >= nst) return -1;
+    if (s >= nbs) return -1;
     if constexpr (DENSE) return qb - (s >> 2);
     return __builtin_amdgcn_readlane(blane, s >> 2);
   };
@@ -154,6 +212,7 @@ void prefill_d128_kernel(KernelParams<PAGED> p) {
   const uint32_t voff = static_cast<uint32_t>(drow * p.vs_l + dunit * 8);
   const int64_t k16 = 16 * p.ks_l, v16 = 16 * p.vs_l;
   const uint32_t ring0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SSA_LDS u32x4*)(ring)));
+  const uint32_t tok0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SSA_LDS int32_t*)(tokl))) + 4 * drow;
   // K fragment c (A operand): row c32, logical unit 2c + h32
   uint32_t kaddr[8];
 #pragma unroll
@@ -222,6 +281,17 @@ void prefill_d128_kernel(KernelParams<PAGED> p) {
         SSA_DMA(vpg + rb * p.vs_l + dunit * 8, vd + 256);
       }
     } else {
+      if constexpr (TOKENS) {
+        if (s >= nbs && s < nst) {  // a token stage: rows are list entries 32(s - nbs) ..
+          int ta, tb;
+          lds_read_tok2(tok0 + 4 * kSK * (s - nbs), ta, tb);
+          SSA_DMA(kbase + static_cast<int64_t>(ta) * p.ks_l + dunit * 8, kd);
+          SSA_DMA(kbase + static_cast<int64_t>(tb) * p.ks_l + dunit * 8, kd + 256);
+          SSA_DMA(vbase + static_cast<int64_t>(ta) * p.vs_l + dunit * 8, vd);
+          SSA_DMA(vbase + static_cast<int64_t>(tb) * p.vs_l + dunit * 8, vd + 256);
+          return;
+        }
+      }
       const int kb = max(stage_block(s), 0);  // skipped entries stage block 0 (unused)
       const int key0 = kb * kBlk + (s & 3) * kSK;
       if (key0 + kSK <= p.L) {
@@ -248,10 +318,11 @@ void prefill_d128_kernel(KernelParams<PAGED> p) {
   auto stage = [&](auto slot_tag, int s, int ns, int nslot) {
     constexpr int SLOT = decltype(slot_tag)::value;
     constexpr int OFF = SLOT * kSlotBytes;
+    const bool tst = TOKENS && s >= nbs;  // a token stage
     const int kb = stage_block(s);
     const int sub = s & 3;
     const int key0 = kb * kBlk + sub * kSK;
-    const bool need = kb >= 0 && key0 < L && !(kb == qb && sub * kSK > qoff + 31);
+    const bool need = tst || (kb >= 0 && key0 < L && !(kb == qb && sub * kSK > qoff + 31));
     if (ns < nst) issue(ns, nslot);
     if (!need) return;
     // S^T = K Q^T: 32 keys x 32 queries
@@ -268,8 +339,15 @@ void prefill_d128_kernel(KernelParams<PAGED> p) {
     // V^T of the stage, read while the score MFMAs run
     u32x2 vraw[16];
     lds_read_vt16<OFF>(vaddr, vraw);
-    // own block: key > query; keys at or past L
-    if (kb == qb || key0 + kSK > L) {
+    // token stage: entries at or past the count
+    if (tst) {
+      const int lim = ntok - 1 - (s - nbs) * kSK - 4 * h32;  // last valid entry offset
+      if ((s - nbs + 1) * kSK > ntok) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + (i & 3) > lim) sc[i] = kNegInf;
+      }
+    } else if (kb == qb || key0 + kSK > L) {  // own block: key > query; keys at or past L
       const int qi = qb * kBlk + qoff + c32;
       const int lim = min(qi, L - 1) - key0 - 4 * h32;  // last valid key offset
 #pragma unroll
@@ -408,9 +486,20 @@ void prefill_d128_kernel(KernelParams<PAGED> p) {
 }
 
 template <typename OutT, bool DENSE, bool PAGED = false>
-hipError_t launch_d128(const KernelParams<PAGED>& p, hipStream_t stream) {
+hipError_t launch_d128(const KernelParams<PAGED, false>& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.nqb) * p.B * p.Hq);
   return launch_kernel(prefill_d128_kernel<OutT, DENSE, PAGED>, grid, dim3(kWaves * 64), 0, stream, p);
+}
+
+template <typename OutT>
+hipError_t launch_d128_tokens(const TokenParams& p, hipStream_t stream) {
+  auto kern = prefill_d128_kernel<OutT, false, false, true>;
+  const size_t lds = sizeof(int32_t) * ((p.K + kSK - 1) & ~(kSK - 1));
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  const dim3 grid(static_cast<unsigned>(p.nqb) * p.B * p.Hq);
+  return launch_kernel(kern, grid, dim3(kWaves * 64), lds, stream, p);
 }
 
 }  // namespace
@@ -422,6 +511,11 @@ bool prefill_d128_supports(const PrefillParams& p, int dqk, int dv) {
 hipError_t launch_prefill_d128(const PrefillParams& p, bool out_f32, hipStream_t stream) {
   if (p.dense) return out_f32 ? launch_d128<float, true>(p, stream) : launch_d128<__bf16, true>(p, stream);
   return out_f32 ? launch_d128<float, false>(p, stream) : launch_d128<__bf16, false>(p, stream);
+}
+
+hipError_t launch_prefill_tokens_d128(const TokenParams& p, bool out_f32, hipStream_t stream) {
+  if (p.W > kMaxW || p.K < 0 || p.K > kMaxTok) return hipErrorNotSupported;
+  return out_f32 ? launch_d128_tokens<float>(p, stream) : launch_d128_tokens<__bf16>(p, stream);
 }
 
 hipError_t launch_prefill_chunk_d128(const ChunkParams& p, bool out_f32, hipStream_t stream) {

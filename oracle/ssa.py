@@ -509,12 +509,12 @@ def token_select(q, k, page_idx, page_cnt, win: Window = DEFAULT_WINDOW, top_k: 
     return tok, tcnt, near
 
 
-def token_list_attention(q, k, v, scale, idx, cnt, tok, tok_cnt, block: int = 128, rows=None):
+def token_list_attention(q, k, v, scale, idx, cnt, tok, tok_cnt, block: int = 128, rows=None, heads=None):
     """Attention of each query over the listed blocks (causal, as in
     ``block_list_attention``) together with the listed single tokens of its
     query block; the tokens all precede the block, so no causal rule applies to
-    them.  ``rows`` (optional) restricts the work to some query blocks (other
-    rows of o / lse are left NaN).
+    them.  ``rows`` / ``heads`` (optional) restrict the work to some query
+    blocks / query heads (other entries of o / lse are left NaN).
 
     Returns o [B, L, Hq, Dv] and lse [B, Hq, L].
     """
@@ -528,7 +528,7 @@ def token_list_attention(q, k, v, scale, idx, cnt, tok, tok_cnt, block: int = 12
         for qb in (range(nqb) if rows is None else rows):
             r0, r1 = qb * block, min((qb + 1) * block, L)
             qi = np.arange(r0, r1)
-            for h in range(Hq):
+            for h in (range(Hq) if heads is None else heads):
                 g = _kv_head(h, Hq, Hkv)
                 ids = [int(t) for t in idx[b, h, qb, :cnt[b, h, qb]] if t >= 0]
                 pos = [j for t in ids for j in range(t * block, min((t + 1) * block, L))]

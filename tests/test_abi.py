@@ -341,6 +341,62 @@ def test_page_select_rejects(lib):
         == ssa.SSA_ERR_UNSUPPORTED
 
 
+def tokens(**over):
+    t = ssa.CTokenLists()
+    t.tok, t.cnt, t.K, t.n_qblocks = FAKE, FAKE, 512, 2
+    for key, val in over.items():
+        setattr(t, key, val)
+    return t
+
+
+@pytest.mark.parametrize("aover,tover,code,needle", [
+    (dict(), dict(K=-1), ssa.SSA_ERR_INVALID, "K="),
+    (dict(), dict(K=1025), ssa.SSA_ERR_INVALID, "K="),
+    (dict(), dict(tok=None), ssa.SSA_ERR_INVALID, "non-NULL"),
+    (dict(), dict(cnt=None, K=0), ssa.SSA_ERR_INVALID, "non-NULL"),
+    (dict(), dict(cnt=FAKE + 2), ssa.SSA_ERR_INVALID, "aligned"),
+    (dict(), dict(n_qblocks=1), ssa.SSA_ERR_INVALID, "rows per head"),
+    (dict(), dict(tok_sb=-1), ssa.SSA_ERR_INVALID, "strides"),
+    (dict(Dqk=64, Dv=64), dict(), ssa.SSA_ERR_UNSUPPORTED, "Dqk = Dv = 128"),
+    (dict(B=0), dict(), ssa.SSA_ERR_INVALID, "sizes"),
+])
+def test_prefill_tokens_rejects(lib, aover, tover, code, needle):
+    a = good_args(**aover)
+    assert lib.ssa_prefill_tokens(ctypes.byref(a), ctypes.byref(lists()), ctypes.byref(tokens(**tover)),
+                                  None) == code
+    assert needle in lib.ssa_last_error().decode()
+    assert lib.ssa_prefill_tokens(ctypes.byref(good_args()), ctypes.byref(lists()), None, None) \
+        == ssa.SSA_ERR_INVALID
+    assert lib.ssa_prefill_tokens(ctypes.byref(good_args()), ctypes.byref(lists(W=0)),
+                                  ctypes.byref(tokens()), None) == ssa.SSA_ERR_INVALID
+
+
+def test_token_select_rejects(lib):
+    a = good_args()
+    w = ssa.CWindow(128, 1, 7)
+    need = lib.ssa_page_select_workspace_size(ctypes.byref(a), ctypes.byref(w))
+
+    def call(a=a, w=w, top_m=8, ws=FAKE, nbytes=need, top_k=512, tok=FAKE):
+        return lib.ssa_token_select(ctypes.byref(a), ctypes.byref(w) if w is not None else None, top_m, FAKE,
+                                    FAKE, ws, nbytes, top_k, tok, FAKE, None)
+    assert call(nbytes=need - 1) == ssa.SSA_ERR_WORKSPACE
+    assert "workspace" in lib.ssa_last_error().decode()
+    assert call(ws=None) == ssa.SSA_ERR_WORKSPACE
+    assert call(ws=FAKE + 16) == ssa.SSA_ERR_INVALID
+    assert call(top_m=33) == ssa.SSA_ERR_INVALID
+    assert call(top_k=-1) == ssa.SSA_ERR_INVALID
+    assert call(top_k=1025) == ssa.SSA_ERR_INVALID
+    assert call(tok=None) == ssa.SSA_ERR_INVALID
+    assert call(tok=FAKE + 1) == ssa.SSA_ERR_INVALID
+    assert call(w=None) == ssa.SSA_ERR_INVALID
+    assert call(w=ssa.CWindow(64, 1, 7)) == ssa.SSA_ERR_UNSUPPORTED
+    assert call(a=good_args(Dqk=576, Dv=512)) == ssa.SSA_ERR_UNSUPPORTED
+    assert call(a=good_args(dtype=ssa.DTYPE_F32, out_dtype=ssa.DTYPE_F32, Dqk=64, Dv=64)) == ssa.SSA_ERR_UNSUPPORTED
+    assert call(a=good_args(Hq=3)) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_token_select(None, ctypes.byref(w), 8, FAKE, FAKE, FAKE, need, 8, FAKE, FAKE, None) \
+        == ssa.SSA_ERR_INVALID
+
+
 def test_error_is_thread_local(lib):
     import threading
     a = good_args(B=0)
