@@ -644,6 +644,7 @@ def main():
     if run["hi"]:  # f2: the window's blocks plus K tokens of the recalled pages
         K5 = W5["K"]
         lists5w = ssa.lists_from_index(*ssa.block_index(nqb5, device=dev))
+        wst5 = torch.empty((ssa.token_select_workspace_size(q5, k5, M5) + 256,), dtype=torch.uint8, device=dev)
         o5h = torch.empty((1, H5, L5, D5), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
     # a4 inputs: values N(0,1)/24, drawn on the device (the query is 38.6 GB)
     if run["mla"]:
@@ -746,7 +747,7 @@ def main():
             ssa.prefill_backward(q2, k2, v2, ob, gb, lseb, dq=dqb, dk=dkb, dv=dvb, workspace=wsb)
         mark(10)
         if run["hi"]:
-            t5, tc5 = ssa.token_select(q5, k5, i5, c5, ws5, top_m=M5, top_k=K5)
+            t5, tc5 = ssa.token_select(q5, k5, i5, c5, ws5, top_m=M5, top_k=K5, workspace=wst5)
         mark(11)
         if run["hi"]:
             ssa.prefill_tokens(q5, k5, v5, lists5w, ssa.token_lists(t5, tc5), out=o5h)

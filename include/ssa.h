@@ -382,22 +382,29 @@ int ssa_page_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_m
  *      < sum of q over block qb , k_j >      (kv head of h, fp64)
  * Candidates are the tokens of the pages c of row (b, h, qb) of page_idx /
  * page_cnt with n_global <= c <= qb - n_local (the pages outside the window;
- * a repeated page counts once; at most the 32 lowest such pages).  The top_k
- * highest scores are kept, equal scores preferring the lower token; with at
- * most top_k candidates all are kept.  Output lists are ascending, padded with
- * -1:  tok [B, Hq, nqb, top_k],  tok_cnt [B, Hq, nqb]  (contiguous), ready for
- * ssa_prefill_tokens with tok_sb = Hq*nqb*top_k, tok_sh = nqb*top_k,
- * cnt_sb = Hq*nqb, cnt_sh = nqb.
+ * a repeated page counts once; at most the top_m lowest such pages).  The
+ * top_k highest scores are kept, equal scores preferring the lower token;
+ * with at most top_k candidates all are kept.  Output lists are ascending,
+ * padded with -1:  tok [B, Hq, nqb, top_k],  tok_cnt [B, Hq, nqb]
+ * (contiguous), ready for ssa_prefill_tokens with tok_sb = Hq*nqb*top_k,
+ * tok_sh = nqb*top_k, cnt_sb = Hq*nqb, cnt_sh = nqb.
  * page_idx / page_cnt are the contiguous lists ssa_page_select wrote with the
  * same a, win and top_m, and page_workspace is the workspace of that call
  * (it holds the fp64 query-block sums), ordered before this call on the
  * stream.  Uses a.k, its strides, a.dtype (BF16), B, L, Hq, Hkv, Dqk (64 or
  * 128).  0 <= top_m <= 32; 0 <= top_k <= 1024 (tok may be NULL when
- * top_k = 0; tok_cnt is then all 0).
+ * top_k = 0; tok_cnt is then all 0).  The work runs page by page (each
+ * recalled page is read once per query head and scored for every query block
+ * that recalled it), through a caller-owned device workspace of at least
+ * ssa_token_select_workspace_size bytes, 256-byte aligned (B*Hq*nqb*(12 +
+ * 8*top_m + 1024*top_m) bytes, about 134 MB at B = 1, Hq = 16, L = 131072,
+ * top_m = 8); SSA_ERR_WORKSPACE if it is missing or short.
  * ------------------------------------------------------------------------- */
+size_t ssa_token_select_workspace_size(const ssa_attn_args* a, const ssa_window* win, int32_t top_m);
 int ssa_token_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_m, const int32_t* page_idx,
                      const int32_t* page_cnt, const void* page_workspace, size_t page_workspace_bytes,
-                     int32_t top_k, int32_t* tok, int32_t* tok_cnt, void* stream);
+                     int32_t top_k, int32_t* tok, int32_t* tok_cnt, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /* Text of the calling thread's last error ("" if none).  Valid until the
  * thread's next failing call. */

@@ -31,7 +31,8 @@ EXPORTS = (
     "ssa_block_index", "ssa_block_index_seq", "ssa_prefill", "ssa_prefill_tokens", "ssa_dense_causal",
     "ssa_prefill_chunk", "ssa_prefill_backward", "ssa_prefill_backward_workspace_size", "ssa_decode",
     "ssa_decode_dense", "ssa_decode_dense_workspace_size", "ssa_decode_workspace_size", "ssa_page_select",
-    "ssa_page_select_workspace_size", "ssa_token_select", "ssa_last_error", "ssa_version",
+    "ssa_page_select_workspace_size", "ssa_token_select", "ssa_token_select_workspace_size", "ssa_last_error",
+    "ssa_version",
 )
 
 
@@ -165,7 +166,9 @@ def load(path: str = LIB_PATH):
     lib.ssa_prefill_tokens.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CBlockLists),
                                        ctypes.POINTER(CTokenLists), vp]
     lib.ssa_token_select.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CWindow), i32, vp, vp, vp,
-                                     ctypes.c_size_t, i32, vp, vp, vp]
+                                     ctypes.c_size_t, i32, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.ssa_token_select_workspace_size.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CWindow), i32]
+    lib.ssa_token_select_workspace_size.restype = ctypes.c_size_t
     lib.ssa_dense_causal.argtypes = [ctypes.POINTER(CAttnArgs), vp]
     lib.ssa_prefill_chunk.argtypes = [ctypes.POINTER(CChunkArgs), ctypes.POINTER(CBlockLists), vp]
     lib.ssa_prefill_backward.argtypes = [ctypes.POINTER(CBwdArgs), ctypes.POINTER(CWindow), vp]
@@ -546,8 +549,15 @@ def prefill_tokens(q, k, v, lists: CBlockLists, tokens: CTokenLists, scale=None,
     return out, lse
 
 
+def token_select_workspace_size(q, k, top_m: int = 8, window: Window = DEFAULT_WINDOW) -> int:
+    lib = load()
+    a = _attn_args(q, k, k, q, None, 1.0)
+    w = window.c()
+    return int(lib.ssa_token_select_workspace_size(ctypes.byref(a), ctypes.byref(w), top_m))
+
+
 def token_select(q, k, page_idx, page_cnt, page_workspace, top_m: int = 8, top_k: int = 512,
-                 window: Window = DEFAULT_WINDOW, stream=None):
+                 window: Window = DEFAULT_WINDOW, workspace=None, stream=None):
     """ssa_token_select after page_select(q, k, top_m, window, workspace=page_workspace):
     (tok int32 [B, Hq, nqb, top_k], tok_cnt int32 [B, Hq, nqb])."""
     lib = load()
@@ -557,9 +567,13 @@ def token_select(q, k, page_idx, page_cnt, page_workspace, top_m: int = 8, top_k
     tcnt = torch.empty((B, Hq, nqb), dtype=torch.int32, device=q.device)
     a = _attn_args(q, k, k, q, None, 1.0)
     w = window.c()
-    base, nbytes = _aligned256(page_workspace)
-    _check(lib.ssa_token_select(ctypes.byref(a), ctypes.byref(w), top_m, _ptr(page_idx), _ptr(page_cnt), base,
-                                nbytes, top_k, _ptr(tok), _ptr(tcnt), _stream(stream)))
+    if workspace is None:
+        need = int(lib.ssa_token_select_workspace_size(ctypes.byref(a), ctypes.byref(w), top_m))
+        workspace = torch.empty((need + 256,), dtype=torch.uint8, device=q.device)
+    pbase, pbytes = _aligned256(page_workspace)
+    wbase, wbytes = _aligned256(workspace)
+    _check(lib.ssa_token_select(ctypes.byref(a), ctypes.byref(w), top_m, _ptr(page_idx), _ptr(page_cnt), pbase,
+                                pbytes, top_k, _ptr(tok), _ptr(tcnt), wbase, wbytes, _stream(stream)))
     return tok, tcnt
 
 

@@ -594,9 +594,15 @@ int ssa_page_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_m
   return device_status(ssa::launch_page_select(p, as_stream(stream)), who);
 }
 
+size_t ssa_token_select_workspace_size(const ssa_attn_args* a, const ssa_window* win, int32_t top_m) {
+  if (!a || !win || a->B < 1 || a->L < 1 || a->Hq < 1 || win->block_size < 1 || top_m < 0 || top_m > 32) return 0;
+  return ssa::token_select_workspace_bytes(a->B, a->Hq, static_cast<int32_t>(ceil_div(a->L, win->block_size)), top_m);
+}
+
 int ssa_token_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_m, const int32_t* page_idx,
                      const int32_t* page_cnt, const void* page_workspace, size_t page_workspace_bytes,
-                     int32_t top_k, int32_t* tok, int32_t* tok_cnt, void* stream) {
+                     int32_t top_k, int32_t* tok, int32_t* tok_cnt, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   const char* who = "ssa_token_select";
   if (!a) return fail(SSA_ERR_INVALID, "%s: args is NULL", who);
   if (!valid_window(win, who, 64)) return SSA_ERR_INVALID;
@@ -611,16 +617,23 @@ int ssa_token_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_
   if (top_k < 0 || top_k > 1024) return fail(SSA_ERR_INVALID, "%s: top_k=%d not in [0, 1024]", who, top_k);
   if (win->block_size != 128) return fail(SSA_ERR_UNSUPPORTED, "%s: block_size must be 128", who);
   if (ceil_div(a->L, 128) > 16384) return fail(SSA_ERR_UNSUPPORTED, "%s: L=%d exceeds 16384 blocks", who, a->L);
+  if (static_cast<int64_t>(a->B) * a->Hq * ceil_div(a->L, 128) > (int64_t{1} << 31) - 1)
+    return fail(SSA_ERR_UNSUPPORTED, "%s: B*Hq*ceil(L/128) exceeds 2^31 - 1 rows", who);
   if (!a->k || !page_idx || !page_cnt || (top_k > 0 && !tok) || !tok_cnt)
     return fail(SSA_ERR_INVALID, "%s: k, page_idx, page_cnt, tok_cnt (and tok when top_k > 0) must be non-NULL", who);
   if (!aligned(a->k, 16) || !aligned(page_idx, 4) || !aligned(page_cnt, 4) || !aligned(tok, 4) || !aligned(tok_cnt, 4))
     return fail(SSA_ERR_INVALID, "%s: k must be 16-byte and the lists 4-byte aligned", who);
   if (!valid_strides(a->k_stride, 2, who, "k")) return SSA_ERR_INVALID;
-  const size_t need = ssa_page_select_workspace_size(a, win);
-  if (!page_workspace || page_workspace_bytes < need)
-    return fail(SSA_ERR_WORKSPACE, "%s: the page selection workspace of %zu bytes is needed, %zu given", who, need,
+  const size_t pneed = ssa_page_select_workspace_size(a, win);
+  if (!page_workspace || page_workspace_bytes < pneed)
+    return fail(SSA_ERR_WORKSPACE, "%s: the page selection workspace of %zu bytes is needed, %zu given", who, pneed,
                 page_workspace ? page_workspace_bytes : static_cast<size_t>(0));
   if (!aligned(page_workspace, 256)) return fail(SSA_ERR_INVALID, "%s: page_workspace must be 256-byte aligned", who);
+  const size_t need = ssa_token_select_workspace_size(a, win, top_m);
+  if (!workspace || workspace_bytes < need)
+    return fail(SSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
+                workspace ? workspace_bytes : static_cast<size_t>(0));
+  if (!aligned(workspace, 256)) return fail(SSA_ERR_INVALID, "%s: workspace must be 256-byte aligned", who);
   ssa::TokenSelectParams p{};
   p.k = a->k;
   p.ks_b = a->k_stride[0];
@@ -630,6 +643,7 @@ int ssa_token_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_
   p.pidx = page_idx;
   p.pcnt = page_cnt;
   p.PW = win->n_global + win->n_local + top_m;
+  p.S = top_m;
   p.B = a->B;
   p.Hq = a->Hq;
   p.Hkv = a->Hkv;
@@ -641,6 +655,20 @@ int ssa_token_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_
   p.K = top_k;
   p.tok = tok;
   p.tcnt = tok_cnt;
+  const size_t R = static_cast<size_t>(a->B) * a->Hq * p.nqb;
+  auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  char* w = static_cast<char*>(workspace);
+  p.cnt = reinterpret_cast<int32_t*>(w);
+  w += r256(4 * R);
+  p.off = reinterpret_cast<int32_t*>(w);
+  w += r256(4 * R);
+  p.npg = reinterpret_cast<int32_t*>(w);
+  w += r256(4 * R);
+  p.pages = reinterpret_cast<int32_t*>(w);
+  w += r256(4 * R * top_m);
+  p.ent = reinterpret_cast<int32_t*>(w);
+  w += r256(4 * R * top_m);
+  p.keys = reinterpret_cast<uint64_t*>(w);
   return device_status(ssa::launch_token_select(p, as_stream(stream)), who);
 }
 

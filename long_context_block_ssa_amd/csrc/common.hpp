@@ -75,19 +75,29 @@ struct TokenParams : PrefillParams {
 // Second stage of hierarchical indexing: page lists as page selection writes
 // them (contiguous [B, Hq, nqb, PW] and [B, Hq, nqb]), the fp64 query-block
 // sums of page selection, token lists out (contiguous [B, Hq, nqb, K] and
-// [B, Hq, nqb]).
+// [B, Hq, nqb]).  Workspace (R = B*Hq*nqb rows, S = slots per row = top_m):
+// per (b, h, page) recall counts and bucket offsets, per row the candidate
+// pages, the buckets (which rows recalled a page, and in which slot), and per
+// row S*128 score keys.
 struct TokenSelectParams {
   const void* k;
   int64_t ks_b, ks_l, ks_h;
   const double* qsum;  // [B, Hq, nqb, D]
   const int32_t* pidx;
   const int32_t* pcnt;
-  int32_t PW;
+  int32_t PW, S;
   int32_t B, Hq, Hkv, group, D, nqb;
   int32_t n_global, n_local, K;
   int32_t* tok;
   int32_t* tcnt;
+  int32_t* cnt;    // [R] recalls of page (b, h, c), then the fill cursor
+  int32_t* off;    // [R] bucket start of page (b, h, c) inside the (b, h) region of ent
+  int32_t* npg;    // [R] candidate pages of row (b, h, qb); 0 once the row is final
+  int32_t* pages;  // [R, S] ascending candidate pages
+  int32_t* ent;    // [B*Hq, nqb*S] bucket entries qb*S + slot
+  uint64_t* keys;  // [R, S*128] order-preserving score keys
 };
+size_t token_select_workspace_bytes(int32_t B, int32_t Hq, int32_t nqb, int32_t S);
 
 // SSA backward, bf16, Dqk = Dv = 128.  lse is the forward's natural-log sum
 // of exponentials [B, Hq, L]; the workspace holds, per (b, query head, stage

@@ -375,10 +375,19 @@ def test_token_select_rejects(lib):
     a = good_args()
     w = ssa.CWindow(128, 1, 7)
     need = lib.ssa_page_select_workspace_size(ctypes.byref(a), ctypes.byref(w))
+    tneed = lib.ssa_token_select_workspace_size(ctypes.byref(a), ctypes.byref(w), 8)
+    R = 1 * 2 * 2
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert tneed == 3 * r256(4 * R) + 2 * r256(4 * R * 8) + r256(8 * R * 8 * 128)
+    assert lib.ssa_token_select_workspace_size(ctypes.byref(a), ctypes.byref(w), 33) == 0
+    assert lib.ssa_token_select_workspace_size(None, ctypes.byref(w), 8) == 0
 
-    def call(a=a, w=w, top_m=8, ws=FAKE, nbytes=need, top_k=512, tok=FAKE):
+    def call(a=a, w=w, top_m=8, ws=FAKE, nbytes=need, top_k=512, tok=FAKE, tws=FAKE, tbytes=tneed):
         return lib.ssa_token_select(ctypes.byref(a), ctypes.byref(w) if w is not None else None, top_m, FAKE,
-                                    FAKE, ws, nbytes, top_k, tok, FAKE, None)
+                                    FAKE, ws, nbytes, top_k, tok, FAKE, tws, tbytes, None)
+    assert call(tbytes=tneed - 1) == ssa.SSA_ERR_WORKSPACE
+    assert call(tws=None) == ssa.SSA_ERR_WORKSPACE
+    assert call(tws=FAKE + 16) == ssa.SSA_ERR_INVALID
     assert call(nbytes=need - 1) == ssa.SSA_ERR_WORKSPACE
     assert "workspace" in lib.ssa_last_error().decode()
     assert call(ws=None) == ssa.SSA_ERR_WORKSPACE
@@ -393,7 +402,7 @@ def test_token_select_rejects(lib):
     assert call(a=good_args(Dqk=576, Dv=512)) == ssa.SSA_ERR_UNSUPPORTED
     assert call(a=good_args(dtype=ssa.DTYPE_F32, out_dtype=ssa.DTYPE_F32, Dqk=64, Dv=64)) == ssa.SSA_ERR_UNSUPPORTED
     assert call(a=good_args(Hq=3)) == ssa.SSA_ERR_INVALID
-    assert lib.ssa_token_select(None, ctypes.byref(w), 8, FAKE, FAKE, FAKE, need, 8, FAKE, FAKE, None) \
+    assert lib.ssa_token_select(None, ctypes.byref(w), 8, FAKE, FAKE, FAKE, need, 8, FAKE, FAKE, FAKE, tneed, None) \
         == ssa.SSA_ERR_INVALID
 
 

@@ -207,3 +207,39 @@ def test_hi_cfg5_full(lib):
         rows = slice(qb * 128, (qb + 1) * 128)
         check_close(to_f64(o[0, rows][:, heads]), ro[0, rows][:, heads], f"cfg5 qb={qb}")
         check_close(to_f64(lse[0, heads][:, rows]), rl[0, heads][:, rows], f"cfg5 lse qb={qb}")
+
+
+def test_cli_index_shared_by_a_layer_pair(lib):
+    """Cross-layer index reuse: the owner layer's page and token lists, computed
+    once from its q and k, drive the next layer's attention over that layer's
+    own q, k and v."""
+    L, H, D, M, K = 128 * 22 + 9, 2, 128, 8, 256
+    qh1, q1 = gen(67, synth.Q, 1, L, H, D)
+    kh1, k1 = gen(67, synth.K, 1, L, H, D)
+    qh2, q2 = gen(68, synth.Q, 1, L, H, D)
+    kh2, k2 = gen(68, synth.K, 1, L, H, D)
+    vh2, v2 = gen(68, synth.V, 1, L, H, D)
+    from long_context_block_ssa_amd import page_select_workspace_size
+    say("CLI: lists of layer 1, attention of layer 2")
+    ws = torch.empty((page_select_workspace_size(q1, k1) + 256,), dtype=torch.uint8, device=q1.device)
+    pidx, pcnt = lib.page_select(q1, k1, top_m=M, workspace=ws)
+    tok, tcnt = lib.token_select(q1, k1, pidx, pcnt, ws, top_m=M, top_k=K)
+    nqb = (L + 127) // 128
+    widx, wcnt = lib.block_index(nqb)
+    o2, l2 = lib.prefill_tokens(q2, k2, v2, lib.lists_from_index(widx, wcnt), lib.token_lists(tok, tcnt),
+                                with_lse=True)
+    op, lp = lib.prefill(q2, k2, v2, lib.lists_per_head(pidx, pcnt), with_lse=True)
+    torch.cuda.synchronize()
+    ridx, rcnt, pnear = oracle.page_select(qh1, kh1, top_m=M)
+    rtok, rtcnt, near = oracle.token_select(qh1, kh1, ridx, rcnt, top_k=K)
+    assert not (pnear.any() or near.any())
+    compare_tokens(tok, tcnt, rtok, rtcnt, near)
+    wi, wc = oracle.block_index(nqb)
+    w4 = np.broadcast_to(wi[None, None], (1, H, nqb, wi.shape[1]))
+    c3 = np.broadcast_to(wc[None, None], (1, H, nqb))
+    ro, rl = oracle.token_list_attention(qh2, kh2, vh2, 1 / math.sqrt(D), w4, c3, rtok, rtcnt)
+    check_close(to_f64(o2), ro, "layer 2 over layer 1's tokens: o")
+    check_close(to_f64(l2), rl, "layer 2 over layer 1's tokens: lse")
+    rpo, rpl = oracle.block_list_attention(qh2, kh2, vh2, 1 / math.sqrt(D), ridx, rcnt)
+    check_close(to_f64(op), rpo, "layer 2 over layer 1's pages: o")
+    check_close(to_f64(lp), rpl, "layer 2 over layer 1's pages: lse")
