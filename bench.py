@@ -643,7 +643,8 @@ def main():
         ws5 = torch.empty((ssa.page_select_workspace_size(q5, k5) + 256,), dtype=torch.uint8, device=dev)
     if run["hi"]:  # f2: the window's blocks plus K tokens of the recalled pages
         K5 = W5["K"]
-        lists5w = ssa.lists_from_index(*ssa.block_index(nqb5, device=dev))
+        win5 = ssa.block_index(nqb5, device=dev)  # held: the lists point into these tensors
+        lists5w = ssa.lists_from_index(*win5)
         wst5 = torch.empty((ssa.token_select_workspace_size(q5, k5, M5) + 256,), dtype=torch.uint8, device=dev)
         o5h = torch.empty((1, H5, L5, D5), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
     # a4 inputs: values N(0,1)/24, drawn on the device (the query is 38.6 GB)
@@ -692,7 +693,8 @@ def main():
         lists6 = ssa.lists_from_index(idx6, cnt6)
     # f3 inputs: the a2 forward's output and lse, an incoming gradient
     if run["bwd"]:
-        lists2 = ssa.lists_from_index(*ssa.block_index(nqb2, device=dev))
+        win2 = ssa.block_index(nqb2, device=dev)
+        lists2 = ssa.lists_from_index(*win2)
         ob, lseb = ssa.prefill(q2, k2, v2, lists2, with_lse=True)
         gb = up(synth.seq_tensor(s2, 90, 1, L2, H2, D2))
         dqb, dkb, dvb = (torch.empty((1, H2, L2, D2), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
@@ -733,7 +735,8 @@ def main():
             ssa.prefill(q5, k5, v5, ssa.lists_per_head(i5, c5), out=o5)
         mark(6)
         if run["mla"]:
-            ssa.prefill(q4, c4, c4[..., :DV4], ssa.lists_from_index(*ssa.block_index(L4 // 128, device=dev)),
+            win4 = ssa.block_index(L4 // 128, device=dev)
+            ssa.prefill(q4, c4, c4[..., :DV4], ssa.lists_from_index(*win4),
                         scale=1 / 24, out=o4)
         mark(7)
         if run["mla"]:

@@ -281,7 +281,8 @@ def block_index_seq(seq_lens: torch.Tensor, window: Window = DEFAULT_WINDOW, str
 
 
 def lists_from_index(idx: torch.Tensor, cnt: torch.Tensor) -> CBlockLists:
-    """Block lists shared by every batch and head (the SSA window)."""
+    """Block lists shared by every batch and head (the SSA window).  The struct
+    holds raw device pointers: keep idx and cnt alive while it is in use."""
     lists = CBlockLists()
     lists.idx, lists.cnt = _ptr(idx), _ptr(cnt)
     lists.W, lists.n_qblocks = idx.shape[1], idx.shape[0]
@@ -290,7 +291,8 @@ def lists_from_index(idx: torch.Tensor, cnt: torch.Tensor) -> CBlockLists:
 
 
 def lists_per_head(idx: torch.Tensor, cnt: torch.Tensor) -> CBlockLists:
-    """Block lists per (batch, query head): idx [B, Hq, nqb, W], cnt [B, Hq, nqb]."""
+    """Block lists per (batch, query head): idx [B, Hq, nqb, W], cnt [B, Hq, nqb].
+    Keep idx and cnt alive while the struct is in use."""
     assert idx.is_contiguous() and cnt.is_contiguous()
     B, H, nqb, W = idx.shape
     lists = CBlockLists()
@@ -526,7 +528,8 @@ def _aligned256(workspace):
 
 
 def token_lists(tok: torch.Tensor, tok_cnt: torch.Tensor) -> CTokenLists:
-    """Token lists per (batch, query head): tok [B, Hq, nqb, K], tok_cnt [B, Hq, nqb]."""
+    """Token lists per (batch, query head): tok [B, Hq, nqb, K], tok_cnt [B, Hq, nqb].
+    Keep tok and tok_cnt alive while the struct is in use."""
     assert tok.is_contiguous() and tok_cnt.is_contiguous()
     B, H, nqb, K = tok.shape
     t = CTokenLists()
