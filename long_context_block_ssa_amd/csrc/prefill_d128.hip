@@ -315,15 +315,16 @@ void prefill_d128_kernel(KernelParams<PAGED, TOKENS> p) {
 
   // ---- one stage: keys of stage s in ring slot SLOT; first this wave's
   // loads of stage ns (if any) into slot nslot ------------------------------
-  auto stage = [&](auto slot_tag, int s, int ns, int nslot) {
+  auto stage = [&](auto slot_tag, auto steady_tag, int s, int ns, int nslot) {
     constexpr int SLOT = decltype(slot_tag)::value;
+    constexpr bool STEADY = decltype(steady_tag)::value;  // ns < nst is known
     constexpr int OFF = SLOT * kSlotBytes;
     const bool tst = TOKENS && s >= nbs;  // a token stage
     const int kb = stage_block(s);
     const int sub = s & 3;
     const int key0 = kb * kBlk + sub * kSK;
     const bool need = tst || (kb >= 0 && key0 < L && !(kb == qb && sub * kSK > qoff + 31));
-    if (ns < nst) issue(ns, nslot);
+    if (STEADY || ns < nst) issue(ns, nslot);
     if (!need) return;
     // S^T = K Q^T: 32 keys x 32 queries
     f32x16 sc;
@@ -424,11 +425,29 @@ void prefill_d128_kernel(KernelParams<PAGED, TOKENS> p) {
     // Whole groups of 4 stages, so that the loop is left only at its end;
     // stages past the end only take the barrier.
     const int nst_pad = (nst + kSlots - 1) & ~(kSlots - 1);
-    for (int s0 = 0; s0 < nst_pad; s0 += kSlots) {
+    int s0 = 0;
+    // steady groups: every stage exists and issues the stage kSlots-1 ahead,
+    // so the wait before the next stage is always "kSlots-2 stages still in
+    // flight" (no runtime choice of the wait, no existence tests)
+    for (; s0 + 2 * kSlots - 2 < nst; s0 += kSlots) {
+#define SSA_STAGE(k)                                                                          \
+  {                                                                                           \
+    const int s = s0 + (k);                                                                   \
+    stage(std::integral_constant<int, (k)>{}, std::true_type{}, s, s + kSlots - 1, ((k) + kSlots - 1) % kSlots); \
+    wait_stages(kSlots - 2);                                                                  \
+    stage_barrier();                                                                          \
+  }
+      SSA_STAGE(0)
+      SSA_STAGE(1)
+      SSA_STAGE(2)
+      SSA_STAGE(3)
+#undef SSA_STAGE
+    }
+    for (; s0 < nst_pad; s0 += kSlots) {
 #define SSA_STAGE(k)                                                                 \
   {                                                                                  \
     const int s = s0 + (k);                                                          \
-    if (s < nst) stage(std::integral_constant<int, (k)>{}, s, s + kSlots - 1, ((k) + kSlots - 1) % kSlots); \
+    if (s < nst) stage(std::integral_constant<int, (k)>{}, std::false_type{}, s, s + kSlots - 1, ((k) + kSlots - 1) % kSlots); \
     settle(s);                                                                       \
   }
       SSA_STAGE(0)
