@@ -222,14 +222,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     }
   };
 
-  auto stage = [&](auto slot_tag, int s, int ns, int nslot) {
+  auto stage = [&](auto slot_tag, auto steady_tag, int s, int ns, int nslot) {
     constexpr int SLOT = decltype(slot_tag)::value;
+    constexpr bool STEADY = decltype(steady_tag)::value;  // ns < nst is known
     constexpr int OFF = SLOT * kSlotBytes;
     const int kb = stage_block(s);
     const int sub = s & 3;
     const int key0 = kb * kBlk + sub * kSK;
     const bool need = kb >= 0 && key0 < L && !(kb == qb && sub * kSK > qoff + 31);
-    if (ns < nst) issue(ns, nslot);
+    if (STEADY || ns < nst) issue(ns, nslot);
     if (!need) return;
     f32x16 sc, dp;
 #pragma unroll
@@ -293,11 +294,27 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   wait_stages(kSlots - 2);
   stage_barrier();
   const int nst_pad = (nst + kSlots - 1) & ~(kSlots - 1);
-  for (int s0 = 0; s0 < nst_pad; s0 += kSlots) {
+  int s0 = 0;
+  // steady groups: every stage exists and issues the stage kSlots-1 ahead
+  for (; s0 + 2 * kSlots - 2 < nst; s0 += kSlots) {
 #define SSA_STAGE(k)                                                                                        \
   {                                                                                                         \
     const int s = s0 + (k);                                                                                 \
-    if (s < nst) stage(std::integral_constant<int, (k)>{}, s, s + kSlots - 1, ((k) + kSlots - 1) % kSlots); \
+    stage(std::integral_constant<int, (k)>{}, std::true_type{}, s, s + kSlots - 1, ((k) + kSlots - 1) % kSlots); \
+    wait_stages(kSlots - 2);                                                                              \
+    stage_barrier();                                                                                        \
+  }
+    SSA_STAGE(0)
+    SSA_STAGE(1)
+    SSA_STAGE(2)
+    SSA_STAGE(3)
+#undef SSA_STAGE
+  }
+  for (; s0 < nst_pad; s0 += kSlots) {
+#define SSA_STAGE(k)                                                                                        \
+  {                                                                                                         \
+    const int s = s0 + (k);                                                                                 \
+    if (s < nst) stage(std::integral_constant<int, (k)>{}, std::false_type{}, s, s + kSlots - 1, ((k) + kSlots - 1) % kSlots); \
     settle(s);                                                                                              \
   }
     SSA_STAGE(0)
@@ -438,15 +455,16 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p, int 
     SSA_DMA(rec, rd);
   };
 
-  auto stage = [&](auto slot_tag, int s, int ns, int nslot) {
+  auto stage = [&](auto slot_tag, auto steady_tag, int s, int ns, int nslot) {
     constexpr int SLOT = decltype(slot_tag)::value;
+    constexpr bool STEADY = decltype(steady_tag)::value;  // ns < nst is known
     constexpr int OFF = SLOT * kSlotBytes;
     int hq, q0;
     stage_rows(s, hq, q0);
     const int qb = q0 / kBlk;
     // nothing to do: no query of the stage reaches this wave's keys, or they do not exist
     const bool need = q0 < L && wave_keys && !(qb == kb && q0 + kSK - 1 < kb * kBlk + wave * 32);
-    if (ns < nst) issue(ns, nslot);
+    if (STEADY || ns < nst) issue(ns, nslot);
     if (!need) return;
     // S = Q K^T and dP = dO V^T: 32 queries x this wave's 32 keys, one key per lane
     f32x16 sc, dp;
@@ -533,11 +551,27 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p, int 
   wait_stages5(kSlots - 2);
   stage_barrier();
   const int nst_pad = (nst + kSlots - 1) & ~(kSlots - 1);
-  for (int s0 = 0; s0 < nst_pad; s0 += kSlots) {
+  int s0 = 0;
+  // steady groups: every stage exists and issues the stage kSlots-1 ahead
+  for (; s0 + 2 * kSlots - 2 < nst; s0 += kSlots) {
 #define SSA_STAGE(k)                                                                                        \
   {                                                                                                         \
     const int s = s0 + (k);                                                                                 \
-    if (s < nst) stage(std::integral_constant<int, (k)>{}, s, s + kSlots - 1, ((k) + kSlots - 1) % kSlots); \
+    stage(std::integral_constant<int, (k)>{}, std::true_type{}, s, s + kSlots - 1, ((k) + kSlots - 1) % kSlots); \
+    wait_stages5(kSlots - 2);                                                                              \
+    stage_barrier();                                                                                        \
+  }
+    SSA_STAGE(0)
+    SSA_STAGE(1)
+    SSA_STAGE(2)
+    SSA_STAGE(3)
+#undef SSA_STAGE
+  }
+  for (; s0 < nst_pad; s0 += kSlots) {
+#define SSA_STAGE(k)                                                                                        \
+  {                                                                                                         \
+    const int s = s0 + (k);                                                                                 \
+    if (s < nst) stage(std::integral_constant<int, (k)>{}, std::false_type{}, s, s + kSlots - 1, ((k) + kSlots - 1) % kSlots); \
     settle(s);                                                                                              \
   }
     SSA_STAGE(0)
