@@ -50,6 +50,7 @@ constexpr int kTsThreads = 256;
 constexpr int kTsWaves = kTsThreads / 64;
 constexpr int kMaxSlots = 32;
 constexpr int kEnt = 16;  // recalling rows staged per round of the score kernel
+static_assert(kTsThreads / 16 == kEnt, "the score kernel stages one recalling row per 16 threads");
 
 // order-preserving map of a score to an unsigned key (larger score -> larger
 // key); -0 is folded onto +0 and NaN onto -inf
@@ -219,6 +220,9 @@ __global__ __launch_bounds__(kTsThreads) __attribute__((amdgpu_waves_per_eu(3)))
         for (int j = 0; j < CPT; ++j) tv[j] = src[j];
 #pragma unroll
         for (int j = 0; j < CPT; ++j) qs[ee][ch0 + j] = tv[j];
+      } else {  // unused A rows: zeros (their outputs are not stored)
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) qs[ee][ch0 + j] = 0.0;
       }
     }
     __syncthreads();
