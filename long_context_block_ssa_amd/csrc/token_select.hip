@@ -29,9 +29,9 @@
 //      (the key rows stay bf16 in registers and are widened per step),
 //      writing order-preserving 64-bit keys (NaN counts as -inf, -0 as +0)
 //      into each recalling row's slot;
-//   5. select: one workgroup per open row finds the K-th largest key T
-//      exactly by a radix select (LDS histograms, 8 bits a pass; once at most
-//      64 keys share the leading bits found so far, one wave ranks those by
+//   5. select: one wave per open row finds the K-th largest key T exactly
+//      by a radix select (LDS histograms, 8 bits a pass; once at most 64
+//      keys share the leading bits found so far, they are ranked by
 //      counting), keeps every key
 //      above T and, of the keys equal to T, the needed number with the lowest
 //      candidate index (= lowest token), and writes them in candidate order,
@@ -254,121 +254,122 @@ __global__ __launch_bounds__(kTsThreads) __attribute__((amdgpu_waves_per_eu(3)))
   }
 }
 
-// 5. one workgroup per open row
+// lanes below this one whose bit is set in b
+__device__ __forceinline__ int rank_below(uint64_t b) {
+  return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u)));
+}
+
+// 5. one wave per open row, four rows per workgroup; everything stays inside
+// the wave (its own LDS regions, ballots and lane shuffles), so no workgroup
+// barrier is needed
 __global__ __launch_bounds__(kTsThreads) void ts_select_kernel(TokenSelectParams p) {
-  extern __shared__ uint64_t key[];  // S * 128 keys (dynamic: 8 KB at S = 8)
-  __shared__ uint32_t hist[256];
-  __shared__ int32_t spg[kMaxSlots];
-  __shared__ int32_t wsum[kTsWaves];
-  __shared__ int32_t s_need, s_left;
-  __shared__ uint64_t s_prefix;
-  __shared__ uint64_t small[64];
-  const int64_t row = blockIdx.x;
+  extern __shared__ uint64_t lds_keys[];  // per wave: S * 128 keys
+  __shared__ uint32_t hist_all[kTsWaves][256];
+  __shared__ uint64_t small_all[kTsWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t R = static_cast<int64_t>(p.B) * p.Hq * p.nqb;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kTsWaves + wave;
+  if (row >= R) return;  // whole waves
   const int npg = p.npg[row];
   if (npg == 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint64_t* key = lds_keys + static_cast<size_t>(wave) * p.S * 128;
+  uint32_t* hist = hist_all[wave];
+  uint64_t* small = small_all[wave];
   const int C = npg * 128, K = p.K;
   const uint64_t* src = p.keys + row * p.S * 128;
-  for (int r = tid; r < C; r += kTsThreads) key[r] = src[r];
-  if (tid < npg) spg[tid] = p.pages[row * p.S + tid];
-  __syncthreads();
+  for (int r = lane; r < C; r += 64) key[r] = src[r];
+  const int cpg = p.pages[row * p.S + (lane < npg ? lane : 0)];  // page of slot `lane`
+  __builtin_amdgcn_wave_barrier();
 
   // the K-th largest key T, 8 bits at a time: `need` keys are still to be
-  // chosen among those whose leading bits equal `prefix`, and at least that
-  // many exist
+  // chosen among those whose leading `bits` bits equal `prefix`, and at least
+  // that many exist
   uint64_t prefix = 0;
   int need = K, bits = 0;
   for (int pass = 0; pass < 8; ++pass) {
     const int shift = 56 - 8 * pass;
-    hist[tid] = 0;  // 256 threads, 256 bins
-    __syncthreads();
-    for (int r = tid; r < C; r += kTsThreads) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0;
+    __builtin_amdgcn_wave_barrier();
+    for (int r = lane; r < C; r += 64) {
       const uint64_t kk = key[r];
       if (pass == 0 || (kk >> (shift + 8)) == prefix) atomicAdd(&hist[(kk >> shift) & 255], 1u);
     }
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t cb[4], tot = 0;  // bins in descending order, 4 per lane
+    __builtin_amdgcn_wave_barrier();
+    uint32_t cb[4], tot = 0;  // bins in descending order, 4 per lane
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        cb[q] = hist[255 - 4 * lane - q];
-        tot += cb[q];
-      }
-      uint32_t incl = tot;
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-      }
-      uint32_t run = incl - tot;  // keys in higher bins
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (run < static_cast<uint32_t>(need) && run + cb[q] >= static_cast<uint32_t>(need)) {
-          s_prefix = (prefix << 8) | static_cast<uint64_t>(255 - 4 * lane - q);
-          s_need = need - static_cast<int>(run);
-          s_left = static_cast<int>(cb[q]);
-        }
-        run += cb[q];
-      }
+    for (int q = 0; q < 4; ++q) {
+      cb[q] = hist[255 - 4 * lane - q];
+      tot += cb[q];
     }
-    __syncthreads();
-    prefix = s_prefix;
-    need = s_need;
+    uint32_t incl = tot;
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    uint32_t run = incl - tot;  // keys in higher bins
+    int fbin = -1, fneed = 0, fleft = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (run < static_cast<uint32_t>(need) && run + cb[q] >= static_cast<uint32_t>(need)) {
+        fbin = 255 - 4 * lane - q;
+        fneed = need - static_cast<int>(run);
+        fleft = static_cast<int>(cb[q]);
+      }
+      run += cb[q];
+    }
+    const int sl = static_cast<int>(__builtin_ctzll(__builtin_amdgcn_ballot_w64(fbin >= 0)));  // one lane
+    prefix = (prefix << 8) | static_cast<uint64_t>(__builtin_amdgcn_readlane(fbin, sl));
+    need = __builtin_amdgcn_readlane(fneed, sl);
+    const int left = __builtin_amdgcn_readlane(fleft, sl);
     bits = 8 * (pass + 1);
-    const int left = s_left;
-    __syncthreads();  // every thread has read the pass's results
-    if (left <= 64) break;  // few keys left: one wave finishes below
+    __builtin_amdgcn_wave_barrier();  // the histogram is read before the next pass clears it
+    if (left <= 64) break;            // few keys left: ranked by counting below
   }
   uint64_t T = prefix;
   if (bits < 64) {
-    // the keys whose leading `bits` bits equal prefix (at most 64) into LDS,
-    // in any order; then the need-th largest of them by counting
-    if (tid == 0) s_left = 0;
-    __syncthreads();
-    for (int r = tid; r < C; r += kTsThreads) {
-      const uint64_t kk = key[r];
-      if ((kk >> (64 - bits)) == prefix) small[atomicAdd(&s_left, 1)] = kk;
+    int m = 0;
+    for (int r0 = 0; r0 < C; r0 += 64) {  // C is a multiple of 128
+      const uint64_t kk = key[r0 + lane];
+      const bool in = (kk >> (64 - bits)) == prefix;
+      const uint64_t bl = __builtin_amdgcn_ballot_w64(in);
+      if (in) small[m + rank_below(bl)] = kk;
+      m += static_cast<int>(__popcll(bl));
     }
-    __syncthreads();
-    if (wave == 0) {
-      const int m = s_left;
-      const uint64_t mine = lane < m ? small[lane] : 0;
-      int gt = 0, ge = 0;
-      for (int j = 0; j < m; ++j) {
-        const uint64_t o = small[j];
-        gt += o > mine;
-        ge += o >= mine;
-      }
-      if (lane < m && gt < need && ge >= need) {  // lanes holding T agree
-        s_prefix = mine;
-        s_need = need - gt;
-      }
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t mine = lane < m ? small[lane] : 0;
+    int gt = 0, ge = 0;
+    for (int j = 0; j < m; ++j) {
+      const uint64_t o = small[j];
+      gt += o > mine;
+      ge += o >= mine;
     }
-    __syncthreads();
-    T = s_prefix;
-    need = s_need;
+    const int sl = static_cast<int>(
+        __builtin_ctzll(__builtin_amdgcn_ballot_w64(lane < m && gt < need && ge >= need)));  // lanes holding T
+    T = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mine >> 32), sl)))
+         << 32) |
+        static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(mine)), sl));
+    need -= __builtin_amdgcn_readlane(gt, sl);
   }
 
   // every key above T, and of those equal to T the first `need` in candidate
-  // order; written in candidate order
+  // order; written in candidate order (e = r0 + lane, r0 ascending)
   int32_t* trow = p.tok + row * K;
-  const int per = (C + kTsThreads - 1) / kTsThreads;
-  const int e0 = min(tid * per, C), e1 = min(e0 + per, C);
-  int eq = 0;
-  for (int e = e0; e < e1; ++e) eq += key[e] == T;
-  int eq_before = block_excl_scan(eq, wsum);
-  const int eq_start = eq_before;
-  int mine = 0;
-  for (int e = e0; e < e1; ++e) {
+  int eqc = 0, at = 0;
+  for (int r0 = 0; r0 < C; r0 += 64) {
+    const int e = r0 + lane;
     const uint64_t kk = key[e];
-    mine += kk > T || (kk == T && eq_before++ < need);
+    const bool eq = kk == T;
+    const uint64_t be = __builtin_amdgcn_ballot_w64(eq);
+    const bool sel = kk > T || (eq && eqc + rank_below(be) < need);
+    const uint64_t bs = __builtin_amdgcn_ballot_w64(sel);
+    const int page = __builtin_amdgcn_readlane(cpg, r0 >> 7);  // 64 | 128: one page per r0
+    if (sel) trow[at + rank_below(bs)] = page * 128 + (e & 127);
+    eqc += static_cast<int>(__popcll(be));
+    at += static_cast<int>(__popcll(bs));
   }
-  int at = block_excl_scan(mine, wsum);
-  eq_before = eq_start;
-  for (int e = e0; e < e1; ++e) {
-    const uint64_t kk = key[e];
-    if (kk > T || (kk == T && eq_before++ < need)) trow[at++] = spg[e >> 7] * 128 + (e & 127);
-  }
-  if (tid == 0) p.tcnt[row] = K;
+  if (lane == 0) p.tcnt[row] = K;
 }
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
@@ -398,11 +399,11 @@ hipError_t launch_token_select(const TokenSelectParams& p, hipStream_t stream) {
   e = p.D == 128 ? launch_kernel(ts_score_kernel<128>, dim3(static_cast<unsigned>(R)), dim3(kTsThreads), 0, stream, p)
                  : launch_kernel(ts_score_kernel<64>, dim3(static_cast<unsigned>(R)), dim3(kTsThreads), 0, stream, p);
   if (e != hipSuccess) return e;
-  const size_t lds = sizeof(uint64_t) * 128 * static_cast<size_t>(p.S);
+  const size_t lds = sizeof(uint64_t) * 128 * static_cast<size_t>(p.S) * kTsWaves;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(ts_select_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  return launch_kernel(ts_select_kernel, dim3(static_cast<unsigned>(R)), dim3(kTsThreads), lds, stream, p);
+  return launch_kernel(ts_select_kernel, dim3(wave_groups), dim3(kTsThreads), lds, stream, p);
 }
 
 }  // namespace ssa
