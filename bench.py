@@ -5,6 +5,7 @@ One step = one pass over every row of the path on resident synthetic inputs:
 
   a1  block index            (256 query blocks)
   a2  SSA prefill            B=1, H=16, d=128, L=32768, bf16, layout [B, H, L, D]
+                             (and the small fp32 case B=1, H=1, d=64, L=2048, timed too)
   a3  SSA decode             batch 64, H=16/16, d=128, context ~ U[65536, 131072]
   a4  latent-shared shape    prefill B=1, L=262144, 128 heads x 576/512 (V = first 512
                              channels of the shared latent); decode batch 8 at 1,048,576
@@ -46,11 +47,14 @@ import synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3
+PEAK_FP64_TFLOPS = 78.6
 
 # ----------------------------------------------------------------------------
 # workload sizes and algorithmic work (closed forms of the window)
 # ----------------------------------------------------------------------------
 
+W1 = dict(B=1, L=2048, H=1, D=64, seed=1)
 W2 = dict(B=1, L=32768, H=16, D=128, seed=2)
 W3 = dict(B=64, H=16, D=128, lo=65536, hi=131072, seed=3)
 W5 = dict(B=1, L=131072, H=16, D=128, M=8, K=512, seed=5)
@@ -146,12 +150,37 @@ def _cpu_task(qb):
     return qb
 
 
+def host_cores():
+    """Host cores this process may use: its CPU affinity set, capped by the
+    cgroup CPU quota and by OMP_NUM_THREADS when those are set (a GPU machine gives
+    each GPU a share of its cores and says so there), with the CPU model."""
+    n = len(os.sched_getaffinity(0))
+    limits = {"affinity": n}
+    try:
+        quota, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if quota != "max":
+            limits["cgroup_quota"] = max(1, int(int(quota) // int(period)))
+    except (OSError, ValueError):
+        pass
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        limits["omp_num_threads"] = max(1, int(os.environ["OMP_NUM_THREADS"]))
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return min(limits.values()), model, limits
+
+
 def cpu_baseline(budget_s: float = 25.0):
     L, H, D, seed = W2["L"], W2["H"], W2["D"], W2["seed"]
     _CPU["q"] = synth.bf16_bits_to_f32(synth.seq_tensor(seed, synth.Q, 1, L, H, D))
     _CPU["k"] = synth.bf16_bits_to_f32(synth.seq_tensor(seed, synth.K, 1, L, H, D))
     _CPU["v"] = synth.bf16_bits_to_f32(synth.seq_tensor(seed, synth.V, 1, L, H, D))
-    cores = min(16, len(os.sched_getaffinity(0)))
+    cores, model, limits = host_cores()
     ctx = mp.get_context("fork")
     nqb = L // 128
     order = list(range(nqb - 1, -1, -1))  # bench order: last query blocks first
@@ -178,10 +207,12 @@ def cpu_baseline(budget_s: float = 25.0):
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": cores,
+        "cpu_model": model,
+        "core_limits": limits,
         "kind": "oracle",
         "sample": f"float64 numpy oracle, SSA prefill of the L={L} H={H} d={D} workload: {len(done)} query-block "
                   f"rows x {H} heads ({len(done) / nqb:.2f} passes over its {nqb} query blocks), "
-                  f"{dt:.1f} s wall on {cores} processes",
+                  f"{dt:.1f} s wall on {cores} processes (one per usable host core, {model})",
         "seconds": dt,
     }
 
@@ -605,6 +636,14 @@ def main():
         q2, k2, v2 = (up(synth.seq_tensor(s2, t, 1, L2, H2, D2)) for t in (synth.Q, synth.K, synth.V))
         o2 = torch.empty((1, H2, L2, D2), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
         od = torch.empty_like(o2)
+    # a2 fp32 inputs (the small case: one head, d = 64, L = 2048)
+    L1, H1, D1, s1 = W1["L"], W1["H"], W1["D"], W1["seed"]
+    if run["prefill"]:
+        q1, k1, v1 = (torch.from_numpy(np.ascontiguousarray(synth.seq_tensor(s1, t, 1, L1, H1, D1, "f32"))).to(dev)
+                      for t in (synth.Q, synth.K, synth.V))
+        o1 = torch.empty_like(q1)
+        win1 = ssa.block_index(L1 // 128, device=dev)
+        lists1 = ssa.lists_from_index(*win1)
     # a3 inputs: one paged pool, several independent (q, table) sets
     B3, H3, D3, s3 = W3["B"], W3["H"], W3["D"], W3["seed"]
     lens = synth.decode_seq_lens(s3, B3, W3["lo"], W3["hi"])
@@ -704,7 +743,7 @@ def main():
 
     rows = ["a1 block_index", "a2 ssa_prefill", "a3 ssa_decode", "a5 dense_causal", "a6-a7 page_select",
             "a8 page_prefill", "a4 mla_prefill", "a4 mla_decode", "f1 chunk_prefill", "f3 ssa_backward",
-            "f2 token_select", "f2 hi_prefill"]
+            "f2 token_select", "f2 hi_prefill", "a2 ssa_prefill_f32"]
     nev = len(rows) + 1
 
     if run["copy"]:
@@ -755,6 +794,9 @@ def main():
         if run["hi"]:
             ssa.prefill_tokens(q5, k5, v5, lists5w, ssa.token_lists(t5, tc5), out=o5h)
         mark(12)
+        if run["prefill"]:
+            ssa.prefill(q1, k1, v1, lists1, out=o1)
+        mark(13)
         if run["copy"]:
             cp_dst.copy_(cp_src)
 
@@ -777,11 +819,13 @@ def main():
 
     if only:
         return
-    for t, name in ((o2, "ssa"), (o3, "decode"), (od, "dense"), (o5, "page"), (o4[0, -128:], "mla"),
+    for t, name in ((o1, "ssa f32"), (o2, "ssa"), (o3, "decode"), (od, "dense"), (o5, "page"), (o4[0, -128:], "mla"),
                     (o4d, "mla decode"), (o6, "chunk"), (dqb, "dq"), (dkb, "dk"), (dvb, "dv"), (o5h, "hi")):
         if not torch.isfinite(t.float()).all():
             raise RuntimeError(f"non-finite {name} output")
 
+    f1 = ssa_flops(L1, H1, D1)
+    t1 = per_row[12] * 1e-3
     f2 = ssa_flops(L2, H2, D2)
     t2 = per_row[1] * 1e-3
     tf2 = f2 / t2 / 1e12
@@ -808,6 +852,11 @@ def main():
                          "unit": "TFLOP/s", "frac": f5 / (per_row[5] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                          "us": per_row[5] * 1e3, "work": f5},
         "block_index": {"us": per_row[0] * 1e3},
+        # the small fp32 case: 16 query blocks cannot fill 256 CUs; its time is
+        # the latency of one tile, reported against the fp32 MFMA peak
+        "ssa_prefill_f32": {"bound": "latency", "achieved": f1 / t1 / 1e12, "peak": PEAK_FP32_TFLOPS,
+                            "unit": "TFLOP/s", "frac": f1 / t1 / 1e12 / PEAK_FP32_TFLOPS, "us": per_row[12] * 1e3,
+                            "work": f1, "tokens_per_s": L1 / t1},
     }
     f4 = mla_flops(L4, H4, DQ4, DV4)
     b4 = mla_decode_bytes(lens4, H4, DQ4, DV4)

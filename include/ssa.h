@@ -211,7 +211,13 @@ int ssa_dense_causal(const ssa_attn_args* a, void* stream);
 /* ---------------------------------------------------------------------------
  * ssa_decode -- one decode step of SSA over a paged cache: the query at
  * position n - 1 reads the window of its block (block 0 and the 7 most recent
- * blocks, the last one holding (n - 1) mod 128 + 1 valid keys).  The window is
+ * blocks, the last one holding (n - 1) mod 128 + 1 valid keys) -- the fixed
+ * 1024-token window of the sparse layers (QbitAI report on LongCat LoZA, the
+ * paragraph on streaming sparse attention: 1 global + 7 local blocks of 128
+ * tokens), with the masked softmax of equation (2) of the "LoZA: ZigZag
+ * sparse attention" page (section 2.1).  Decoding at long context is bound by
+ * reading the cache (LongCat sparse attention article, section 1), so each
+ * window block is read once, as whole contiguous pages.  The window is
  * split over its blocks and the per-block softmax partials are merged exactly
  * (max-subtracted pieces rescaled to the common maximum): inside one kernel
  * for the 64- and 128-wide heads, through the workspace and a second kernel

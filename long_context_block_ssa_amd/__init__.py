@@ -13,7 +13,10 @@ There is no fallback: if the library is missing, every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
+import inspect
 import math
 import os
 from dataclasses import dataclass
@@ -21,7 +24,9 @@ from dataclasses import dataclass
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "_lib", "libssa.so")
+# SSA_LIB_PATH selects another build of the same library (the host-sanitized
+# one, for the CPU-side checks of the C ABI)
+LIB_PATH = os.environ.get("SSA_LIB_PATH") or os.path.join(_PKG, "_lib", "libssa.so")
 
 SSA_OK, SSA_ERR_INVALID, SSA_ERR_UNSUPPORTED, SSA_ERR_DEVICE, SSA_ERR_WORKSPACE = range(5)
 DTYPE_F32, DTYPE_BF16 = 0, 1
@@ -207,6 +212,22 @@ def version() -> int:
     return load().ssa_version()
 
 
+def _on_stream(fn):
+    """Run an entry point with ``stream`` (when given) as torch's current stream,
+    so that the outputs and temporaries it allocates belong to the stream its
+    kernels run on: the caching allocator then hands their memory only to work
+    ordered after those kernels."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        stream = sig.bind_partial(*args, **kwargs).arguments.get("stream")
+        ctx = torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+        with ctx:
+            return fn(*args, **kwargs)
+    return wrapper
+
+
 def _stream(stream=None) -> int:
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
@@ -259,6 +280,7 @@ def _out(q, v, out_dtype, with_lse):
 # entry points
 # ---------------------------------------------------------------------------
 
+@_on_stream
 def block_index(n_qblocks: int, window: Window = DEFAULT_WINDOW, device="cuda", stream=None):
     """ssa_block_index: (idx int32 [n_qblocks, W], cnt int32 [n_qblocks])."""
     lib = load()
@@ -269,6 +291,7 @@ def block_index(n_qblocks: int, window: Window = DEFAULT_WINDOW, device="cuda", 
     return idx, cnt
 
 
+@_on_stream
 def block_index_seq(seq_lens: torch.Tensor, window: Window = DEFAULT_WINDOW, stream=None):
     """ssa_block_index_seq for decode rows (seq_lens int32 [B] on the device)."""
     lib = load()
@@ -303,6 +326,7 @@ def lists_per_head(idx: torch.Tensor, cnt: torch.Tensor) -> CBlockLists:
     return lists
 
 
+@_on_stream
 def prefill(q, k, v, lists: CBlockLists, scale=None, out=None, out_dtype=None, with_lse=False,
             lse=None, stream=None):
     """ssa_prefill over the given block lists.  Returns (o, lse or None)."""
@@ -315,6 +339,7 @@ def prefill(q, k, v, lists: CBlockLists, scale=None, out=None, out_dtype=None, w
     return out, lse
 
 
+@_on_stream
 def ssa(q, k, v, scale=None, window: Window = DEFAULT_WINDOW, out_dtype=None, with_lse=False, stream=None):
     """Block index + SSA prefill, the two calls of the hot path."""
     nqb = (q.shape[1] + window.block_size - 1) // window.block_size
@@ -323,6 +348,7 @@ def ssa(q, k, v, scale=None, window: Window = DEFAULT_WINDOW, out_dtype=None, wi
                    with_lse=with_lse, stream=stream)
 
 
+@_on_stream
 def dense_causal(q, k, v, scale=None, out=None, out_dtype=None, with_lse=False, lse=None, stream=None):
     """ssa_dense_causal: the dense comparison layer."""
     lib = load()
@@ -334,6 +360,7 @@ def dense_causal(q, k, v, scale=None, out=None, out_dtype=None, with_lse=False, 
     return out, lse
 
 
+@_on_stream
 def prefill_chunk(q, k_pages, v_pages, block_table, seq_lens, lists: CBlockLists, scale=None, out=None,
                   out_dtype=None, with_lse=False, lse=None, stream=None):
     """ssa_prefill_chunk: q [B, T, Hq, D] = the last T positions of each cached
@@ -390,6 +417,7 @@ def prefill_backward_workspace_size(q, k, window: Window = DEFAULT_WINDOW) -> in
     return int(load().ssa_prefill_backward_workspace_size(ctypes.byref(a), ctypes.byref(w)))
 
 
+@_on_stream
 def prefill_backward(q, k, v, o, dout, lse, scale=None, window: Window = DEFAULT_WINDOW, grad_dtype=None,
                      dq=None, dk=None, dv=None, workspace=None, stream=None):
     """ssa_prefill_backward: (dq, dk, dv) of the SSA prefill whose output o and
@@ -419,6 +447,7 @@ def decode_workspace_size(B: int, Hq: int, Dqk: int, Dv: int, window: Window = D
     return int(load().ssa_decode_workspace_size(ctypes.byref(a), ctypes.byref(w)))
 
 
+@_on_stream
 def decode(q, k_pages, v_pages, block_table, seq_lens, scale=None, window: Window = DEFAULT_WINDOW,
            out=None, with_lse=False, lse=None, workspace=None, stream=None):
     """ssa_decode over a paged cache.  Returns (o [B, Hq, Dv], lse [B, Hq] or None).
@@ -460,6 +489,7 @@ def decode(q, k_pages, v_pages, block_table, seq_lens, scale=None, window: Windo
     return out, lse
 
 
+@_on_stream
 def decode_dense(q, k_pages, v_pages, block_table, seq_lens, scale=None, out=None, with_lse=False, lse=None,
                  workspace=None, stream=None):
     """ssa_decode_dense: the new query over every cached key.  Returns (o [B, Hq, Dv], lse or None)."""
@@ -501,6 +531,7 @@ def page_select_workspace_size(q, k, window: Window = DEFAULT_WINDOW) -> int:
     return int(lib.ssa_page_select_workspace_size(ctypes.byref(a), ctypes.byref(w)))
 
 
+@_on_stream
 def page_select(q, k, top_m: int = 8, window: Window = DEFAULT_WINDOW, workspace=None, stream=None):
     """ssa_page_select: (idx int32 [B, Hq, nqb, W], cnt int32 [B, Hq, nqb])."""
     lib = load()
@@ -540,6 +571,7 @@ def token_lists(tok: torch.Tensor, tok_cnt: torch.Tensor) -> CTokenLists:
     return t
 
 
+@_on_stream
 def prefill_tokens(q, k, v, lists: CBlockLists, tokens: CTokenLists, scale=None, out=None, out_dtype=None,
                    with_lse=False, lse=None, stream=None):
     """ssa_prefill_tokens: attention over the block lists plus the token lists.  Returns (o, lse or None)."""
@@ -559,6 +591,7 @@ def token_select_workspace_size(q, k, top_m: int = 8, window: Window = DEFAULT_W
     return int(lib.ssa_token_select_workspace_size(ctypes.byref(a), ctypes.byref(w), top_m))
 
 
+@_on_stream
 def token_select(q, k, page_idx, page_cnt, page_workspace, top_m: int = 8, top_k: int = 512,
                  window: Window = DEFAULT_WINDOW, workspace=None, stream=None):
     """ssa_token_select after page_select(q, k, top_m, window, workspace=page_workspace):
@@ -580,10 +613,12 @@ def token_select(q, k, page_idx, page_cnt, page_workspace, top_m: int = 8, top_k
     return tok, tcnt
 
 
+@_on_stream
 def hi_attention(q, k, v, top_m: int = 8, top_k: int = 512, scale=None, window: Window = DEFAULT_WINDOW,
-                 out_dtype=None, with_lse=False, stream=None):
+                 out_dtype=None, with_lse=False, with_pages=False, stream=None):
     """Both stages of hierarchical indexing, then attention over the window blocks
-    plus the chosen tokens.  Returns (o, lse, tok, tok_cnt)."""
+    plus the chosen tokens.  Returns (o, lse, tok, tok_cnt), followed by the
+    first stage's (page_idx, page_cnt) when ``with_pages``."""
     B, L, Hq, _ = q.shape
     ws = torch.empty((page_select_workspace_size(q, k, window) + 256,), dtype=torch.uint8, device=q.device)
     pidx, pcnt = page_select(q, k, top_m, window, workspace=ws, stream=stream)
@@ -592,9 +627,12 @@ def hi_attention(q, k, v, top_m: int = 8, top_k: int = 512, scale=None, window: 
     widx, wcnt = block_index(nqb, window, device=q.device, stream=stream)
     o, lse = prefill_tokens(q, k, v, lists_from_index(widx, wcnt), token_lists(tok, tcnt), scale=scale,
                             out_dtype=out_dtype, with_lse=with_lse, stream=stream)
+    if with_pages:
+        return o, lse, tok, tcnt, pidx, pcnt
     return o, lse, tok, tcnt
 
 
+@_on_stream
 def page_attention(q, k, v, top_m: int = 8, scale=None, window: Window = DEFAULT_WINDOW, out_dtype=None,
                    with_lse=False, stream=None):
     """Page selection followed by attention over the per-head lists."""

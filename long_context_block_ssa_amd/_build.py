@@ -50,9 +50,30 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-x", "hip", "-c", src, "-o", obj]
+# Host-side sanitizers for the C-ABI layer only (argument validation, error
+# strings): AddressSanitizer and UndefinedBehaviorSanitizer on the host pass of
+# api.cpp; device code is never instrumented.  The resulting library needs the
+# ASan runtime preloaded into the (uninstrumented) Python process.
+SAN_LIB = os.path.join(OUT_DIR, "libssa_san.so")
+SAN_OBJ_DIR = os.path.join(ROOT, "_build", "obj_san")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-shared-libasan"]
+SAN_SOURCES = ("api.cpp",)
+
+
+def asan_runtime() -> str:
+    """Path of the shared ASan runtime of hipcc's clang (to LD_PRELOAD)."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
+    name = os.path.basename(src)
+    san = sanitize and name in SAN_SOURCES
+    obj = os.path.join(SAN_OBJ_DIR if san else OBJ_DIR, name + ".o")
+    extra = SAN_FLAGS if san else []
+    cmd = [HIPCC, *COMMON_FLAGS, *FILE_FLAGS.get(name, []), *extra, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -63,22 +84,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, sanitize: bool = False) -> str:
+    """Build libssa.so; with ``sanitize`` build libssa_san.so instead, whose
+    C-ABI layer carries the host sanitizers (kernels are the same objects)."""
     os.makedirs(OBJ_DIR, exist_ok=True)
+    os.makedirs(SAN_OBJ_DIR, exist_ok=True)
     os.makedirs(OUT_DIR, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda f: _compile(f, sanitize), srcs))
+    out = SAN_LIB if sanitize else LIB
+    tmp = out + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *(SAN_FLAGS if sanitize else []), *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
-    return LIB
+        print(f"built {out} from {len(srcs)} sources")
+    return out
 
 
 if __name__ == "__main__":
-    build()
+    build(sanitize="--sanitize" in sys.argv[1:])

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <tuple>
 #include <type_traits>
 #include <utility>
@@ -23,6 +24,26 @@ hipError_t launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t s
         return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, shmem, stream);
       },
       held);
+}
+
+// Raise the dynamic-LDS limit of kernel KERN to `bytes` (the largest any call
+// may pass) once per device.  The limit is a process-wide attribute of the
+// function: setting it on every call with that call's own size would let one
+// host thread lower it between another thread's set and launch.
+constexpr int kMaxDevices = 64;
+template <auto KERN>
+hipError_t raise_lds_limit_once(int bytes) {
+  static std::once_flag once[kMaxDevices];
+  static hipError_t status[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [&] {
+    status[dev] = hipFuncSetAttribute(reinterpret_cast<const void*>(KERN),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  });
+  return status[dev];
 }
 
 // ---------------------------------------------------------------------------

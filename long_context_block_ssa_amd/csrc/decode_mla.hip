@@ -382,9 +382,8 @@ hipError_t launch_mla(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.B) * W * static_cast<unsigned>(p.Hq / (kHeads * HG)));
   const size_t lds = sizeof(f32x4) * kSteps * HG * kMWaves * 64 + sizeof(u32x4) * kMWaves * kGroups * 64 +
                      sizeof(bf16x4) * kSteps * HG * 64 + 2 * sizeof(float) * kSteps * HG * kHeads;
-  auto kern = decode_mla_partial_kernel<SHARED, HG>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(lds));
+  constexpr auto kern = decode_mla_partial_kernel<SHARED, HG>;
+  hipError_t e = raise_lds_limit_once<kern>(static_cast<int>(lds));
   if (e != hipSuccess) return e;
   e = launch_kernel(kern, grid, dim3(kMWaves * 64), lds, stream, p);
   if (e != hipSuccess) return e;

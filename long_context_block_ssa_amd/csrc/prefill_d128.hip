@@ -512,10 +512,9 @@ hipError_t launch_d128(const KernelParams<PAGED, false>& p, hipStream_t stream) 
 
 template <typename OutT>
 hipError_t launch_d128_tokens(const TokenParams& p, hipStream_t stream) {
-  auto kern = prefill_d128_kernel<OutT, false, false, true>;
+  constexpr auto kern = prefill_d128_kernel<OutT, false, false, true>;
   const size_t lds = sizeof(int32_t) * ((p.K + kSK - 1) & ~(kSK - 1));
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(lds));
+  hipError_t e = raise_lds_limit_once<kern>(static_cast<int>(sizeof(int32_t) * kMaxTok));
   if (e != hipSuccess) return e;
   const dim3 grid(static_cast<unsigned>(p.nqb) * p.B * p.Hq);
   return launch_kernel(kern, grid, dim3(kWaves * 64), lds, stream, p);

@@ -655,8 +655,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   const unsigned bh = static_cast<unsigned>(p.B) * p.Hkv;
   const int n_part_items = n_glob * p.nparts * static_cast<int>(bh);
   const unsigned items = static_cast<unsigned>(n_part_items) + static_cast<unsigned>(p.nqb - n_glob) * bh;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_dkdv_kernel<GradT>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kDkdvLds);
+  e = raise_lds_limit_once<bwd_dkdv_kernel<GradT>>(kDkdvLds);
   if (e != hipSuccess) return e;
   e = launch_kernel(bwd_dkdv_kernel<GradT>, dim3(items), dim3(kWaves * 64), kDkdvLds, stream, p, n_part_items);
   if (e != hipSuccess) return e;

@@ -400,8 +400,7 @@ hipError_t launch_token_select(const TokenSelectParams& p, hipStream_t stream) {
                  : launch_kernel(ts_score_kernel<64>, dim3(static_cast<unsigned>(R)), dim3(kTsThreads), 0, stream, p);
   if (e != hipSuccess) return e;
   const size_t lds = sizeof(uint64_t) * 128 * static_cast<size_t>(p.S) * kTsWaves;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(ts_select_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          static_cast<int>(lds));
+  e = raise_lds_limit_once<ts_select_kernel>(static_cast<int>(sizeof(uint64_t) * 128 * kMaxSlots * kTsWaves));
   if (e != hipSuccess) return e;
   return launch_kernel(ts_select_kernel, dim3(wave_groups), dim3(kTsThreads), lds, stream, p);
 }

@@ -36,6 +36,9 @@ against the sources by eye:
   variant (LongCat sparse attention article, section 3: streaming-aware
   indexing keeps sink + local window, hierarchical indexing scores 128-token
   pages and keeps the top-M).
+* ``page_scores_exact`` / ``token_scores_exact`` -- one row's selection scores
+  as exact rationals with the rounding band the selections are certified
+  against, so that a list decided differently inside that band can be judged.
 * ``token_select`` / ``token_list_attention`` -- the second stage of
   hierarchical indexing (same section: inside the recalled pages every token is
   scored and the top K are kept) and attention over window blocks plus those
@@ -68,6 +71,8 @@ from .ssa import (  # noqa: F401
     chunk_prefill,
     block_sums,
     page_select,
+    page_scores_exact,
+    token_scores_exact,
     block_list_rows,
     block_list_attention,
     token_select,

@@ -409,6 +409,63 @@ def page_select(q, k, win: Window = DEFAULT_WINDOW, top_m: int = 8, heads=None):
     return idx, cnt, near
 
 
+def _exact_block_sum(rows):
+    """Exact rational per-channel sum of the rows [n, D] (their float values are
+    dyadic, so every partial sum is exact)."""
+    rows = np.asarray(rows, np.float64)
+    return [sum((Fraction(float(x)) for x in rows[:, d]), Fraction(0)) for d in range(rows.shape[1])]
+
+
+def page_scores_exact(q, k, b, h, qb, win: Window = DEFAULT_WINDOW):
+    """The first-stage scores of one row (batch b, query head h, query block qb)
+    as exact rationals, for judging a selection that float rounding may have
+    decided differently (LongCat sparse attention article, section 3,
+    hierarchical indexing: a coarse score per 128-token page).
+
+    Returns (cands, exact, band): the candidate pages [n_global, qb - n_local],
+    their scores <sum of q over block qb, sum of k over page c> as Fractions,
+    and per candidate the rounding band 1e-9 * sum |a_d b_d| that
+    ``page_select`` certifies its float64 decisions against.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    _, L, Hq, _ = q.shape
+    g = _kv_head(h, Hq, k.shape[2])
+    bs = win.block_size
+    cands = list(range(win.n_global, qb - win.n_local + 1))
+    qsum = _exact_block_sum(q[b, qb * bs:min((qb + 1) * bs, L), h])
+    af = np.asarray([float(x) for x in qsum])
+    exact, band = [], []
+    for c in cands:
+        ksum = _exact_block_sum(k[b, c * bs:min((c + 1) * bs, L), g])
+        exact.append(sum((a * x for a, x in zip(qsum, ksum)), Fraction(0)))
+        band.append(1e-9 * float(np.abs(af) @ np.abs(np.asarray([float(x) for x in ksum]))))
+    return cands, exact, band
+
+
+def token_scores_exact(q, k, pages, b, h, qb, win: Window = DEFAULT_WINDOW):
+    """The second-stage scores of one row as exact rationals (same section,
+    second stage of hierarchical indexing, with the training-free score of
+    ``token_select``): candidates are the tokens of the listed ``pages`` that
+    lie outside the window of qb; score(j) = <sum of q over block qb, k_j>.
+
+    Returns (cands, exact, band) like ``page_scores_exact``.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    _, L, Hq, _ = q.shape
+    g = _kv_head(h, Hq, k.shape[2])
+    bs = win.block_size
+    inside = set(window_blocks(qb, win))
+    pages = sorted({int(c) for c in pages if c >= 0 and int(c) not in inside})
+    cands = [j for c in pages for j in range(c * bs, min((c + 1) * bs, L))]
+    qsum = _exact_block_sum(q[b, qb * bs:min((qb + 1) * bs, L), h])
+    af = np.asarray([float(x) for x in qsum])
+    exact = [sum((a * Fraction(float(x)) for a, x in zip(qsum, k[b, j, g])), Fraction(0)) for j in cands]
+    band = [1e-9 * float(np.abs(af) @ np.abs(k[b, j, g])) for j in cands]
+    return cands, exact, band
+
+
 def block_list_rows(q_rows, row0, k_seq, v_seq, scale, heads, Hq, lists, block: int = 128):
     """Attention of rows row0.. (one query block, one sequence) over explicit block
     lists: ``lists[n]`` is the list of readable block ids for query head heads[n];
