@@ -382,6 +382,8 @@ def page_select(q, k, win: Window = DEFAULT_WINDOW, top_m: int = 8, heads=None):
                 cands = list(range(c0, c1))
                 if len(cands) <= top_m:
                     chosen = cands
+                elif top_m == 0:
+                    chosen = []
                 else:
                     a = qs[b, qb, h]
                     kc = ks[b, c0:c1, g]

@@ -36,7 +36,7 @@ def judge_choice(chosen, cands, exact, band, m):
         return f"not candidates: {sorted(chosen - set(pos))[:5]}"
     if len(chosen) != min(m, len(cands)):
         return f"{len(chosen)} chosen, expected {min(m, len(cands))}"
-    if len(chosen) == len(cands):
+    if len(chosen) == len(cands) or not chosen:
         return None
     low = min(exact[pos[c]] + Fraction(band[pos[c]]) for c in chosen)
     high = max(exact[pos[d]] - Fraction(band[pos[d]]) for d in cands if d not in chosen)
