@@ -379,6 +379,23 @@ size_t ssa_page_select_workspace_size(const ssa_attn_args* a, const ssa_window* 
 int ssa_page_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_m, int32_t* idx,
                     int32_t* cnt, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ssa_page_select_noalloc -- ssa_page_select for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the fp64 block sums go to a fixed scratch array
+ * inside the library instead of a caller workspace.  Same arguments, lists
+ * and errors as ssa_page_select, minus the workspace; the kernels are the
+ * same.  Limit: ssa_page_select_workspace_size(a, win) must not exceed
+ * 32 MiB (33554432 bytes; e.g. B = 1, Hq = Hkv = 16, L = 131072, Dqk = 128),
+ * else SSA_ERR_WORKSPACE and nothing is launched.  The call allocates
+ * nothing: each GPU the library runs on holds one copy of the scratch from
+ * its first use until the process ends (SSA_ERR_DEVICE if its address cannot
+ * be looked up).  Every call on a GPU shares that copy, so calls that overlap
+ * on one GPU (other streams, other host threads) race and must be ordered by
+ * the caller; calls in one stream are ordered.  Nothing in the scratch needs
+ * to start at zero. */
+int ssa_page_select_noalloc(const ssa_attn_args* a, const ssa_window* win, int32_t top_m, int32_t* idx,
+                            int32_t* cnt, void* stream);
+
 /* ---------------------------------------------------------------------------
  * ssa_token_select -- the fine stage of hierarchical indexing (LongCat sparse
  * attention article, section 3: inside the top-M recalled pages every token

@@ -36,7 +36,7 @@ EXPORTS = (
     "ssa_block_index", "ssa_block_index_seq", "ssa_prefill", "ssa_prefill_tokens", "ssa_dense_causal",
     "ssa_prefill_chunk", "ssa_prefill_backward", "ssa_prefill_backward_workspace_size", "ssa_decode",
     "ssa_decode_dense", "ssa_decode_dense_workspace_size", "ssa_decode_workspace_size", "ssa_page_select",
-    "ssa_page_select_workspace_size", "ssa_token_select", "ssa_token_select_workspace_size", "ssa_last_error",
+    "ssa_page_select_workspace_size", "ssa_page_select_noalloc", "ssa_token_select", "ssa_token_select_workspace_size", "ssa_last_error",
     "ssa_version",
 )
 
@@ -189,6 +189,7 @@ def load(path: str = LIB_PATH):
     lib.ssa_page_select_workspace_size.restype = ctypes.c_size_t
     lib.ssa_page_select.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CWindow), i32, vp, vp, vp,
                                     ctypes.c_size_t, vp]
+    lib.ssa_page_select_noalloc.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CWindow), i32, vp, vp, vp]
     lib.ssa_last_error.restype = ctypes.c_char_p
     lib.ssa_last_error.argtypes = []
     lib.ssa_version.argtypes = []
@@ -549,6 +550,29 @@ def page_select(q, k, top_m: int = 8, window: Window = DEFAULT_WINDOW, workspace
     off = (-base) % 256
     _check(lib.ssa_page_select(ctypes.byref(a), ctypes.byref(w), top_m, _ptr(idx), _ptr(cnt),
                                base + off, workspace.numel() - off, _stream(stream)))
+    return idx, cnt
+
+
+@_on_stream
+def page_select_noalloc(q, k, top_m: int = 8, window: Window = DEFAULT_WINDOW, idx=None, cnt=None, stream=None):
+    """ssa_page_select_noalloc: page selection with the library's fixed scratch
+    (no workspace).  Pass preallocated ``idx`` [B, Hq, nqb, W] / ``cnt``
+    [B, Hq, nqb] (int32, contiguous) to allocate nothing here either."""
+    lib = load()
+    B, L, Hq, D = q.shape
+    nqb = (L + window.block_size - 1) // window.block_size
+    W = window.width + top_m
+    if idx is None:
+        idx = torch.empty((B, Hq, nqb, W), dtype=torch.int32, device=q.device)
+    if cnt is None:
+        cnt = torch.empty((B, Hq, nqb), dtype=torch.int32, device=q.device)
+    if tuple(idx.shape) != (B, Hq, nqb, W) or tuple(cnt.shape) != (B, Hq, nqb) or not (
+            idx.is_contiguous() and cnt.is_contiguous()):
+        raise SSAError(SSA_ERR_INVALID, "idx / cnt must be contiguous [B, Hq, nqb, W] / [B, Hq, nqb]")
+    a = _attn_args(q, k, k, q, None, 1.0)
+    w = window.c()
+    _check(lib.ssa_page_select_noalloc(ctypes.byref(a), ctypes.byref(w), top_m, _ptr(idx), _ptr(cnt),
+                                       _stream(stream)))
     return idx, cnt
 
 

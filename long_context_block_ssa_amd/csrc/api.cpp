@@ -542,9 +542,14 @@ size_t ssa_page_select_workspace_size(const ssa_attn_args* a, const ssa_window* 
          round256(sizeof(double) * a->B * a->Hkv * nqb * a->Dqk);
 }
 
-int ssa_page_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_m, int32_t* idx, int32_t* cnt,
-                    void* workspace, size_t workspace_bytes, void* stream) {
-  const char* who = "ssa_page_select";
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the page-selection entry points; fills everything of
+// `p` but the workspace pointers.
+int page_select_params(const ssa_attn_args* a, const ssa_window* win, int32_t top_m, int32_t* idx, int32_t* cnt,
+                       const char* who, ssa::PageSelectParams& p) {
   if (!a) return fail(SSA_ERR_INVALID, "%s: args is NULL", who);
   if (!valid_window(win, who, 64)) return SSA_ERR_INVALID;
   if (a->dtype != SSA_DTYPE_BF16) return fail(SSA_ERR_UNSUPPORTED, "%s: only BF16 q/k are supported", who);
@@ -561,12 +566,7 @@ int ssa_page_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_m
   if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(idx, 4) || !aligned(cnt, 4))
     return fail(SSA_ERR_INVALID, "%s: q/k must be 16-byte and idx/cnt 4-byte aligned", who);
   if (!valid_strides(a->q_stride, 2, who, "q") || !valid_strides(a->k_stride, 2, who, "k")) return SSA_ERR_INVALID;
-  const size_t need = ssa_page_select_workspace_size(a, win);
-  if (!workspace || workspace_bytes < need)
-    return fail(SSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
-                workspace ? workspace_bytes : static_cast<size_t>(0));
-  if (!aligned(workspace, 256)) return fail(SSA_ERR_INVALID, "%s: workspace must be 256-byte aligned", who);
-  ssa::PageSelectParams p{};
+  p = ssa::PageSelectParams{};
   p.q = a->q;
   p.k = a->k;
   p.qs_b = a->q_stride[0];
@@ -586,11 +586,49 @@ int ssa_page_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_m
   p.n_local = win->n_local;
   p.top_m = top_m;
   p.W = win->n_global + win->n_local + top_m;
-  const size_t qbytes = (sizeof(double) * a->B * a->Hq * p.nqb * a->Dqk + 255) / 256 * 256;
-  p.qsum = static_cast<double*>(workspace);
-  p.ksum = reinterpret_cast<double*>(static_cast<char*>(workspace) + qbytes);
   p.idx = idx;
   p.cnt = cnt;
+  return SSA_OK;
+}
+
+// the q sums, then the k sums, each from a 256-byte boundary
+void page_select_workspace(ssa::PageSelectParams& p, void* ws) {
+  const size_t qbytes = (sizeof(double) * p.B * p.Hq * p.nqb * p.D + 255) / 256 * 256;
+  p.qsum = static_cast<double*>(ws);
+  p.ksum = reinterpret_cast<double*>(static_cast<char*>(ws) + qbytes);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssa_page_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_m, int32_t* idx, int32_t* cnt,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "ssa_page_select";
+  ssa::PageSelectParams p;
+  if (const int rc = page_select_params(a, win, top_m, idx, cnt, who, p); rc != SSA_OK) return rc;
+  const size_t need = ssa_page_select_workspace_size(a, win);
+  if (!workspace || workspace_bytes < need)
+    return fail(SSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
+                workspace ? workspace_bytes : static_cast<size_t>(0));
+  if (!aligned(workspace, 256)) return fail(SSA_ERR_INVALID, "%s: workspace must be 256-byte aligned", who);
+  page_select_workspace(p, workspace);
+  return device_status(ssa::launch_page_select(p, as_stream(stream)), who);
+}
+
+int ssa_page_select_noalloc(const ssa_attn_args* a, const ssa_window* win, int32_t top_m, int32_t* idx,
+                            int32_t* cnt, void* stream) {
+  const char* who = "ssa_page_select_noalloc";
+  ssa::PageSelectParams p;
+  if (const int rc = page_select_params(a, win, top_m, idx, cnt, who, p); rc != SSA_OK) return rc;
+  const size_t need = ssa_page_select_workspace_size(a, win);
+  if (need > ssa::kPageScratchBytes)
+    return fail(SSA_ERR_WORKSPACE, "%s: these sizes need %zu bytes of scratch; the fixed scratch holds %zu", who,
+                need, ssa::kPageScratchBytes);
+  void* scratch = nullptr;
+  if (const hipError_t e = ssa::page_select_scratch(&scratch); e != hipSuccess)
+    return fail(SSA_ERR_DEVICE, "%s: the fixed scratch has no device address: %s", who, hipGetErrorString(e));
+  page_select_workspace(p, scratch);
   return device_status(ssa::launch_page_select(p, as_stream(stream)), who);
 }
 

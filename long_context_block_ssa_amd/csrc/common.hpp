@@ -231,4 +231,10 @@ size_t decode_mla_workspace_bytes(int32_t B, int32_t Hq, int32_t W);
 
 hipError_t launch_page_select(const PageSelectParams& p, hipStream_t stream);
 
+// The fixed device scratch of the allocation-free page selection (the fp64
+// block sums of q and k): its size, and its address on the current device
+// (looked up once per device).
+constexpr size_t kPageScratchBytes = size_t{32} << 20;
+hipError_t page_select_scratch(void** ptr);
+
 }  // namespace ssa

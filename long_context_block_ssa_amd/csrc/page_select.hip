@@ -294,6 +294,34 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(PageSelectParams p)
 
 }  // namespace
 
+// Scratch of the allocation-free entry point, for callers that cannot
+// allocate device memory (graph capture, serving loops): the fp64 block sums
+// of q and k, kPageScratchBytes at most.  Each GPU the library runs on holds
+// its own copy until the process ends.  Every call on a GPU shares it and it
+// keeps the last call's sums; nothing in it has to start at zero (the sums
+// kernel writes every value the select kernel reads), but calls that overlap
+// on one GPU race on it.  Host code uses the address looked up below, never
+// the array's name.
+static __device__ __align__(256) unsigned char scratch[kPageScratchBytes];
+
+hipError_t page_select_scratch(void** ptr) {
+  static std::once_flag once[kMaxDevices];
+  static void* addr[kMaxDevices];
+  static hipError_t status[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [&] {
+    void* a = nullptr;
+    status[dev] = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    addr[dev] = a;
+  });
+  if (status[dev] != hipSuccess) return status[dev];
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 hipError_t launch_page_select(const PageSelectParams& p, hipStream_t stream) {
   const int64_t nsum = static_cast<int64_t>(p.B) * (p.Hq + p.Hkv) * p.nqb;
   hipError_t e = p.D == 128 ? launch_kernel(block_sums_kernel<128>, dim3(static_cast<unsigned>(nsum)), dim3(kSumThreads), 0, stream, p)

@@ -341,6 +341,28 @@ def test_page_select_rejects(lib):
         == ssa.SSA_ERR_UNSUPPORTED
 
 
+def test_page_select_noalloc_rejects(lib):
+    """Sizes beyond the fixed 32 MiB scratch are refused before any device call;
+    the usual argument checks run first."""
+    w = ssa.CWindow(128, 1, 7)
+    # B=1, Hq=Hkv=16, L=131072, D=128: exactly 32 MiB of sums -- accepted by the size check
+    a = good_args(Hq=16, Hkv=16, L=131072)
+    assert lib.ssa_page_select_workspace_size(ctypes.byref(a), ctypes.byref(w)) == 32 << 20
+    # one more query block on top: refused
+    big = good_args(Hq=16, Hkv=16, L=131072 + 1)
+    assert lib.ssa_page_select_noalloc(ctypes.byref(big), ctypes.byref(w), 8, FAKE, FAKE, None) \
+        == ssa.SSA_ERR_WORKSPACE
+    assert "scratch" in lib.ssa_last_error().decode()
+    assert lib.ssa_page_select_noalloc(ctypes.byref(good_args()), ctypes.byref(w), 33, FAKE, FAKE, None) \
+        == ssa.SSA_ERR_INVALID
+    assert lib.ssa_page_select_noalloc(ctypes.byref(good_args()), ctypes.byref(w), 8, None, FAKE, None) \
+        == ssa.SSA_ERR_INVALID
+    assert lib.ssa_page_select_noalloc(None, ctypes.byref(w), 8, FAKE, FAKE, None) == ssa.SSA_ERR_INVALID
+    a2 = good_args(Dqk=576, Dv=512)
+    assert lib.ssa_page_select_noalloc(ctypes.byref(a2), ctypes.byref(w), 8, FAKE, FAKE, None) \
+        == ssa.SSA_ERR_UNSUPPORTED
+
+
 def tokens(**over):
     t = ssa.CTokenLists()
     t.tok, t.cnt, t.K, t.n_qblocks = FAKE, FAKE, 512, 2
