@@ -121,6 +121,46 @@ __device__ __forceinline__ void lds_read_vt16(const uint32_t (&a)[2][4], u32x2 (
       : "memory");
 }
 
+// the stage's 8 K fragments and its 16 transposed V reads (the two readers
+// above) in one batch with one wait: 24 reads in flight instead of 8, then 16
+template <int OFF>
+__device__ __forceinline__ void lds_read_kv(const uint32_t (&a)[8], const uint32_t (&b)[2][4], u32x4 (&o)[8],
+                                            u32x2 (&w)[16]) {
+  asm volatile(
+      "ds_read_b128 %0, %24 offset:%40\n"
+      "ds_read_b128 %1, %25 offset:%40\n"
+      "ds_read_b128 %2, %26 offset:%40\n"
+      "ds_read_b128 %3, %27 offset:%40\n"
+      "ds_read_b128 %4, %28 offset:%40\n"
+      "ds_read_b128 %5, %29 offset:%40\n"
+      "ds_read_b128 %6, %30 offset:%40\n"
+      "ds_read_b128 %7, %31 offset:%40\n"
+      "ds_read_b64_tr_b16 %8, %32 offset:%40\n"
+      "ds_read_b64_tr_b16 %9, %33 offset:%40\n"
+      "ds_read_b64_tr_b16 %10, %34 offset:%40\n"
+      "ds_read_b64_tr_b16 %11, %35 offset:%40\n"
+      "ds_read_b64_tr_b16 %12, %32 offset:%41\n"
+      "ds_read_b64_tr_b16 %13, %33 offset:%41\n"
+      "ds_read_b64_tr_b16 %14, %34 offset:%41\n"
+      "ds_read_b64_tr_b16 %15, %35 offset:%41\n"
+      "ds_read_b64_tr_b16 %16, %36 offset:%40\n"
+      "ds_read_b64_tr_b16 %17, %37 offset:%40\n"
+      "ds_read_b64_tr_b16 %18, %38 offset:%40\n"
+      "ds_read_b64_tr_b16 %19, %39 offset:%40\n"
+      "ds_read_b64_tr_b16 %20, %36 offset:%41\n"
+      "ds_read_b64_tr_b16 %21, %37 offset:%41\n"
+      "ds_read_b64_tr_b16 %22, %38 offset:%41\n"
+      "ds_read_b64_tr_b16 %23, %39 offset:%41\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]),
+        "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]), "=&v"(w[5]), "=&v"(w[6]), "=&v"(w[7]),
+        "=&v"(w[8]), "=&v"(w[9]), "=&v"(w[10]), "=&v"(w[11]), "=&v"(w[12]), "=&v"(w[13]), "=&v"(w[14]), "=&v"(w[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(b[0][0]),
+        "v"(b[0][1]), "v"(b[0][2]), "v"(b[0][3]), "v"(b[1][0]), "v"(b[1][1]), "v"(b[1][2]), "v"(b[1][3]), "i"(OFF),
+        "i"(OFF + 4096)
+      : "memory");
+}
+
 template <typename OutT>
 __device__ __forceinline__ void store4(OutT* dst, f32x4 v);
 template <>

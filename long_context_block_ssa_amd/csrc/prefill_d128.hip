@@ -12,9 +12,8 @@
 //     two workgroups per CU, so each SIMD interleaves two waves;
 //   - keys stream in 32-key stages through a 4-slot LDS ring filled with
 //     global_load_lds_dwordx4 (global -> LDS, no registers), 3 stages in
-//     flight, one barrier per stage; a stage's K fragments are read in one
-//     batch, and its V^T fragments in a second batch issued behind the score
-//     MFMAs, so the LDS latency is exposed twice per stage;
+//     flight, one barrier per stage; a stage's K fragments and V^T
+//     fragments are read from LDS in one batch with one wait;
 //   - S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16: each lane
 //     owns one query column of the 32 x 32 tile and 16 of its keys, so the
 //     row max needs one cross-lane swap (v_permlane32_swap) and the row sum
@@ -330,16 +329,15 @@ void prefill_d128_kernel(KernelParams<PAGED, TOKENS> p) {
     f32x16 sc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+    // K and V^T of the stage in one batch of LDS reads
+    u32x2 vraw[16];
     {
       u32x4 kraw[8];
-      lds_read_k8<OFF>(kaddr, kraw);
+      lds_read_kv<OFF>(kaddr, vaddr, kraw, vraw);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kraw[c]), qf[c], sc, 0, 0, 0);
     }
-    // V^T of the stage, read while the score MFMAs run
-    u32x2 vraw[16];
-    lds_read_vt16<OFF>(vaddr, vraw);
     // token stage: entries at or past the count
     if (tst) {
       const int lim = ntok - 1 - (s - nbs) * kSK - 4 * h32;  // last valid entry offset
