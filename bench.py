@@ -7,6 +7,7 @@ One step = one pass over every row of the path on resident synthetic inputs:
   a2  SSA prefill            B=1, H=16, d=128, L=32768, bf16, layout [B, H, L, D]
                              (and the small fp32 case B=1, H=1, d=64, L=2048, timed too)
   a3  SSA decode             batch 64, H=16/16, d=128, context ~ U[65536, 131072]
+                             (and grouped heads: the same batch with 16 query heads on 2 kv heads)
   a4  latent-shared shape    prefill B=1, L=262144, 128 heads x 576/512 (V = first 512
                              channels of the shared latent); decode batch 8 at 1,048,576
   a5  dense causal layer     same tensors as a2 (the comparison layer)
@@ -56,7 +57,7 @@ PEAK_FP64_TFLOPS = 78.6
 
 W1 = dict(B=1, L=2048, H=1, D=64, seed=1)
 W2 = dict(B=1, L=32768, H=16, D=128, seed=2)
-W3 = dict(B=64, H=16, D=128, lo=65536, hi=131072, seed=3)
+W3 = dict(B=64, H=16, D=128, lo=65536, hi=131072, seed=3, Hkv_gqa=2)
 W5 = dict(B=1, L=131072, H=16, D=128, M=8, K=512, seed=5)
 W4 = dict(L=262144, H=128, DQK=576, DV=512, seed=4, dec_B=8, dec_n=1048576, dec_rot=32)
 W6 = dict(B=16, T=2048, H=16, D=128, lo=65536, hi=131072, seed=6)
@@ -247,6 +248,7 @@ def cpu_rows_baseline():
     f64 = lambda bits: synth.bf16_bits_to_f32(bits).astype(np.float64)
     # a3 decode: 4 of the 64 sequences
     B3, H3, D3, s3 = W3["B"], W3["H"], W3["D"], W3["seed"]
+    Hkv3g = W3["Hkv_gqa"]
     nd = 16
     lens = synth.decode_seq_lens(s3, B3, W3["lo"], W3["hi"])[:nd]
     fill = synth.decode_fill_blocks(lens, 128, 1, 7)
@@ -346,6 +348,7 @@ KERNEL_SOURCES = {  # row key -> (kernel-name fragments in the trace, source fil
     "ssa_decode": (("decode_mha_kernel", "128"), "decode.hip"),
     "mla_prefill": (("prefill_wide_kernel", "576"), "prefill_wide.hip"),
     "mla_decode": (("decode_mla_partial_kernel", "true"), "decode_mla.hip"),
+    "ssa_decode_gqa": (("decode_gqa_kernel",), "decode_gqa.hip"),
 }
 
 
@@ -646,6 +649,7 @@ def main():
         lists1 = ssa.lists_from_index(*win1)
     # a3 inputs: one paged pool, several independent (q, table) sets
     B3, H3, D3, s3 = W3["B"], W3["H"], W3["D"], W3["seed"]
+    Hkv3g = W3["Hkv_gqa"]
     lens = synth.decode_seq_lens(s3, B3, W3["lo"], W3["hi"])
     if run["decode"]:
         tables = []
@@ -671,6 +675,9 @@ def main():
         bts = [torch.from_numpy(bt).to(dev) for bt in tables]
         sl3 = torch.from_numpy(lens).to(dev)
         o3 = torch.empty((B3, H3, D3), dtype=torch.bfloat16, device=dev)
+        # grouped heads: the same 16 query heads on the first Hkv3g kv heads of the pool
+        kp3g, vp3g = kp[:, :Hkv3g], vp[:, :Hkv3g]
+        o3g = torch.empty((B3, H3, D3), dtype=torch.bfloat16, device=dev)
     # a6-a8 inputs
     if run["page"]:
         L5, H5, D5, M5, s5 = W5["L"], W5["H"], W5["D"], W5["M"], W5["seed"]
@@ -743,7 +750,7 @@ def main():
 
     rows = ["a1 block_index", "a2 ssa_prefill", "a3 ssa_decode", "a5 dense_causal", "a6-a7 page_select",
             "a8 page_prefill", "a4 mla_prefill", "a4 mla_decode", "f1 chunk_prefill", "f3 ssa_backward",
-            "f2 token_select", "f2 hi_prefill", "a2 ssa_prefill_f32"]
+            "f2 token_select", "f2 hi_prefill", "a2 ssa_prefill_f32", "a3 ssa_decode_gqa"]
     nev = len(rows) + 1
 
     if run["copy"]:
@@ -797,6 +804,9 @@ def main():
         if run["prefill"]:
             ssa.prefill(q1, k1, v1, lists1, out=o1)
         mark(13)
+        if run["decode"]:
+            ssa.decode(q3[r], kp3g, vp3g, bts[r], sl3, out=o3g)
+        mark(14)
         if run["copy"]:
             cp_dst.copy_(cp_src)
 
@@ -819,7 +829,7 @@ def main():
 
     if only:
         return
-    for t, name in ((o1, "ssa f32"), (o2, "ssa"), (o3, "decode"), (od, "dense"), (o5, "page"), (o4[0, -128:], "mla"),
+    for t, name in ((o1, "ssa f32"), (o2, "ssa"), (o3, "decode"), (o3g, "decode gqa"), (od, "dense"), (o5, "page"), (o4[0, -128:], "mla"),
                     (o4d, "mla decode"), (o6, "chunk"), (dqb, "dq"), (dkb, "dk"), (dvb, "dv"), (o5h, "hi")):
         if not torch.isfinite(t.float()).all():
             raise RuntimeError(f"non-finite {name} output")
@@ -832,6 +842,9 @@ def main():
     b3 = decode_bytes(lens, H3, H3, D3, D3)
     t3 = per_row[2] * 1e-3
     gb3 = b3 / t3 / 1e9
+    b3g = decode_bytes(lens, H3, Hkv3g, D3, D3)
+    t3g = per_row[13] * 1e-3
+    gb3g = b3g / t3g / 1e9
     fd = dense_flops(L2, H2, D2)
     f5 = page_flops(L5, H5, D5, M5)
     b5 = 2 * L5 * H5 * D5 * 2
@@ -842,6 +855,9 @@ def main():
         "ssa_decode": {"bound": "hbm", "achieved": gb3, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                        "frac": gb3 / PEAK_HBM_GBS, "traffic": traffic_for("ssa_decode"),
                        "us": per_row[2] * 1e3, "work": b3},
+        "ssa_decode_gqa": {"bound": "hbm", "achieved": gb3g, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": gb3g / PEAK_HBM_GBS, "traffic": traffic_for("ssa_decode_gqa"),
+                           "us": per_row[13] * 1e3, "work": b3g, "heads": f"{H3}/{Hkv3g}"},
         "dense_causal": {"bound": "mfma", "achieved": fd / (per_row[3] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": fd / (per_row[3] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                          "us": per_row[3] * 1e3, "work": fd},
@@ -912,6 +928,8 @@ def main():
             "decode_gbps": gb3,
             "decode_frac_hbm": gb3 / PEAK_HBM_GBS,
             "decode_tokens_per_s": B3 / t3,
+            "decode_gqa_gbps": gb3g,
+            "decode_gqa_frac_hbm": gb3g / PEAK_HBM_GBS,
             "page_select_index_share": per_row[4] / (per_row[4] + per_row[5]),
             "hi_index_share": (per_row[4] + per_row[10]) / (per_row[4] + per_row[10] + per_row[11]),
         },

@@ -136,10 +136,12 @@ typedef struct ssa_token_lists {
  * Hq/Hkv <= 16 and a page's rows within 2^31 bytes of the page base
  * (2 * (127 * slot stride + D) <= 2^31 - 1, else SSA_ERR_UNSUPPORTED), and
  * (BF16, 576, 512) with Hkv == 1 and Hq a multiple of 16.
- * The (576, 512) shape splits every window over its blocks and keeps fp32
- * per-block partials in a caller-owned device workspace of at least
- * ssa_decode_workspace_size bytes, 256-byte aligned (SSA_ERR_WORKSPACE if it
- * is missing or short); the other shapes ignore both fields. */
+ * The (576, 512) shape splits every window over its blocks, and (128, 128)
+ * with 2 <= Hq/Hkv <= 16 and a window wider than 4 blocks splits it over
+ * groups of 4 blocks; both keep fp32 partials in a caller-owned device
+ * workspace of at least ssa_decode_workspace_size bytes, 256-byte aligned
+ * (SSA_ERR_WORKSPACE if it is missing or short); the other shapes ignore both
+ * fields. */
 typedef struct ssa_decode_args {
   int32_t dtype; /* of q, k_pages, v_pages and o: BF16 */
   int32_t B, Hq, Hkv, Dqk, Dv;
@@ -227,10 +229,11 @@ int ssa_dense_causal(const ssa_attn_args* a, void* stream);
  * ------------------------------------------------------------------------- */
 int ssa_decode(const ssa_decode_args* a, const ssa_window* win, void* stream);
 
-/* Bytes of workspace ssa_decode needs for these sizes and window: 0 for the
- * 64- and 128-wide heads, B * Hq * (n_global + n_local) * 2064 rounded up to
- * a multiple of 256 for Dqk = 576, Dv = 512.  Reads only B, Hq, Dqk, Dv and
- * the window; 0 for NULL arguments. */
+/* Bytes of workspace ssa_decode needs for these sizes and window, rounded up
+ * to a multiple of 256: B * Hq * (n_global + n_local) * 2064 for Dqk = 576,
+ * Dv = 512; B * Hq * ceil((n_global + n_local) / 4) * 520 for Dqk = Dv = 128
+ * with 2 <= Hq/Hkv <= 16 and n_global + n_local > 4; otherwise 0.  Reads only
+ * B, Hq, Hkv, Dqk, Dv and the window; 0 for NULL arguments. */
 size_t ssa_decode_workspace_size(const ssa_decode_args* a, const ssa_window* win);
 
 /* ---------------------------------------------------------------------------

@@ -440,10 +440,12 @@ def prefill_backward(q, k, v, o, dout, lse, scale=None, window: Window = DEFAULT
     return dq, dk, dv
 
 
-def decode_workspace_size(B: int, Hq: int, Dqk: int, Dv: int, window: Window = DEFAULT_WINDOW) -> int:
-    """ssa_decode_workspace_size: bytes of device workspace ssa_decode needs (0 for most shapes)."""
+def decode_workspace_size(B: int, Hq: int, Dqk: int, Dv: int, window: Window = DEFAULT_WINDOW,
+                          Hkv: int | None = None) -> int:
+    """ssa_decode_workspace_size: bytes of device workspace ssa_decode needs (0 for most shapes);
+    ``Hkv`` defaults to Hq (one query head per kv head)."""
     a = CDecodeArgs()
-    a.B, a.Hq, a.Dqk, a.Dv = B, Hq, Dqk, Dv
+    a.B, a.Hq, a.Hkv, a.Dqk, a.Dv = B, Hq, Hq if Hkv is None else Hkv, Dqk, Dv
     w = window.c()
     return int(load().ssa_decode_workspace_size(ctypes.byref(a), ctypes.byref(w)))
 

@@ -218,6 +218,15 @@ size_t prefill_backward_workspace_bytes(int32_t B, int32_t L, int32_t Hq, int32_
                                         int32_t n_local);
 
 hipError_t launch_decode(const DecodeParams& p, int dqk, int dv, hipStream_t stream);
+// d = 128 with 2..16 query heads per kv head: each K/V row read once for
+// all heads of its kv head.  A window of more than 4 blocks is split over
+// workgroups whose pieces go through p.work (decode_gqa_workspace_bytes) and
+// the dense decode's merge kernel.
+bool decode_gqa_supports(const DecodeParams& p, int dqk, int dv);
+size_t decode_gqa_workspace_bytes(int32_t B, int32_t Hq, int32_t width);
+hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream);
+// merge p.nsplit pieces (o relative to m, m, l) per (sequence, head) of p.work
+hipError_t launch_decode_merge(const DecodeParams& p, int d, hipStream_t stream);
 
 // Dense decode (every cached key), MHA/GQA d = 64/128: nsplit groups of 16
 // blocks per (sequence, kv head), partials in p.work, then a merge

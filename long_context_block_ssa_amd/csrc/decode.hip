@@ -271,8 +271,8 @@ __global__ __launch_bounds__(MAXT) __attribute__((amdgpu_waves_per_eu(4))) void 
   }
 }
 
-// Dense decode merge: one wave per (sequence, query head) combines the
-// groups' pieces, M = max m_s, o = sum o_s e^(m_s - M) / sum l_s e^(m_s - M)
+// Decode merge (the dense decode's block groups, the grouped-head decode's
+// window splits): one wave per (sequence, query head) combines the pieces, M = max m_s, o = sum o_s e^(m_s - M) / sum l_s e^(m_s - M)
 // (the exact merge of max-subtracted softmax pieces, CSA/HCA tutorial page,
 // section 7.1); a NaN l in any group makes the row NaN.
 template <int D>
@@ -314,6 +314,13 @@ size_t decode_dense_workspace_bytes(int32_t B, int32_t Hq, int32_t max_blocks, i
   return static_cast<size_t>(static_cast<int64_t>(B) * Hq * nsplit * (d + 2) * sizeof(float));
 }
 
+hipError_t launch_decode_merge(const DecodeParams& p, int d, hipStream_t stream) {
+  const dim3 mgrid(static_cast<unsigned>(p.B) * p.Hq);
+  return d == 128 ? launch_kernel(decode_dense_merge_kernel<128>, mgrid, dim3(64), 0, stream, p)
+       : d == 64  ? launch_kernel(decode_dense_merge_kernel<64>, mgrid, dim3(64), 0, stream, p)
+                  : hipErrorNotSupported;
+}
+
 hipError_t launch_decode_dense(const DecodeParams& p, int d, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.nsplit) * p.B * p.Hkv);
   const dim3 block(64 * kDenseGroup);
@@ -321,13 +328,12 @@ hipError_t launch_decode_dense(const DecodeParams& p, int d, hipStream_t stream)
                : d == 64  ? launch_kernel(decode_mha_kernel<64, 1024, true>, grid, block, 0, stream, p)
                           : hipErrorNotSupported;
   if (e != hipSuccess) return e;
-  const dim3 mgrid(static_cast<unsigned>(p.B) * p.Hq);
-  return d == 128 ? launch_kernel(decode_dense_merge_kernel<128>, mgrid, dim3(64), 0, stream, p)
-                  : launch_kernel(decode_dense_merge_kernel<64>, mgrid, dim3(64), 0, stream, p);
+  return launch_decode_merge(p, d, stream);
 }
 
 hipError_t launch_decode(const DecodeParams& p, int dqk, int dv, hipStream_t stream) {
   if (dqk == 576 && dv == 512) return launch_decode_mla(p, stream);
+  if (decode_gqa_supports(p, dqk, dv)) return launch_decode_gqa(p, stream);
   const int width = p.n_global + p.n_local;  // validated <= 16
   const dim3 grid(static_cast<unsigned>(p.B) * p.Hkv);
   const dim3 block(64 * width);

@@ -308,6 +308,23 @@ def test_decode_workspace_size(lib):
     assert ssa.decode_workspace_size(3, 32, 576, 512) == (3 * 32 * 8 * 516 * 4 + 255) // 256 * 256
 
 
+def test_decode_gqa_workspace(lib):
+    """Grouped heads at d = 128: a window wider than 4 blocks is split over
+    groups of 4, with fp32 (128 channels, m, l) per (sequence, head, group)."""
+    w = ssa.CWindow(128, 1, 7)
+    a = decode_args(Hq=16, Hkv=2)
+    need = lib.ssa_decode_workspace_size(ctypes.byref(a), ctypes.byref(w))
+    assert need == (2 * 16 * 2 * 130 * 4 + 255) // 256 * 256
+    assert lib.ssa_decode_workspace_size(ctypes.byref(a), ctypes.byref(ssa.CWindow(128, 1, 3))) == 0
+    assert lib.ssa_decode_workspace_size(ctypes.byref(a), ctypes.byref(ssa.CWindow(128, 2, 10))) == \
+        (2 * 16 * 3 * 130 * 4 + 255) // 256 * 256
+    assert ssa.decode_workspace_size(2, 16, 128, 128, Hkv=2) == need
+    assert ssa.decode_workspace_size(2, 16, 128, 128) == 0
+    assert lib.ssa_decode(ctypes.byref(a), ctypes.byref(w), None) == ssa.SSA_ERR_WORKSPACE
+    a = decode_args(Hq=16, Hkv=2, workspace=FAKE + 16, workspace_bytes=need)
+    assert lib.ssa_decode(ctypes.byref(a), ctypes.byref(w), None) == ssa.SSA_ERR_INVALID
+
+
 def test_decode_mla_workspace_rules(lib):
     w = ssa.CWindow(128, 1, 7)
     a = mla_decode_args()

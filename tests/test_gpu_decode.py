@@ -71,7 +71,8 @@ def run_and_check(lib, dev, host, scale, name, rel=False, v_view=None):
     return o
 
 
-@pytest.mark.parametrize("D,Hq,Hkv", [(128, 4, 2), (128, 2, 2), (64, 3, 1), (128, 16, 1)])
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 4, 2), (128, 2, 2), (64, 3, 1), (128, 16, 1), (128, 8, 1), (128, 6, 2),
+                                     (128, 15, 3), (128, 16, 2)])
 def test_decode_small_nan_poisoned(lib, D, Hq, Hkv):
     lens = [1, 2, 127, 128, 129, 1000, 1024, 1025, 5000, 7777]
     dev, host = build_case(21, len(lens), Hq, Hkv, D, lens)
@@ -79,10 +80,12 @@ def test_decode_small_nan_poisoned(lib, D, Hq, Hkv):
 
 
 @pytest.mark.parametrize("win,D,Hq,Hkv", [((128, 2, 3), 128, 4, 2), ((128, 1, 15), 128, 2, 2),
-                                         ((128, 0, 6), 64, 3, 1), ((128, 4, 12), 64, 2, 1)])
+                                         ((128, 0, 6), 64, 3, 1), ((128, 4, 12), 64, 2, 1),
+                                         ((128, 0, 8), 128, 8, 2), ((128, 2, 10), 128, 8, 2)])
 def test_decode_other_windows(lib, win, D, Hq, Hkv):
     """Other window geometries; a 16-block window runs the 1024-thread
-    instantiation (one wave per block)."""
+    instantiation (one wave per block); grouped heads split a window of more
+    than 4 blocks over groups of 4 (12 blocks: 3 groups)."""
     lens = [1, 130, 700, 2048, 2049, 3001]
     w = oracle.Window(*win)
     dev, host = build_case(23, len(lens), Hq, Hkv, D, lens, head=win[1], tail=win[2])
@@ -99,6 +102,14 @@ def test_decode_cfg3_full(lib):
     lens = synth.decode_seq_lens(3, 64, 65536, 131072)
     dev, host = build_case(3, 64, 16, 16, 128, lens)
     run_and_check(lib, dev, host, 1 / math.sqrt(128), "cfg3 full")
+
+
+def test_decode_gqa_cfg3_full(lib):
+    """Grouped heads at the decode workload's contexts: batch 64, 16 query heads
+    on 2 kv heads (8 per kv head), d = 128, lengths uniform in [65536, 131072]."""
+    lens = synth.decode_seq_lens(3, 64, 65536, 131072)
+    dev, host = build_case(5, 64, 16, 2, 128, lens)
+    run_and_check(lib, dev, host, 1 / math.sqrt(128), "gqa 16/2 full")
 
 
 def test_decode_equals_prefill_last_row(lib):
