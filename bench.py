@@ -419,6 +419,98 @@ def write_traffic(fetch_dir: str, write_dir: str, out_path: str):
     print("\n".join(lines))
 
 
+# counter groups for the per-kernel summaries: each fits one rocprofv3 pass
+# (at most 8 SQ, 2 TA, 2 TD counters)
+COUNTER_GROUPS = [
+    "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT "
+    "SQ_LDS_IDX_ACTIVE",
+    "SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_MISC SQ_INST_CYCLES_VMEM "
+    "SQ_ACTIVE_INST_LDS SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_ANY",
+    "SQ_WAIT_ANY SQ_ACTIVE_INST_VMEM SQ_INST_CYCLES_VMEM_RD SQ_ACTIVE_INST_SCA SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_SALU "
+    "SQ_INSTS_VMEM_RD SQ_ACTIVE_INST_FLAT TA_TA_BUSY_sum TA_ADDR_STALLED_BY_TC_CYCLES_sum",
+    "TD_TD_BUSY_sum TD_TC_STALL_sum TA_DATA_STALLED_BY_TC_CYCLES_sum TA_ADDR_STALLED_BY_TD_CYCLES_sum SQ_BUSY_CYCLES",
+]
+
+
+def write_counters(root: str, frags: str, out_path: str, title: str, command: str):
+    """Per-kernel summary of the COUNTER_GROUPS passes under ROOT (one
+    sub-directory per pass, each a rocprofv3 --pmc --kernel-trace run): the
+    counters averaged per dispatch of the kernels whose name holds every
+    comma-separated fragment of FRAGS (a fragment 'grid=N' matches the grid
+    size in threads instead), and the derived figures of the MI355X's 8 XCDs x
+    4 shader engines, 256 CUs and 1024 SIMDs."""
+    import csv
+    import glob
+
+    want = [f for f in frags.split(",") if f]
+
+    def match(name, grid):
+        for f in want:
+            if f.startswith("grid="):
+                if str(grid) != f[5:]:
+                    return False
+            elif f not in name:
+                return False
+        return True
+
+    vals, durs = {}, []
+    for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        per = {}
+        for r in csv.DictReader(open(f)):
+            grid = r.get("Grid_Size", r.get("Grid_Size_X", ""))
+            if not match(r["Kernel_Name"], grid):
+                continue
+            per.setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+            per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        for c, d in per.items():
+            vals[c] = sum(d.values()) / len(d)
+    for f in glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if match(r["Kernel_Name"], r.get("Grid_Size_X", "")):
+                durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    if not vals:
+        raise RuntimeError(f"no counters for kernel fragments {frags} under {root}")
+    dur = sorted(durs)[len(durs) // 2] if durs else float("nan")
+    v = vals.get
+    lines = [f"# {title}", f"# {command}",
+             f"# kernel duration under the counters (median over {len(durs)} dispatches): {dur * 1e6:.1f} us",
+             f"{'counter':40s} {'per_dispatch':>14s}"]
+    lines += [f"{k:40s} {x:14.4g}" for k, x in sorted(vals.items())]
+    lines.append("")
+    lines.append("derived (MI355X: 8 XCDs x 4 shader engines, 256 CUs, 1024 SIMDs)")
+    busy = v("SQ_BUSY_CYCLES")
+    if busy and dur == dur:
+        clk = busy / 32 / dur
+        cyc = dur * clk
+        lines.append(f"shader clock       SQ_BUSY_CYCLES / 32 SEs / duration               {clk / 1e9:.2f} GHz")
+        if v("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
+            lines.append(f"MFMA utilisation   SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles)  "
+                         f"{100 * v('SQ_VALU_MFMA_BUSY_CYCLES') / (1024 * cyc):.1f} %")
+        for ctr, name in (("TA_TA_BUSY_sum", "TA busy"), ("TD_TD_BUSY_sum", "TD busy")):
+            if v(ctr) is not None:
+                lines.append(f"{name:18s} {ctr} / (256 CUs x cycles)               {100 * v(ctr) / (256 * cyc):.1f} %")
+        if v("TD_TD_BUSY_sum") and v("TD_TC_STALL_sum") is not None:
+            lines.append(f"TD stalled on TC   TD_TC_STALL_sum / TD_TD_BUSY_sum                    "
+                         f"{100 * v('TD_TC_STALL_sum') / v('TD_TD_BUSY_sum'):.1f} %")
+    waves = v("SQ_WAVES")
+    if waves:
+        parts = [f"{v(c) / waves:.0f} {n}" for c, n in (("SQ_INSTS_MFMA", "MFMA"), ("SQ_INSTS_VALU", "VALU (MFMA included)"),
+                                                        ("SQ_INSTS_VALU_TRANS_F32", "trans"), ("SQ_INSTS_SALU", "SALU"),
+                                                        ("SQ_INSTS_LDS", "LDS"), ("SQ_INSTS_VMEM_RD", "VMEM reads"))
+                 if v(c) is not None]
+        lines.append("per wave           " + ", ".join(parts))
+    wc = v("SQ_WAVE_CYCLES")
+    if wc and v("SQ_ACTIVE_INST_ANY") is not None and v("SQ_WAIT_INST_ANY") is not None and v("SQ_WAIT_ANY") is not None:
+        lines.append(f"wave time          issuing {100 * v('SQ_ACTIVE_INST_ANY') / wc:.0f} %, blocked on issue "
+                     f"{100 * v('SQ_WAIT_INST_ANY') / wc:.0f} %, waiting (waitcnt/barrier) {100 * v('SQ_WAIT_ANY') / wc:.0f} %"
+                     " of SQ_WAVE_CYCLES")
+    if v("SQ_LDS_BANK_CONFLICT") is not None and v("SQ_LDS_IDX_ACTIVE"):
+        lines.append(f"LDS bank conflicts SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE          "
+                     f"{100 * v('SQ_LDS_BANK_CONFLICT') / v('SQ_LDS_IDX_ACTIVE'):.1f} %")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def short_kernel_name(name: str) -> str:
     """'void ssa::(anonymous namespace)::k<128, 128, false, 2, __bf16>(ssa::P)' -> 'k<128, 128, false, 2, __bf16>'."""
     # the profiler's own demangler prints the leading template arguments <__bf16, true, ...> of the
@@ -585,12 +677,21 @@ def main():
                     "for profiling one kernel -- the JSON line is printed only for a full run")
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="summarise two rocprofv3 --pmc runs into a traffic file and exit")
+    ap.add_argument("--write-counters", nargs=5, metavar=("PMC_ROOT", "KERNEL_FRAGMENTS", "OUT", "TITLE", "COMMAND"),
+                    help="summarise the COUNTER_GROUPS rocprofv3 passes for one kernel into a text file and exit")
+    ap.add_argument("--counter-groups", action="store_true", help="print the counter groups, one per line, and exit")
     ap.add_argument("--zigzag", action="store_true", help="f4: dense/SSA layer-stack prefill timing and exit")
     ap.add_argument("--trace-summary", nargs=3, metavar=("KERNEL_STATS_CSV", "OUT", "COMMAND"),
                     help="summarise a rocprofv3 --kernel-trace --stats run into a short text file and exit")
     args = ap.parse_args()
     if args.trace_summary:
         write_trace_summary(*args.trace_summary)
+        return
+    if args.counter_groups:
+        print("\n".join(COUNTER_GROUPS))
+        return
+    if args.write_counters:
+        write_counters(*args.write_counters)
         return
     if args.write_traffic:
         write_traffic(*args.write_traffic)

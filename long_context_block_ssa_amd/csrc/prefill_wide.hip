@@ -13,8 +13,10 @@
 // 8 waves), two waves per SIMD.  Keys stream in 64-key stages through two
 // LDS slots:
 //   - staging uses global_load_lds_dwordx4 (global -> LDS, no registers);
-//     rows are padded by one 16-byte unit so that the 16 lanes reading a
-//     fragment column hit 16 distinct bank groups;
+//     d = 64 rows are padded by one 16-byte unit so that the 16 lanes
+//     reading a fragment column hit 16 distinct bank groups; the 576-wide
+//     latent rows are XOR-swizzled instead (see wswz), which also keeps the
+//     transposed V reads free of bank conflicts;
 //   - S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K rows, ds_read_b128;
 //     B = Q^T held in registers), so each lane owns one query column;
 //   - O^T = V^T P^T: P^T comes from the S^T accumulators converted to bf16;
@@ -63,10 +65,22 @@ __device__ __forceinline__ void store4<__bf16>(__bf16* dst, f32x4 v) {
   *reinterpret_cast<bf16x4*>(dst) = __builtin_convertvector(v, bf16x4);
 }
 
+// Row layout of the 576-wide latent slab: rows 76 units (1216 bytes) apart,
+// so that rows r, r+1, r+2, r+3 start 48 banks apart modulo the 64 banks, and
+// unit u of row r at u ^ f(r) with f(r) = 2 ((r >> 2) mod 2) + (r >> 3) mod 2
+// (an XOR of the unit's two low bits only, so the fragment offsets stay
+// immediates).  The fragment reads (16 rows, one unit: 4 row bases x 4 values
+// of f) and the transposed reads (per 32 lanes 8 rows x 2 units x 2 halves)
+// then each cover the 64 banks once; a one-unit pad per row (73 units) left
+// half of the LDS cycles in bank conflicts.
+constexpr int kWidePitch576 = 76;
+__device__ __forceinline__ int wswz(int row) { return (((row >> 2) & 1) << 1) | ((row >> 3) & 1); }
+
 // LDS geometry of one stage slot, in 16-byte units.
 template <int DQK, int DV, bool SHARED>
 struct WideGeom {
-  static constexpr int UK = DQK / 8 + 1;  // K row pitch (one pad unit)
+  static constexpr bool KSW = DQK == 576;  // K slab swizzled instead of padded by one unit
+  static constexpr int UK = KSW ? kWidePitch576 : DQK / 8 + 1;  // K row pitch
   static constexpr int UV = DV / 8 + 1;   // V row pitch when V is staged apart
   static constexpr int KUNITS = kStageKeys * UK;
   static constexpr int VUNITS = SHARED ? 0 : kStageKeys * UV;
@@ -83,17 +97,22 @@ struct WideGeom {
 // is recomputed per stage (the 512-wide accumulator leaves no registers).  A
 // lane on a row's pad unit loads unit 0 of its row.  Keys at or past L are
 // clamped to row L-1 (finite data, masked later).
-template <int D, int U, int NW, bool CACHE>
+template <int D, int U, int NW, bool CACHE, bool SW = false>
 struct Stager {
   static constexpr int TOTAL = kStageKeys * U / 64;  // wave-instructions per slab
   static constexpr int PER = (TOTAL + NW - 1) / NW;  // per wave
   int32_t off[CACHE ? PER : 1];
 
+  // SW: the lane at unit position pos of a row loads logical unit pos ^ f(row)
+  // (f flips the two low bits only, so pos < D/8 stays below D/8)
   __device__ __forceinline__ static void place(int i, int lane, int& row, int& unit) {
     const int pidx = i * 64 + lane;
     row = pidx / U;
     const int pos = pidx - row * U;
-    unit = pos < D / 8 ? pos : 0;
+    if constexpr (SW)
+      unit = pos < D / 8 ? pos ^ wswz(row) : 0;
+    else
+      unit = pos < D / 8 ? pos : 0;
   }
   __device__ __forceinline__ void init(int64_t stride_l, int wave, int lane) {
     if constexpr (CACHE) {
@@ -209,7 +228,7 @@ void prefill_wide_kernel(PrefillParams p) {
     for (int n = 0; n < kNQ; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int NS = G::NSLOTS;
-  Stager<DQK, G::UK, kWWaves, (kNQ >= 2)> kst;
+  Stager<DQK, G::UK, kWWaves, (kNQ >= 2), G::KSW> kst;
   kst.init(p.ks_l, wave, lane);
   Stager<DV, G::UV, kWWaves, (kNQ >= 2)> vst;
   if constexpr (!SHARED) vst.init(p.vs_l, wave, lane);
@@ -231,6 +250,10 @@ void prefill_wide_kernel(PrefillParams p) {
     const SSA_LDS u32x4* kslab = (const SSA_LDS u32x4*)(cur);
     const SSA_LDS u32x4* vslab = SHARED ? kslab : kslab + G::KUNITS;
     constexpr int UV = SHARED ? G::UK : G::UV;
+    constexpr bool VSW = SHARED && G::KSW;  // V read from the swizzled latent slab
+    // the lane's unit within each 4-unit group of a K fragment read (rows
+    // t*16 + r share f(r))
+    const int kg = G::KSW ? g ^ wswz(r) : g;
     f32x4 sc[4][kNQ];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -244,7 +267,7 @@ void prefill_wide_kernel(PrefillParams p) {
       auto load_k = [&](int c) {
   #pragma unroll
         for (int t = 0; t < 4; ++t)
-          kf[c % (KD + 1)][t] = __builtin_bit_cast(bf16x8, kslab[(t * 16 + r) * G::UK + c * 4 + g]);
+          kf[c % (KD + 1)][t] = __builtin_bit_cast(bf16x8, kslab[(t * 16 + r) * G::UK + c * 4 + kg]);
       };
   #pragma unroll
       for (int c = 0; c < KD && c < NC; ++c) load_k(c);
@@ -271,7 +294,7 @@ void prefill_wide_kernel(PrefillParams p) {
       for (int c = 0; c < NC; ++c) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const bf16x8 kf1 = __builtin_bit_cast(bf16x8, kslab[(t * 16 + r) * G::UK + c * 4 + g]);
+          const bf16x8 kf1 = __builtin_bit_cast(bf16x8, kslab[(t * 16 + r) * G::UK + c * 4 + kg]);
 #pragma unroll
           for (int n = 0; n < kNQ; ++n)
             sc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf1, qf[n][c], sc[t][n], 0, 0, 0);
@@ -337,7 +360,8 @@ void prefill_wide_kernel(PrefillParams p) {
         const int c = st / NJ, jt = st % NJ;
         const int krow = c * 32 + 4 * g + (r >> 2);
         const int ch = jt * 16 + 4 * (r & 3);
-        const SSA_LDS char* base0 = (const SSA_LDS char*)(vslab + krow * UV + (ch >> 3)) + (ch & 7) * 2;
+        const int vu = VSW ? 4 * (jt >> 1) + ((2 * (jt & 1) + ((r & 3) >> 1)) ^ wswz(krow)) : (ch >> 3);
+        const SSA_LDS char* base0 = (const SSA_LDS char*)(vslab + krow * UV + vu) + (ch & 7) * 2;
         const SSA_LDS char* base1 = base0 + 16 * UV * 16;
         const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSA_LDS bf16x4*)base0);
         const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSA_LDS bf16x4*)base1);
@@ -384,8 +408,11 @@ void prefill_wide_kernel(PrefillParams p) {
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt) {
           const int ch = jt * 16 + ch_off;
-          const SSA_LDS char* base0 = (const SSA_LDS char*)(vslab + krow * UV + (ch >> 3)) + (ch & 7) * 2;
-          const SSA_LDS char* base1 = base0 + 16 * UV * 16;
+          // unit 2jt + (r mod 4)/2 of row krow, its two low bits XOR f(krow): a
+          // per-lane unit for even and for odd jt plus an immediate 4 (jt / 2)
+          const int vu = VSW ? 4 * (jt >> 1) + ((2 * (jt & 1) + ((r & 3) >> 1)) ^ wswz(krow)) : (ch >> 3);
+          const SSA_LDS char* base0 = (const SSA_LDS char*)(vslab + krow * UV + vu) + (ch & 7) * 2;
+          const SSA_LDS char* base1 = base0 + 16 * UV * 16;  // rows krow + 16: the same swizzle
           const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSA_LDS bf16x4*)base0);
           const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSA_LDS bf16x4*)base1);
           const bf16x8 vf = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
