@@ -849,7 +849,7 @@ def main():
         wsb = torch.empty((ssa.prefill_backward_workspace_size(q2, k2) + 256,), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    rows = ["a1 block_index", "a2 ssa_prefill", "a3 ssa_decode", "a5 dense_causal", "a6-a7 page_select",
+    rows = ["a1 block_index", "a2 ssa_prefill", "a3 ssa_decode", "a5 dense_causal", "a6 page_sums", "a7 page_top_m",
             "a8 page_prefill", "a4 mla_prefill", "a4 mla_decode", "f1 chunk_prefill", "f3 ssa_backward",
             "f2 token_select", "f2 hi_prefill", "a2 ssa_prefill_f32", "a3 ssa_decode_gqa"]
     nev = len(rows) + 1
@@ -875,39 +875,42 @@ def main():
         if run["dense"]:
             ssa.dense_causal(q2, k2, v2, out=od)
         mark(4)
-        if run["page"]:
-            i5, c5 = ssa.page_select(q5, k5, top_m=M5, workspace=ws5)
+        if run["page"]:  # a6 then a7: ssa_page_select in its two phases, timed apart
+            ssa.page_block_sums(q5, k5, ws5)
         mark(5)
         if run["page"]:
-            ssa.prefill(q5, k5, v5, ssa.lists_per_head(i5, c5), out=o5)
+            i5, c5 = ssa.page_select_top(q5, k5, ws5, top_m=M5)
         mark(6)
+        if run["page"]:
+            ssa.prefill(q5, k5, v5, ssa.lists_per_head(i5, c5), out=o5)
+        mark(7)
         if run["mla"]:
             win4 = ssa.block_index(L4 // 128, device=dev)
             ssa.prefill(q4, c4, c4[..., :DV4], ssa.lists_from_index(*win4),
                         scale=1 / 24, out=o4)
-        mark(7)
+        mark(8)
         if run["mla"]:
             r4 = s % R4
             ssa.decode(q4d[r4], pool4, pool4[..., :DV4], bts4[r4], sl4, scale=1 / 24, out=o4d, workspace=ws4)
-        mark(8)
+        mark(9)
         if run["chunk"]:
             ssa.prefill_chunk(q6, kp6, vp6, bt6d, sl6, lists6, out=o6)
-        mark(9)
+        mark(10)
         if run["bwd"]:
             ssa.prefill_backward(q2, k2, v2, ob, gb, lseb, dq=dqb, dk=dkb, dv=dvb, workspace=wsb)
-        mark(10)
-        if run["hi"]:
-            t5, tc5 = ssa.token_select(q5, k5, i5, c5, ws5, top_m=M5, top_k=K5, workspace=wst5)
         mark(11)
         if run["hi"]:
-            ssa.prefill_tokens(q5, k5, v5, lists5w, ssa.token_lists(t5, tc5), out=o5h)
+            t5, tc5 = ssa.token_select(q5, k5, i5, c5, ws5, top_m=M5, top_k=K5, workspace=wst5)
         mark(12)
+        if run["hi"]:
+            ssa.prefill_tokens(q5, k5, v5, lists5w, ssa.token_lists(t5, tc5), out=o5h)
+        mark(13)
         if run["prefill"]:
             ssa.prefill(q1, k1, v1, lists1, out=o1)
-        mark(13)
+        mark(14)
         if run["decode"]:
             ssa.decode(q3[r], kp3g, vp3g, bts[r], sl3, out=o3g)
-        mark(14)
+        mark(15)
         if run["copy"]:
             cp_dst.copy_(cp_src)
 
@@ -935,75 +938,88 @@ def main():
         if not torch.isfinite(t.float()).all():
             raise RuntimeError(f"non-finite {name} output")
 
+    T = dict(zip(rows, per_row))
+    T["a6-a7"] = T["a6 page_sums"] + T["a7 page_top_m"]  # one ssa_page_select
     f1 = ssa_flops(L1, H1, D1)
-    t1 = per_row[12] * 1e-3
+    t1 = T["a2 ssa_prefill_f32"] * 1e-3
     f2 = ssa_flops(L2, H2, D2)
-    t2 = per_row[1] * 1e-3
+    t2 = T["a2 ssa_prefill"] * 1e-3
     tf2 = f2 / t2 / 1e12
     b3 = decode_bytes(lens, H3, H3, D3, D3)
-    t3 = per_row[2] * 1e-3
+    t3 = T["a3 ssa_decode"] * 1e-3
     gb3 = b3 / t3 / 1e9
     b3g = decode_bytes(lens, H3, Hkv3g, D3, D3)
-    t3g = per_row[13] * 1e-3
+    t3g = T["a3 ssa_decode_gqa"] * 1e-3
     gb3g = b3g / t3g / 1e9
     fd = dense_flops(L2, H2, D2)
     f5 = page_flops(L5, H5, D5, M5)
     b5 = 2 * L5 * H5 * D5 * 2
+    # block sums: q and k read (bf16), their fp64 sums written; scores: 2*D fp64
+    # flops per (query block, candidate page) pair of every head
+    b5s = b5 + 2 * H5 * nqb5 * D5 * 8
+    f5s = 2 * D5 * H5 * sum(max(qb - 7, 0) for qb in range(nqb5))
     kernels = {
         "ssa_prefill": {"bound": "mfma", "achieved": tf2, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": tf2 / PEAK_BF16_TFLOPS, "traffic": traffic_for("ssa_prefill"),
-                        "us": per_row[1] * 1e3, "work": f2},
+                        "us": T["a2 ssa_prefill"] * 1e3, "work": f2},
         "ssa_decode": {"bound": "hbm", "achieved": gb3, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                        "frac": gb3 / PEAK_HBM_GBS, "traffic": traffic_for("ssa_decode"),
-                       "us": per_row[2] * 1e3, "work": b3},
+                       "us": T["a3 ssa_decode"] * 1e3, "work": b3},
         "ssa_decode_gqa": {"bound": "hbm", "achieved": gb3g, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": gb3g / PEAK_HBM_GBS, "traffic": traffic_for("ssa_decode_gqa"),
-                           "us": per_row[13] * 1e3, "work": b3g, "heads": f"{H3}/{Hkv3g}"},
-        "dense_causal": {"bound": "mfma", "achieved": fd / (per_row[3] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": fd / (per_row[3] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                         "us": per_row[3] * 1e3, "work": fd},
-        "page_select": {"bound": "hbm", "achieved": b5 / (per_row[4] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                        "unit": "GB/s", "frac": b5 / (per_row[4] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                        "us": per_row[4] * 1e3, "work": b5},
-        "page_prefill": {"bound": "mfma", "achieved": f5 / (per_row[5] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": f5 / (per_row[5] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                         "us": per_row[5] * 1e3, "work": f5},
-        "block_index": {"us": per_row[0] * 1e3},
+                           "us": T["a3 ssa_decode_gqa"] * 1e3, "work": b3g, "heads": f"{H3}/{Hkv3g}"},
+        "dense_causal": {"bound": "mfma", "achieved": fd / (T["a5 dense_causal"] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": fd / (T["a5 dense_causal"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         "us": T["a5 dense_causal"] * 1e3, "work": fd},
+        # a6: an HBM scan (q and k read once, fp64 block sums written)
+        "page_sums": {"bound": "hbm", "achieved": b5s / (T["a6 page_sums"] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                      "unit": "GB/s", "frac": b5s / (T["a6 page_sums"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                      "us": T["a6 page_sums"] * 1e3, "work": b5s},
+        # a7: fp64 scores of every (query block, candidate page) pair, then the top-M lists
+        "page_top_m": {"bound": "mfma_fp64", "achieved": f5s / (T["a7 page_top_m"] * 1e-3) / 1e12,
+                       "peak": PEAK_FP64_TFLOPS, "unit": "TFLOP/s",
+                       "frac": f5s / (T["a7 page_top_m"] * 1e-3) / 1e12 / PEAK_FP64_TFLOPS,
+                       "us": T["a7 page_top_m"] * 1e3, "work": f5s},
+        "page_select": {"us": T["a6-a7"] * 1e3},
+        "page_prefill": {"bound": "mfma", "achieved": f5 / (T["a8 page_prefill"] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": f5 / (T["a8 page_prefill"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         "us": T["a8 page_prefill"] * 1e3, "work": f5},
+        "block_index": {"us": T["a1 block_index"] * 1e3},
         # the small fp32 case: 16 query blocks cannot fill 256 CUs; its time is
         # the latency of one tile, reported against the fp32 MFMA peak
         "ssa_prefill_f32": {"bound": "latency", "achieved": f1 / t1 / 1e12, "peak": PEAK_FP32_TFLOPS,
-                            "unit": "TFLOP/s", "frac": f1 / t1 / 1e12 / PEAK_FP32_TFLOPS, "us": per_row[12] * 1e3,
+                            "unit": "TFLOP/s", "frac": f1 / t1 / 1e12 / PEAK_FP32_TFLOPS, "us": T["a2 ssa_prefill_f32"] * 1e3,
                             "work": f1, "tokens_per_s": L1 / t1},
     }
     f4 = mla_flops(L4, H4, DQ4, DV4)
     b4 = mla_decode_bytes(lens4, H4, DQ4, DV4)
-    kernels["mla_prefill"] = {"bound": "mfma", "achieved": f4 / (per_row[6] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
-                              "unit": "TFLOP/s", "frac": f4 / (per_row[6] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                              "traffic": traffic_for("mla_prefill"), "us": per_row[6] * 1e3, "work": f4}
-    kernels["mla_decode"] = {"bound": "hbm", "achieved": b4 / (per_row[7] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                             "unit": "GB/s", "frac": b4 / (per_row[7] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                             "traffic": traffic_for("mla_decode"), "us": per_row[7] * 1e3, "work": b4}
+    kernels["mla_prefill"] = {"bound": "mfma", "achieved": f4 / (T["a4 mla_prefill"] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                              "unit": "TFLOP/s", "frac": f4 / (T["a4 mla_prefill"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                              "traffic": traffic_for("mla_prefill"), "us": T["a4 mla_prefill"] * 1e3, "work": f4}
+    kernels["mla_decode"] = {"bound": "hbm", "achieved": b4 / (T["a4 mla_decode"] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": b4 / (T["a4 mla_decode"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                             "traffic": traffic_for("mla_decode"), "us": T["a4 mla_decode"] * 1e3, "work": b4}
     f6 = chunk_flops(lens6, T6, H6, D6)
-    kernels["chunk_prefill"] = {"bound": "mfma", "achieved": f6 / (per_row[8] * 1e-3) / 1e12,
+    kernels["chunk_prefill"] = {"bound": "mfma", "achieved": f6 / (T["f1 chunk_prefill"] * 1e-3) / 1e12,
                                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                "frac": f6 / (per_row[8] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                                "us": per_row[8] * 1e3, "work": f6}
+                                "frac": f6 / (T["f1 chunk_prefill"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                "us": T["f1 chunk_prefill"] * 1e3, "work": f6}
     fb = bwd_flops(L2, H2, D2)
-    kernels["ssa_backward"] = {"bound": "mfma", "achieved": fb / (per_row[9] * 1e-3) / 1e12,
+    kernels["ssa_backward"] = {"bound": "mfma", "achieved": fb / (T["f3 ssa_backward"] * 1e-3) / 1e12,
                                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                               "frac": fb / (per_row[9] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                               "us": per_row[9] * 1e3, "work": fb}
+                               "frac": fb / (T["f3 ssa_backward"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                               "us": T["f3 ssa_backward"] * 1e3, "work": fb}
     fh = hi_flops(L5, H5, D5, M5, K5)
     # the second stage scores every recalled token: D fp64 FMAs on a key row
     # (2D bytes, re-read from cache by neighbouring query blocks) per candidate
     cand5 = H5 * sum(128 * min(M5, max(qb - 7, 0)) for qb in range(nqb5) if 128 * min(M5, max(qb - 7, 0)) > K5)
-    kernels["token_select"] = {"us": per_row[10] * 1e3, "candidates": cand5,
-                               "candidate_rows_per_s": cand5 / (per_row[10] * 1e-3),
-                               "fp64_gflops": 2 * D5 * cand5 / (per_row[10] * 1e-3) / 1e9}
-    kernels["hi_prefill"] = {"bound": "mfma", "achieved": fh / (per_row[11] * 1e-3) / 1e12,
+    kernels["token_select"] = {"us": T["f2 token_select"] * 1e3, "candidates": cand5,
+                               "candidate_rows_per_s": cand5 / (T["f2 token_select"] * 1e-3),
+                               "fp64_gflops": 2 * D5 * cand5 / (T["f2 token_select"] * 1e-3) / 1e9}
+    kernels["hi_prefill"] = {"bound": "mfma", "achieved": fh / (T["f2 hi_prefill"] * 1e-3) / 1e12,
                              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                             "frac": fh / (per_row[11] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                             "us": per_row[11] * 1e3, "work": fh}
+                             "frac": fh / (T["f2 hi_prefill"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                             "us": T["f2 hi_prefill"] * 1e3, "work": fh}
     out = {
         "metric": "SSA prefill TFLOP/s (frac MFMA peak) + decode GB/s (frac HBM) at 128K ctx",
         "value": tf2,
@@ -1031,8 +1047,8 @@ def main():
             "decode_tokens_per_s": B3 / t3,
             "decode_gqa_gbps": gb3g,
             "decode_gqa_frac_hbm": gb3g / PEAK_HBM_GBS,
-            "page_select_index_share": per_row[4] / (per_row[4] + per_row[5]),
-            "hi_index_share": (per_row[4] + per_row[10]) / (per_row[4] + per_row[10] + per_row[11]),
+            "page_select_index_share": T["a6-a7"] / (T["a6-a7"] + T["a8 page_prefill"]),
+            "hi_index_share": (T["a6-a7"] + T["f2 token_select"]) / (T["a6-a7"] + T["f2 token_select"] + T["f2 hi_prefill"]),
         },
         "roofline": kernels["ssa_prefill"],
         "roofline_decode": kernels["ssa_decode"],

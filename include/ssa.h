@@ -382,6 +382,23 @@ size_t ssa_page_select_workspace_size(const ssa_attn_args* a, const ssa_window* 
 int ssa_page_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_m, int32_t* idx,
                     int32_t* cnt, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ssa_page_block_sums, ssa_page_select_top -- ssa_page_select in its two
+ * phases, for callers that reuse the block sums (the second stage of
+ * hierarchical indexing, ssa_token_select, reads them from the same
+ * workspace) or time the phases apart.  ssa_page_block_sums writes the fp64
+ * block sums of q and k (the coarse page representations of the LongCat
+ * sparse attention article, section 3) into the workspace; it uses the same
+ * fields as ssa_page_select and neither lists nor top_m.  ssa_page_select_top
+ * then scores and ranks exactly as ssa_page_select from the sums already in
+ * the workspace (it only reads it) and writes idx and cnt.  Arguments,
+ * workspace size and alignment, and errors as ssa_page_select; the pair gives
+ * the same lists bit for bit as one ssa_page_select call on the same
+ * stream. */
+int ssa_page_block_sums(const ssa_attn_args* a, const ssa_window* win, void* workspace, size_t workspace_bytes,
+                        void* stream);
+int ssa_page_select_top(const ssa_attn_args* a, const ssa_window* win, int32_t top_m, int32_t* idx,
+                        int32_t* cnt, const void* workspace, size_t workspace_bytes, void* stream);
+
 /* ssa_page_select_noalloc -- ssa_page_select for callers that cannot allocate
  * device memory (code under graph capture, tight serving loops, harnesses
  * that forbid hipMalloc): the fp64 block sums go to a fixed scratch array

@@ -36,7 +36,8 @@ EXPORTS = (
     "ssa_block_index", "ssa_block_index_seq", "ssa_prefill", "ssa_prefill_tokens", "ssa_dense_causal",
     "ssa_prefill_chunk", "ssa_prefill_backward", "ssa_prefill_backward_workspace_size", "ssa_decode",
     "ssa_decode_dense", "ssa_decode_dense_workspace_size", "ssa_decode_workspace_size", "ssa_page_select",
-    "ssa_page_select_workspace_size", "ssa_page_select_noalloc", "ssa_token_select", "ssa_token_select_workspace_size", "ssa_last_error",
+    "ssa_page_select_workspace_size", "ssa_page_select_noalloc", "ssa_page_block_sums", "ssa_page_select_top",
+    "ssa_token_select", "ssa_token_select_workspace_size", "ssa_last_error",
     "ssa_version",
 )
 
@@ -190,11 +191,14 @@ def load(path: str = LIB_PATH):
     lib.ssa_page_select.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CWindow), i32, vp, vp, vp,
                                     ctypes.c_size_t, vp]
     lib.ssa_page_select_noalloc.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CWindow), i32, vp, vp, vp]
+    lib.ssa_page_block_sums.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CWindow), vp, ctypes.c_size_t, vp]
+    lib.ssa_page_select_top.argtypes = [ctypes.POINTER(CAttnArgs), ctypes.POINTER(CWindow), i32, vp, vp, vp,
+                                        ctypes.c_size_t, vp]
     lib.ssa_last_error.restype = ctypes.c_char_p
     lib.ssa_last_error.argtypes = []
     lib.ssa_version.argtypes = []
     for name in ("ssa_block_index", "ssa_block_index_seq", "ssa_prefill", "ssa_dense_causal", "ssa_prefill_chunk",
-                 "ssa_decode", "ssa_page_select", "ssa_version"):
+                 "ssa_decode", "ssa_page_select", "ssa_page_block_sums", "ssa_page_select_top", "ssa_version"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -552,6 +556,39 @@ def page_select(q, k, top_m: int = 8, window: Window = DEFAULT_WINDOW, workspace
     off = (-base) % 256
     _check(lib.ssa_page_select(ctypes.byref(a), ctypes.byref(w), top_m, _ptr(idx), _ptr(cnt),
                                base + off, workspace.numel() - off, _stream(stream)))
+    return idx, cnt
+
+
+@_on_stream
+def page_block_sums(q, k, workspace, window: Window = DEFAULT_WINDOW, stream=None):
+    """ssa_page_block_sums: the fp64 block sums of q and k into ``workspace``
+    (uint8, at least page_select_workspace_size + 256 bytes); returns it."""
+    lib = load()
+    a = _attn_args(q, k, k, q, None, 1.0)
+    w = window.c()
+    base = workspace.data_ptr()
+    off = (-base) % 256
+    _check(lib.ssa_page_block_sums(ctypes.byref(a), ctypes.byref(w), base + off, workspace.numel() - off,
+                                   _stream(stream)))
+    return workspace
+
+
+@_on_stream
+def page_select_top(q, k, workspace, top_m: int = 8, window: Window = DEFAULT_WINDOW, stream=None):
+    """ssa_page_select_top: (idx, cnt) of ssa_page_select from the block sums
+    ``page_block_sums`` left in ``workspace``."""
+    lib = load()
+    B, L, Hq, D = q.shape
+    nqb = (L + window.block_size - 1) // window.block_size
+    W = window.width + top_m
+    idx = torch.empty((B, Hq, nqb, W), dtype=torch.int32, device=q.device)
+    cnt = torch.empty((B, Hq, nqb), dtype=torch.int32, device=q.device)
+    a = _attn_args(q, k, k, q, None, 1.0)
+    w = window.c()
+    base = workspace.data_ptr()
+    off = (-base) % 256
+    _check(lib.ssa_page_select_top(ctypes.byref(a), ctypes.byref(w), top_m, _ptr(idx), _ptr(cnt), base + off,
+                                   workspace.numel() - off, _stream(stream)))
     return idx, cnt
 
 

@@ -557,9 +557,10 @@ size_t ssa_page_select_workspace_size(const ssa_attn_args* a, const ssa_window* 
 namespace {
 
 // Validation shared by the page-selection entry points; fills everything of
-// `p` but the workspace pointers.
+// `p` but the workspace pointers.  lists = false: the block-sums phase, which
+// writes no lists (idx and cnt unused).
 int page_select_params(const ssa_attn_args* a, const ssa_window* win, int32_t top_m, int32_t* idx, int32_t* cnt,
-                       const char* who, ssa::PageSelectParams& p) {
+                       const char* who, ssa::PageSelectParams& p, bool lists = true) {
   if (!a) return fail(SSA_ERR_INVALID, "%s: args is NULL", who);
   if (!valid_window(win, who, 64)) return SSA_ERR_INVALID;
   if (a->dtype != SSA_DTYPE_BF16) return fail(SSA_ERR_UNSUPPORTED, "%s: only BF16 q/k are supported", who);
@@ -572,8 +573,9 @@ int page_select_params(const ssa_attn_args* a, const ssa_window* win, int32_t to
     return fail(SSA_ERR_INVALID, "%s: list width %d exceeds 64", who, win->n_global + win->n_local + top_m);
   if (win->block_size != 128) return fail(SSA_ERR_UNSUPPORTED, "%s: block_size must be 128", who);
   if (ceil_div(a->L, 128) > 16384) return fail(SSA_ERR_UNSUPPORTED, "%s: L=%d exceeds 16384 blocks", who, a->L);
-  if (!a->q || !a->k || !idx || !cnt) return fail(SSA_ERR_INVALID, "%s: q, k, idx and cnt must be non-NULL", who);
-  if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(idx, 4) || !aligned(cnt, 4))
+  if (!a->q || !a->k) return fail(SSA_ERR_INVALID, "%s: q and k must be non-NULL", who);
+  if (lists && (!idx || !cnt)) return fail(SSA_ERR_INVALID, "%s: idx and cnt must be non-NULL", who);
+  if (!aligned(a->q, 16) || !aligned(a->k, 16) || (lists && (!aligned(idx, 4) || !aligned(cnt, 4))))
     return fail(SSA_ERR_INVALID, "%s: q/k must be 16-byte and idx/cnt 4-byte aligned", who);
   if (!valid_strides(a->q_stride, 2, who, "q") || !valid_strides(a->k_stride, 2, who, "k")) return SSA_ERR_INVALID;
   p = ssa::PageSelectParams{};
@@ -624,6 +626,37 @@ int ssa_page_select(const ssa_attn_args* a, const ssa_window* win, int32_t top_m
   if (!aligned(workspace, 256)) return fail(SSA_ERR_INVALID, "%s: workspace must be 256-byte aligned", who);
   page_select_workspace(p, workspace);
   return device_status(ssa::launch_page_select(p, as_stream(stream)), who);
+}
+
+// the workspace checks of the page-selection entry points
+static int page_workspace_ok(const ssa_attn_args* a, const ssa_window* win, const void* workspace,
+                             size_t workspace_bytes, const char* who) {
+  const size_t need = ssa_page_select_workspace_size(a, win);
+  if (!workspace || workspace_bytes < need)
+    return fail(SSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
+                workspace ? workspace_bytes : static_cast<size_t>(0));
+  if (!aligned(workspace, 256)) return fail(SSA_ERR_INVALID, "%s: workspace must be 256-byte aligned", who);
+  return SSA_OK;
+}
+
+int ssa_page_block_sums(const ssa_attn_args* a, const ssa_window* win, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  const char* who = "ssa_page_block_sums";
+  ssa::PageSelectParams p;
+  if (const int rc = page_select_params(a, win, 0, nullptr, nullptr, who, p, false); rc != SSA_OK) return rc;
+  if (const int rc = page_workspace_ok(a, win, workspace, workspace_bytes, who); rc != SSA_OK) return rc;
+  page_select_workspace(p, workspace);
+  return device_status(ssa::launch_page_sums(p, as_stream(stream)), who);
+}
+
+int ssa_page_select_top(const ssa_attn_args* a, const ssa_window* win, int32_t top_m, int32_t* idx, int32_t* cnt,
+                        const void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "ssa_page_select_top";
+  ssa::PageSelectParams p;
+  if (const int rc = page_select_params(a, win, top_m, idx, cnt, who, p); rc != SSA_OK) return rc;
+  if (const int rc = page_workspace_ok(a, win, workspace, workspace_bytes, who); rc != SSA_OK) return rc;
+  page_select_workspace(p, const_cast<void*>(workspace));  // read only by the select kernel
+  return device_status(ssa::launch_page_top(p, as_stream(stream)), who);
 }
 
 int ssa_page_select_noalloc(const ssa_attn_args* a, const ssa_window* win, int32_t top_m, int32_t* idx,

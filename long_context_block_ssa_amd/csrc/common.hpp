@@ -239,6 +239,10 @@ hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t stream);
 size_t decode_mla_workspace_bytes(int32_t B, int32_t Hq, int32_t W);
 
 hipError_t launch_page_select(const PageSelectParams& p, hipStream_t stream);
+// its two phases: the fp64 block sums into p.qsum / p.ksum, then the scores
+// and top-M lists from them
+hipError_t launch_page_sums(const PageSelectParams& p, hipStream_t stream);
+hipError_t launch_page_top(const PageSelectParams& p, hipStream_t stream);
 
 // The fixed device scratch of the allocation-free page selection (the fp64
 // block sums of q and k): its size, and its address on the current device

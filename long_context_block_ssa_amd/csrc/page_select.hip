@@ -322,16 +322,23 @@ hipError_t page_select_scratch(void** ptr) {
   return hipSuccess;
 }
 
-hipError_t launch_page_select(const PageSelectParams& p, hipStream_t stream) {
+hipError_t launch_page_sums(const PageSelectParams& p, hipStream_t stream) {
   const int64_t nsum = static_cast<int64_t>(p.B) * (p.Hq + p.Hkv) * p.nqb;
-  hipError_t e = p.D == 128 ? launch_kernel(block_sums_kernel<128>, dim3(static_cast<unsigned>(nsum)), dim3(kSumThreads), 0, stream, p)
-               : p.D == 64  ? launch_kernel(block_sums_kernel<64>, dim3(static_cast<unsigned>(nsum)), dim3(kSumThreads), 0, stream, p)
-                            : hipErrorNotSupported;
-  if (e != hipSuccess) return e;
+  return p.D == 128 ? launch_kernel(block_sums_kernel<128>, dim3(static_cast<unsigned>(nsum)), dim3(kSumThreads), 0, stream, p)
+       : p.D == 64  ? launch_kernel(block_sums_kernel<64>, dim3(static_cast<unsigned>(nsum)), dim3(kSumThreads), 0, stream, p)
+                    : hipErrorNotSupported;
+}
+
+hipError_t launch_page_top(const PageSelectParams& p, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.Hq * ((p.nqb + kRows - 1) / kRows));
   if (p.D == 128) return launch_kernel(select_kernel<128>, dim3(grid), dim3(kSelThreads), 0, stream, p);
   if (p.D == 64) return launch_kernel(select_kernel<64>, dim3(grid), dim3(kSelThreads), 0, stream, p);
   return hipErrorNotSupported;
+}
+
+hipError_t launch_page_select(const PageSelectParams& p, hipStream_t stream) {
+  const hipError_t e = launch_page_sums(p, stream);
+  return e != hipSuccess ? e : launch_page_top(p, stream);
 }
 
 }  // namespace ssa

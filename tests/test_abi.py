@@ -358,6 +358,27 @@ def test_page_select_rejects(lib):
         == ssa.SSA_ERR_UNSUPPORTED
 
 
+def test_page_phases_reject(lib):
+    """ssa_page_block_sums / ssa_page_select_top validate like ssa_page_select
+    (the sums phase takes no lists), and nothing is launched on an error."""
+    a = good_args()
+    w = ssa.CWindow(128, 1, 7)
+    need = lib.ssa_page_select_workspace_size(ctypes.byref(a), ctypes.byref(w))
+    assert lib.ssa_page_block_sums(ctypes.byref(a), ctypes.byref(w), FAKE, need - 1, None) == ssa.SSA_ERR_WORKSPACE
+    assert lib.ssa_page_block_sums(ctypes.byref(a), ctypes.byref(w), None, need, None) == ssa.SSA_ERR_WORKSPACE
+    assert lib.ssa_page_block_sums(ctypes.byref(a), ctypes.byref(w), FAKE + 16, need, None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_page_block_sums(None, ctypes.byref(w), FAKE, need, None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_page_block_sums(ctypes.byref(good_args(Dqk=576, Dv=512)), ctypes.byref(w), FAKE, 1 << 30, None) \
+        == ssa.SSA_ERR_UNSUPPORTED
+    assert lib.ssa_page_select_top(ctypes.byref(a), ctypes.byref(w), 8, FAKE, FAKE, FAKE, need - 1, None) \
+        == ssa.SSA_ERR_WORKSPACE
+    assert lib.ssa_page_select_top(ctypes.byref(a), ctypes.byref(w), 8, None, FAKE, FAKE, need, None) \
+        == ssa.SSA_ERR_INVALID
+    assert lib.ssa_page_select_top(ctypes.byref(a), ctypes.byref(w), 33, FAKE, FAKE, FAKE, need, None) \
+        == ssa.SSA_ERR_INVALID
+    assert "ssa_page_select_top" in lib.ssa_last_error().decode()
+
+
 def test_page_select_noalloc_rejects(lib):
     """Sizes beyond the fixed 32 MiB scratch are refused before any device call;
     the usual argument checks run first."""

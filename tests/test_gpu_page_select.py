@@ -35,6 +35,23 @@ def test_page_select_small(lib, L, Hq, Hkv, D, M):
     compare_lists(idx, cnt, qh, kh, M, ridx, rcnt, near)
 
 
+@pytest.mark.parametrize("L,Hq,Hkv,D,M", [(128 * 40 + 17, 2, 1, 128, 8), (128 * 33, 2, 2, 64, 4)])
+def test_page_select_phases_equal_one_call(lib, L, Hq, Hkv, D, M):
+    """ssa_page_block_sums then ssa_page_select_top on one workspace give the
+    lists of one ssa_page_select call bit for bit (the same kernels)."""
+    qh, q = gen(53, synth.Q, 1, L, Hq, D)
+    kh, k = gen(53, synth.K, 1, L, Hkv, D)
+    say(f"page phases L={L} Hq={Hq} Hkv={Hkv} D={D} M={M}")
+    idx, cnt = lib.page_select(q, k, top_m=M)
+    ws = torch.full((lib.page_select_workspace_size(q, k) + 256,), 0xFF, dtype=torch.uint8, device="cuda")
+    lib.page_block_sums(q, k, ws)
+    idx2, cnt2 = lib.page_select_top(q, k, ws, top_m=M)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)
+    ridx, rcnt, near = oracle.page_select(qh, kh, top_m=M)
+    compare_lists(idx2, cnt2, qh, kh, M, ridx, rcnt, near)
+
+
 def test_page_select_planted_and_tie(lib):
     """A planted page is selected; an exact duplicate loses the tie to the
     lower page; both are taken when M = 2."""
