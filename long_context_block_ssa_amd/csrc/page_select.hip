@@ -120,15 +120,35 @@ __device__ __forceinline__ double read_lane_f64(double v, int l) {
   return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// (t1, t2): the two largest of the lane's set; merged with the set of the
+// lane CTRL's DPP pattern reads from (disjoint from the lane's own at every
+// step of a rotate-and-merge all-reduce)
+template <int CTRL>
+__device__ __forceinline__ void top2_merge(double& t1, double& t2) {
+  const uint64_t u1 = __builtin_bit_cast(uint64_t, t1), u2 = __builtin_bit_cast(uint64_t, t2);
+  const uint32_t a = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(u1)), CTRL, 0xF, 0xF, false);
+  const uint32_t b = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(u1 >> 32)), CTRL, 0xF, 0xF, false);
+  const uint32_t c = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(u2)), CTRL, 0xF, 0xF, false);
+  const uint32_t d = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(u2 >> 32)), CTRL, 0xF, 0xF, false);
+  const double p1 = __builtin_bit_cast(double, (static_cast<uint64_t>(b) << 32) | a);
+  const double p2 = __builtin_bit_cast(double, (static_cast<uint64_t>(d) << 32) | c);
+  const double n2 = __builtin_fmax(__builtin_fmin(t1, p1), __builtin_fmax(t2, p2));
+  t1 = __builtin_fmax(t1, p1);
+  t2 = n2;
+}
+
 template <int D>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(PageSelectParams p) {
   constexpr int NM = D / 8;  // 16-byte loads per operand row share; 2 MFMAs each
   __shared__ double sc[kRows][kPad];
 
+  // heaviest tiles first (a tile's candidates grow with its query blocks),
+  // every (b, head) of a tile index side by side, so the long tiles start
+  // early and the short ones fill in behind them
   const int tiles = (p.nqb + kRows - 1) / kRows;
-  const int tile = blockIdx.x % tiles;
-  const int h = (blockIdx.x / tiles) % p.Hq;
-  const int b = blockIdx.x / (tiles * p.Hq);
+  const int tile = tiles - 1 - static_cast<int>(blockIdx.x / (p.B * p.Hq));
+  const int h = static_cast<int>(blockIdx.x % p.Hq);
+  const int b = static_cast<int>((blockIdx.x / p.Hq) % p.B);
   const int hk = h / p.group;
   const int qb0 = tile * kRows;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -194,7 +214,27 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(PageSelectParams p)
       // skipped.  The bar comes from a bitonic sort across the lanes.
       double bs = -__builtin_inf();
       int bc = 0x7fffffff;
-      if (tc == 0x7fffffff) {
+      if (tc == 0x7fffffff && M <= 8) {
+        // Up to 8 kept: each 16-lane row of the wave finds the two best of
+        // its lanes' best scores (a rotate-and-merge all-reduce on DPP, no
+        // LDS); every row's second best is reached by two distinct
+        // candidates, so the lowest of the four is reached by 8 >= M of
+        // them and a candidate scoring strictly below it cannot be kept.
+        double t1 = -__builtin_inf(), t2 = -__builtin_inf();
+#pragma unroll
+        for (int k = 0; k < kChunk / 64; ++k) {
+          const int c = cc + 64 * k + lane;
+          double s = sc[wave + 4 * rr][64 * k + lane];
+          if (s != s) s = -__builtin_inf();
+          if (c >= c_lo && c < c_hi) t1 = __builtin_fmax(t1, s);
+        }
+        top2_merge<0x128>(t1, t2);  // row_ror:8
+        top2_merge<0x124>(t1, t2);  // row_ror:4
+        top2_merge<0x122>(t1, t2);  // row_ror:2
+        top2_merge<0x121>(t1, t2);  // row_ror:1
+        bs = __builtin_fmin(__builtin_fmin(read_lane_f64(t2, 0), read_lane_f64(t2, 16)),
+                            __builtin_fmin(read_lane_f64(t2, 32), read_lane_f64(t2, 48)));
+      } else if (tc == 0x7fffffff) {
 #pragma unroll
         for (int k = 0; k < kChunk / 64; ++k) {
           const int c = cc + 64 * k + lane;

@@ -24,11 +24,11 @@
 //   3. fill: each open row appends (row, slot) to its pages' buckets (the
 //      order inside a bucket is free: every entry has its own output place);
 //   4. score: one workgroup per (b, head, page) loads the page's 128 key
-//      rows once into registers and multiplies the query-block sums of up to
-//      16 recalling rows at a time against them on the fp64 matrix cores
-//      (the key rows stay bf16 in registers and are widened per step),
-//      writing order-preserving 64-bit keys (NaN counts as -inf, -0 as +0)
-//      into each recalling row's slot;
+//      rows once into registers (a row per lane, bf16) and takes the dot
+//      products with the query-block sums of up to 8 recalling rows at a
+//      time as fp64 FMAs on the vector units, the query-block sum reaching
+//      every lane through a row broadcast, writing order-preserving 64-bit
+//      keys (NaN counts as -inf, -0 as +0) into each recalling row's slot;
 //   5. select: one wave per open row finds the K-th largest key T exactly
 //      by a radix select (LDS histograms, 8 bits a pass; once at most 64
 //      keys share the leading bits found so far, they are ranked by
@@ -44,13 +44,11 @@ namespace ssa {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTsThreads = 256;
 constexpr int kTsWaves = kTsThreads / 64;
 constexpr int kMaxSlots = 32;
-constexpr int kEnt = 16;  // recalling rows staged per round of the score kernel
-static_assert(kTsThreads / 16 == kEnt, "the score kernel stages one recalling row per 16 threads");
 
 // order-preserving map of a score to an unsigned key (larger score -> larger
 // key); -0 is folded onto +0 and NaN onto -inf
@@ -59,13 +57,6 @@ __device__ __forceinline__ uint64_t order_key(double x) {
   if (x != x) x = -__builtin_inf();
   const uint64_t u = __builtin_bit_cast(uint64_t, x);
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-}
-
-__device__ __forceinline__ double shfl_xor_f64(double v, int m) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, v);
-  const int lo = __shfl_xor(static_cast<int>(static_cast<uint32_t>(u)), m);
-  const int hi = __shfl_xor(static_cast<int>(static_cast<uint32_t>(u >> 32)), m);
-  return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo));
 }
 
 // exclusive prefix sum of v over the workgroup (every thread calls it)
@@ -168,19 +159,62 @@ __global__ __launch_bounds__(kTsThreads) void ts_fill_kernel(TokenSelectParams p
   p.ent[bh * p.nqb * p.S + pos] = qb * p.S + lane;
 }
 
-// 4. one workgroup per (b, h, page): scores = (query-block sums of up to 16
-// recalling rows) x (the page's 128 key rows)^T on v_mfma_f64_16x16x4f64.
-// Wave w owns rows 32w .. 32w+31 as two 16-row tiles.  Contraction step s
-// takes channels (D/4) kk + s for kk = 0..3 (lane l feeds kk = l / 16), so a
-// lane's key channels are D/4 contiguous bf16 values, loaded once and
-// widened to fp64 per step.  A lane's output register r holds recalling row
-// l/16 + 4r and key row l mod 16 of the tile.
+// 4. one workgroup of two waves per (b, h, page): lane l of wave w owns key
+// row 64 w + l of the page.  On this chip fp64 FMAs on the vector units run
+// at the fp64 matrix rate, so the scores are plain dot products with no
+// padding of the recalling rows to a matrix tile (a page is recalled by ~8
+// rows on average, half a 16-row tile).  A wave reads its 64 key rows
+// coalesced through LDS into registers once (bf16, a row per lane), stages
+// the query-block sums of up to 8 recalling rows in LDS (all loads in flight
+// together), then widens 16 channels of its key row to fp64 at a time and
+// accumulates the 8 dot products side by side; lane j of each 16-lane row
+// holds channel j of a query-block sum and the FMA's row broadcast hands it
+// to every lane.  Measured at L = 131072, H = 16, M = 8 (same box, same
+// inputs): ~235 us against ~330 us for the former 16 x 16 fp64 MFMA tiles;
+// the counters show the vector unit ~2/3 busy at a 1.4 GHz clock (fp64 FMAs
+// keep the card's clock low), a quarter of its instructions the widening.
+constexpr int kScThreads = 128;
+constexpr int kScEnt = 8;     // recalling rows per batch, accumulated side by side
+constexpr int kScSlice = 16;  // channels of a key row widened to fp64 at a time
+
+// acc += (lane j of this lane's 16-lane row of q) * k[j] for j = 0..15: the
+// fp64 FMA takes its first operand through a row broadcast, so 16 lanes
+// holding 16 channels of a query-block sum feed every key lane of the row.
+// The s_nop covers the wait states a broadcast source needs after a vector
+// write of it.
+__device__ __forceinline__ void fmac_row_bcast16(double& acc, double q, const double* k) {
+  asm volatile(
+      "s_nop 1\n"
+      "v_fmac_f64_dpp %0, %1, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %0, %1, %3 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %0, %1, %4 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %0, %1, %5 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %0, %1, %6 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %0, %1, %7 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %0, %1, %8 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %0, %1, %9 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %0, %1, %10 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %0, %1, %11 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %0, %1, %12 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %0, %1, %13 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %0, %1, %14 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %0, %1, %15 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %0, %1, %16 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f64_dpp %0, %1, %17 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+      : "+v"(acc)
+      : "v"(q), "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(k[4]), "v"(k[5]), "v"(k[6]), "v"(k[7]), "v"(k[8]),
+        "v"(k[9]), "v"(k[10]), "v"(k[11]), "v"(k[12]), "v"(k[13]), "v"(k[14]), "v"(k[15]));
+}
+
 template <int D>
-__global__ __launch_bounds__(kTsThreads) __attribute__((amdgpu_waves_per_eu(3))) void ts_score_kernel(TokenSelectParams p) {
-  constexpr int NS = D / 4;     // contraction steps
-  constexpr int QP = D + 2;     // padded LDS row of query-block sums
-  __shared__ double qs[kEnt][QP];
-  __shared__ int32_t ents[kEnt];
+__global__ __launch_bounds__(kScThreads) __attribute__((amdgpu_waves_per_eu(4))) void ts_score_kernel(TokenSelectParams p) {
+  constexpr int HD = kScSlice < D ? kScSlice : D;  // channels per slice
+  constexpr int QM = HD / 16;                      // query-sum values per lane and slice
+  static_assert(HD % 16 == 0 && D % HD == 0, "slices are whole 16-lane rows of channels");
+  // per wave: a 128-byte segment of its 64 key rows at a time, then the
+  // batch's query-block sums
+  constexpr int kUnits = (kScEnt * D * 8 > 64 * 128 ? kScEnt * D * 8 : 64 * 128) / 16;
+  __shared__ u32x4 lds[kScThreads / 64][kUnits];
   const int64_t pcix = blockIdx.x;
   const int n = p.cnt[pcix];
   if (n == 0) return;
@@ -188,69 +222,95 @@ __global__ __launch_bounds__(kTsThreads) __attribute__((amdgpu_waves_per_eu(3)))
   const int64_t bh = pcix / p.nqb;
   const int h = static_cast<int>(bh % p.Hq), b = static_cast<int>(bh / p.Hq);
   const int hk = h / p.group;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, kk = lane >> 4;
-  // B operand: key row 32 wave + 16 t + col, channels NS kk .. NS kk + NS-1
-  constexpr int NV = NS / 8;  // 16-byte loads per tile
-  u32x4 kr[2][NV];
-  {
-    const __bf16* kbase = static_cast<const __bf16*>(p.k) + b * p.ks_b + hk * p.ks_h +
-                          static_cast<int64_t>(c) * 128 * p.ks_l + NS * kk;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int v = 0; v < NV; ++v)
-        kr[t][v] = *reinterpret_cast<const u32x4*>(kbase + (32 * wave + 16 * t + col) * p.ks_l + 8 * v);
-  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int key = 64 * wave + lane;
+  const __bf16* kpage = static_cast<const __bf16*>(p.k) + b * p.ks_b + hk * p.ks_h +
+                        (static_cast<int64_t>(c) * 128 + 64 * wave) * p.ks_l;
   const int32_t* eb = p.ent + bh * p.nqb * p.S + p.off[pcix];
   const double* qsb = p.qsum + bh * p.nqb * D;
   uint64_t* kb = p.keys + bh * p.nqb * p.S * 128;
-  for (int e0 = 0; e0 < n; e0 += kEnt) {
-    const int ne = min(kEnt, n - e0);
-    __syncthreads();  // the previous round's reads of qs and ents are done
-    if (tid < ne) ents[tid] = eb[e0 + tid];
-    __syncthreads();
-    {  // thread t stages D/16 channels of entry t/16 (independent loads)
-      constexpr int CPT = D / 16;
-      const int ee = tid / 16, ch0 = (tid % 16) * CPT;
-      if (ee < ne) {
-        const double* src = qsb + static_cast<int64_t>(ents[ee] / p.S) * D + ch0;
-        double tv[CPT];
+  double (*wq)[D] = reinterpret_cast<double (*)[D]>(lds[wave]);
+  u32x4* wk = lds[wave];  // [64 rows][8 units of 16 bytes], unit u of row r at u ^ (r & 7)
+  // the wave's key rows, bf16, into registers (lane = row): each 128-byte
+  // segment is read coalesced (8 rows per load) into LDS and read back by
+  // rows; the XOR keeps 8 neighbouring lanes on distinct banks
+  u32x4 raw[D / 8];
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) tv[j] = src[j];
+  for (int sg = 0; sg < D / 64; ++sg) {
+    u32x4 t[8];
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) qs[ee][ch0 + j] = tv[j];
-      } else {  // unused A rows: zeros (their outputs are not stored)
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) qs[ee][ch0 + j] = 0.0;
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      t[i] = *reinterpret_cast<const u32x4*>(kpage + r * p.ks_l + 64 * sg + 8 * (lane & 7));
     }
-    __syncthreads();
-    f64x4 acc[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
-    const double* arow = &qs[col][NS * kk];  // A operand: recalling row col (rows >= ne are ignored)
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      wk[8 * r + ((lane & 7) ^ (r & 7))] = t[i];
+    }
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int st = 8 * v + j;
-        const double a = arow[st];
+    for (int u = 0; u < 8; ++u) raw[8 * sg + u] = wk[8 * lane + (u ^ (lane & 7))];
+    __builtin_amdgcn_wave_barrier();
+  }
+  for (int e0 = 0; e0 < n; e0 += kScEnt) {
+    const int ne = min(kScEnt, n - e0);
+    // lane e < ne holds the batch's recalling row e (qb * S + slot)
+    const int my_ev = lane < ne ? eb[e0 + lane] : 0;
+    const int my_qo = (my_ev / p.S) * D;
+    // the batch's query-block sums into this wave's LDS rows (wave-local:
+    // the wave's own LDS accesses complete in order)
+    // (every row of the batch is loaded, past ne the first block's sums, so
+    // that all loads are in flight together)
+    {
+      constexpr int PL = (D + 127) / 128;  // 16-byte loads per lane and row
+      f64x2 t[kScEnt][PL];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const uint32_t x = kr[t][v][j >> 1];
-          const float kf = __builtin_bit_cast(float, (j & 1) ? (x & 0xFFFF0000u) : (x << 16));
-          acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, static_cast<double>(kf), acc[t], 0, 0, 0);
+      for (int e = 0; e < kScEnt; ++e) {
+        const double* src = qsb + __builtin_amdgcn_readlane(my_qo, e);
+#pragma unroll
+        for (int i = 0; i < PL; ++i)
+          if (2 * lane + 128 * i < D) t[e][i] = *reinterpret_cast<const f64x2*>(src + 2 * lane + 128 * i);
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int e = 0; e < kScEnt; ++e)
+#pragma unroll
+        for (int i = 0; i < PL; ++i)
+          if (2 * lane + 128 * i < D) *reinterpret_cast<f64x2*>(&wq[e][2 * lane + 128 * i]) = t[e][i];
+    }
+    __builtin_amdgcn_wave_barrier();
+    double acc[kScEnt];
+#pragma unroll
+    for (int e = 0; e < kScEnt; ++e) acc[e] = 0.0;
+#pragma unroll
+    for (int ps = 0; ps < D / HD; ++ps) {
+      // one slice of widened keys live at a time: the empty asm keeps the
+      // widening inside the batch loop instead of hoisted (all D channels
+      // as fp64 would not fit in registers)
+#pragma unroll
+      for (int v = 0; v < HD / 8; ++v) asm volatile("" : "+v"(raw[HD / 8 * ps + v]));
+      double kf[HD];
+#pragma unroll
+      for (int v = 0; v < HD / 8; ++v)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t x = raw[HD / 8 * ps + v][w];
+          kf[8 * v + 2 * w] = static_cast<double>(__builtin_bit_cast(float, x << 16));
+          kf[8 * v + 2 * w + 1] = static_cast<double>(__builtin_bit_cast(float, x & 0xFFFF0000u));
+        }
+#pragma unroll
+      for (int e = 0; e < kScEnt; ++e) {
+        if (e < ne) {
+#pragma unroll
+          for (int m = 0; m < QM; ++m) fmac_row_bcast16(acc[e], wq[e][HD * ps + 16 * m + (lane & 15)], kf + 16 * m);
         }
       }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = kk + 4 * r;
-      if (e < ne) {
-        const int ev = ents[e];
-        uint64_t* dst = kb + (static_cast<int64_t>(ev / p.S) * p.S + ev % p.S) * 128 + 32 * wave + col;
-        dst[0] = order_key(acc[0][r]);
-        dst[16] = order_key(acc[1][r]);
-      }
     }
+#pragma unroll
+    for (int e = 0; e < kScEnt; ++e)
+      if (e < ne) kb[static_cast<int64_t>(__builtin_amdgcn_readlane(my_ev, e)) * 128 + key] = order_key(acc[e]);
   }
 }
 
@@ -396,8 +456,8 @@ hipError_t launch_token_select(const TokenSelectParams& p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   e = launch_kernel(ts_fill_kernel, dim3(wave_groups), dim3(kTsThreads), 0, stream, p);
   if (e != hipSuccess) return e;
-  e = p.D == 128 ? launch_kernel(ts_score_kernel<128>, dim3(static_cast<unsigned>(R)), dim3(kTsThreads), 0, stream, p)
-                 : launch_kernel(ts_score_kernel<64>, dim3(static_cast<unsigned>(R)), dim3(kTsThreads), 0, stream, p);
+  e = p.D == 128 ? launch_kernel(ts_score_kernel<128>, dim3(static_cast<unsigned>(R)), dim3(kScThreads), 0, stream, p)
+                 : launch_kernel(ts_score_kernel<64>, dim3(static_cast<unsigned>(R)), dim3(kScThreads), 0, stream, p);
   if (e != hipSuccess) return e;
   const size_t lds = sizeof(uint64_t) * 128 * static_cast<size_t>(p.S) * kTsWaves;
   e = raise_lds_limit_once<ts_select_kernel>(static_cast<int>(sizeof(uint64_t) * 128 * kMaxSlots * kTsWaves));
