@@ -338,7 +338,16 @@ __global__ __launch_bounds__(kTsThreads) void ts_select_kernel(TokenSelectParams
   uint64_t* small = small_all[wave];
   const int C = npg * 128, K = p.K;
   const uint64_t* src = p.keys + row * p.S * 128;
-  for (int r = lane; r < C; r += 64) key[r] = src[r];
+  // C is a multiple of 128: 8 loads of a lane in flight together
+  for (int r0 = 0; r0 < C; r0 += 512) {
+    uint64_t t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (r0 + 64 * i < C) t[i] = src[r0 + 64 * i + lane];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (r0 + 64 * i < C) key[r0 + 64 * i + lane] = t[i];
+  }
   const int cpg = p.pages[row * p.S + (lane < npg ? lane : 0)];  // page of slot `lane`
   __builtin_amdgcn_wave_barrier();
 
@@ -352,9 +361,15 @@ __global__ __launch_bounds__(kTsThreads) void ts_select_kernel(TokenSelectParams
 #pragma unroll
     for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0;
     __builtin_amdgcn_wave_barrier();
-    for (int r = lane; r < C; r += 64) {
-      const uint64_t kk = key[r];
-      if (pass == 0 || (kk >> (shift + 8)) == prefix) atomicAdd(&hist[(kk >> shift) & 255], 1u);
+    for (int r0 = 0; r0 < C; r0 += 512) {  // 8 reads of a lane before their atomics
+      uint64_t t[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (r0 + 64 * i < C) t[i] = key[r0 + 64 * i + lane];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (r0 + 64 * i < C && (pass == 0 || (t[i] >> (shift + 8)) == prefix))
+          atomicAdd(&hist[(t[i] >> shift) & 255], 1u);
     }
     __builtin_amdgcn_wave_barrier();
     uint32_t cb[4], tot = 0;  // bins in descending order, 4 per lane
