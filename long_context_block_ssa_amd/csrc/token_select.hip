@@ -49,6 +49,7 @@ typedef double f64x2 __attribute__((ext_vector_type(2)));
 constexpr int kTsThreads = 256;
 constexpr int kTsWaves = kTsThreads / 64;
 constexpr int kMaxSlots = 32;
+constexpr int kRegSlots = 8;  // rows of at most this many pages keep their keys in registers
 
 // order-preserving map of a score to an unsigned key (larger score -> larger
 // key); -0 is folded onto +0 and NaN onto -inf
@@ -322,9 +323,13 @@ __device__ __forceinline__ int rank_below(uint64_t b) {
 
 // 5. one wave per open row, four rows per workgroup; everything stays inside
 // the wave (its own LDS regions, ballots and lane shuffles), so no workgroup
-// barrier is needed
+// barrier is needed.  Candidate e = 64 i + lane of a row is lane's i-th key:
+// in registers when a row has at most NK * 64 candidates (NK > 0), else in
+// the wave's LDS region (NK = 0).
+template <int NK>
 __global__ __launch_bounds__(kTsThreads) void ts_select_kernel(TokenSelectParams p) {
-  extern __shared__ uint64_t lds_keys[];  // per wave: S * 128 keys
+  constexpr bool kRegs = NK > 0;
+  extern __shared__ uint64_t lds_keys[];  // NK = 0: per wave S * 128 keys
   __shared__ uint32_t hist_all[kTsWaves][256];
   __shared__ uint64_t small_all[kTsWaves][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -333,21 +338,38 @@ __global__ __launch_bounds__(kTsThreads) void ts_select_kernel(TokenSelectParams
   if (row >= R) return;  // whole waves
   const int npg = p.npg[row];
   if (npg == 0) return;
-  uint64_t* key = lds_keys + static_cast<size_t>(wave) * p.S * 128;
   uint32_t* hist = hist_all[wave];
   uint64_t* small = small_all[wave];
   const int C = npg * 128, K = p.K;
+  const int NI = C / 64;  // keys per lane (C is a multiple of 128)
   const uint64_t* src = p.keys + row * p.S * 128;
-  // C is a multiple of 128: 8 loads of a lane in flight together
-  for (int r0 = 0; r0 < C; r0 += 512) {
-    uint64_t t[8];
+  uint64_t kv[kRegs ? NK : 1];
+  uint64_t* key = lds_keys + (kRegs ? 0 : static_cast<size_t>(wave) * p.S * 128);
+  if constexpr (kRegs) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (r0 + 64 * i < C) t[i] = src[r0 + 64 * i + lane];
+    for (int i = 0; i < NK; ++i) kv[i] = i < NI ? src[64 * i + lane] : 0;
+  } else {
+    // 8 loads of a lane in flight together
+    for (int r0 = 0; r0 < C; r0 += 512) {
+      uint64_t t[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (r0 + 64 * i < C) key[r0 + 64 * i + lane] = t[i];
+      for (int i = 0; i < 8; ++i)
+        if (r0 + 64 * i < C) t[i] = src[r0 + 64 * i + lane];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (r0 + 64 * i < C) key[r0 + 64 * i + lane] = t[i];
+    }
   }
+  // f(i, key) for every key of the lane, i ascending
+  auto each = [&](auto&& f) {
+    if constexpr (kRegs) {
+#pragma unroll
+      for (int i = 0; i < NK; ++i)
+        if (i < NI) f(i, kv[i]);
+    } else {
+      for (int i = 0; i < NI; ++i) f(i, key[64 * i + lane]);
+    }
+  };
   const int cpg = p.pages[row * p.S + (lane < npg ? lane : 0)];  // page of slot `lane`
   __builtin_amdgcn_wave_barrier();
 
@@ -361,15 +383,21 @@ __global__ __launch_bounds__(kTsThreads) void ts_select_kernel(TokenSelectParams
 #pragma unroll
     for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0;
     __builtin_amdgcn_wave_barrier();
-    for (int r0 = 0; r0 < C; r0 += 512) {  // 8 reads of a lane before their atomics
-      uint64_t t[8];
+    auto count = [&](uint64_t kk) {
+      if (pass == 0 || (kk >> (shift + 8)) == prefix) atomicAdd(&hist[(kk >> shift) & 255], 1u);
+    };
+    if constexpr (kRegs) {
+      each([&](int, uint64_t kk) { count(kk); });
+    } else {
+      for (int r0 = 0; r0 < C; r0 += 512) {  // 8 reads of a lane before their atomics
+        uint64_t t[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (r0 + 64 * i < C) t[i] = key[r0 + 64 * i + lane];
+        for (int i = 0; i < 8; ++i)
+          if (r0 + 64 * i < C) t[i] = key[r0 + 64 * i + lane];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (r0 + 64 * i < C && (pass == 0 || (t[i] >> (shift + 8)) == prefix))
-          atomicAdd(&hist[(t[i] >> shift) & 255], 1u);
+        for (int i = 0; i < 8; ++i)
+          if (r0 + 64 * i < C) count(t[i]);
+      }
     }
     __builtin_amdgcn_wave_barrier();
     uint32_t cb[4], tot = 0;  // bins in descending order, 4 per lane
@@ -405,13 +433,12 @@ __global__ __launch_bounds__(kTsThreads) void ts_select_kernel(TokenSelectParams
   uint64_t T = prefix;
   if (bits < 64) {
     int m = 0;
-    for (int r0 = 0; r0 < C; r0 += 64) {  // C is a multiple of 128
-      const uint64_t kk = key[r0 + lane];
+    each([&](int, uint64_t kk) {
       const bool in = (kk >> (64 - bits)) == prefix;
       const uint64_t bl = __builtin_amdgcn_ballot_w64(in);
       if (in) small[m + rank_below(bl)] = kk;
       m += static_cast<int>(__popcll(bl));
-    }
+    });
     __builtin_amdgcn_wave_barrier();
     const uint64_t mine = lane < m ? small[lane] : 0;
     int gt = 0, ge = 0;
@@ -429,21 +456,20 @@ __global__ __launch_bounds__(kTsThreads) void ts_select_kernel(TokenSelectParams
   }
 
   // every key above T, and of those equal to T the first `need` in candidate
-  // order; written in candidate order (e = r0 + lane, r0 ascending)
+  // order; written in candidate order (e = 64 i + lane, i ascending)
   int32_t* trow = p.tok + row * K;
   int eqc = 0, at = 0;
-  for (int r0 = 0; r0 < C; r0 += 64) {
-    const int e = r0 + lane;
-    const uint64_t kk = key[e];
+  each([&](int i, uint64_t kk) {
+    const int e = 64 * i + lane;
     const bool eq = kk == T;
     const uint64_t be = __builtin_amdgcn_ballot_w64(eq);
     const bool sel = kk > T || (eq && eqc + rank_below(be) < need);
     const uint64_t bs = __builtin_amdgcn_ballot_w64(sel);
-    const int page = __builtin_amdgcn_readlane(cpg, r0 >> 7);  // 64 | 128: one page per r0
+    const int page = __builtin_amdgcn_readlane(cpg, i >> 1);  // 64 | 128: one page per i
     if (sel) trow[at + rank_below(bs)] = page * 128 + (e & 127);
     eqc += static_cast<int>(__popcll(be));
     at += static_cast<int>(__popcll(bs));
-  }
+  });
   if (lane == 0) p.tcnt[row] = K;
 }
 
@@ -474,10 +500,11 @@ hipError_t launch_token_select(const TokenSelectParams& p, hipStream_t stream) {
   e = p.D == 128 ? launch_kernel(ts_score_kernel<128>, dim3(static_cast<unsigned>(R)), dim3(kScThreads), 0, stream, p)
                  : launch_kernel(ts_score_kernel<64>, dim3(static_cast<unsigned>(R)), dim3(kScThreads), 0, stream, p);
   if (e != hipSuccess) return e;
+  if (p.S <= kRegSlots) return launch_kernel(ts_select_kernel<2 * kRegSlots>, dim3(wave_groups), dim3(kTsThreads), 0, stream, p);
   const size_t lds = sizeof(uint64_t) * 128 * static_cast<size_t>(p.S) * kTsWaves;
-  e = raise_lds_limit_once<ts_select_kernel>(static_cast<int>(sizeof(uint64_t) * 128 * kMaxSlots * kTsWaves));
+  e = raise_lds_limit_once<ts_select_kernel<0>>(static_cast<int>(sizeof(uint64_t) * 128 * kMaxSlots * kTsWaves));
   if (e != hipSuccess) return e;
-  return launch_kernel(ts_select_kernel, dim3(wave_groups), dim3(kTsThreads), lds, stream, p);
+  return launch_kernel(ts_select_kernel<0>, dim3(wave_groups), dim3(kTsThreads), lds, stream, p);
 }
 
 }  // namespace ssa
