@@ -111,7 +111,7 @@ struct TokenSelectParams {
   int32_t n_global, n_local, K;
   int32_t* tok;
   int32_t* tcnt;
-  int32_t* cnt;    // [R] recalls of page (b, h, c), then the fill cursor
+  int32_t* cnt;    // [R] recalls of page (b, h, c)
   int32_t* off;    // [R] bucket start of page (b, h, c) inside the (b, h) region of ent
   int32_t* npg;    // [R] candidate pages of row (b, h, qb); 0 once the row is final
   int32_t* pages;  // [R, S] ascending candidate pages

@@ -14,22 +14,20 @@
 // Page-major: a page is recalled by several query blocks (about M of them
 // on average), so scoring row by row would gather each recalled page once
 // per recalling block.  Instead the work is turned around:
-//   0. zero the per-page recall counters;
 //   1. rows: one wave per (b, head, query block) turns the page list into
 //      the ascending, duplicate-free candidate pages (at most top_m); a row
-//      with at most K candidate tokens (or K = 0) is written out here, the
-//      others count themselves into their pages' recall counters;
-//   2. offsets: one workgroup per (b, head) scans the counters into bucket
-//      offsets;
-//   3. fill: each open row appends (row, slot) to its pages' buckets (the
-//      order inside a bucket is free: every entry has its own output place);
-//   4. score: one workgroup per (b, head, page) loads the page's 128 key
+//      with at most K candidate tokens (or K = 0) is written out here;
+//   2. buckets: one workgroup per (b, head) counts the open rows' (row,
+//      slot) entries per page, scans the counts into bucket offsets and
+//      appends every entry to its page's bucket (the order inside a bucket
+//      is free: every entry has its own output place);
+//   3. score: one workgroup per (b, head, page) loads the page's 128 key
 //      rows once into registers (a row per lane, bf16) and takes the dot
 //      products with the query-block sums of up to 8 recalling rows at a
 //      time as fp64 FMAs on the vector units, the query-block sum reaching
 //      every lane through a row broadcast, writing order-preserving 64-bit
 //      keys (NaN counts as -inf, -0 as +0) into each recalling row's slot;
-//   5. select: one wave per open row finds the K-th largest key T exactly
+//   4. select: one wave per open row finds the K-th largest key T exactly
 //      by a radix select (LDS histograms, 8 bits a pass; once at most 64
 //      keys share the leading bits found so far, they are ranked by
 //      counting), keeps every key
@@ -76,11 +74,6 @@ __device__ __forceinline__ int block_excl_scan(int v, int32_t* wsum) {
   return at;
 }
 
-__global__ __launch_bounds__(kTsThreads) void ts_zero_kernel(int32_t* cnt, int64_t n) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kTsThreads + threadIdx.x;
-  if (i < n) cnt[i] = 0;
-}
-
 // 1. one wave per row (b, h, qb)
 __global__ __launch_bounds__(kTsThreads) void ts_rows_kernel(TokenSelectParams p) {
   __shared__ int32_t spg[kTsWaves][kMaxSlots];
@@ -89,7 +82,6 @@ __global__ __launch_bounds__(kTsThreads) void ts_rows_kernel(TokenSelectParams p
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kTsWaves + wave;
   if (row >= R) return;  // whole waves
   const int qb = static_cast<int>(row % p.nqb);
-  const int64_t bh = row / p.nqb;
   const int32_t* prow = p.pidx + row * p.PW;
   const int pc = min(max(p.pcnt[row], 0), p.PW);
   const int c = lane < pc ? prow[lane] : -1;
@@ -121,46 +113,67 @@ __global__ __launch_bounds__(kTsThreads) void ts_rows_kernel(TokenSelectParams p
     return;
   }
   if (lane == 0) p.npg[row] = npg;
-  if (keep) atomicAdd(&p.cnt[bh * p.nqb + c], 1);
 }
 
-// 2. one workgroup per (b, h): bucket offsets of its pages; counters reset
-// to serve as fill cursors
-__global__ __launch_bounds__(kTsThreads) void ts_offsets_kernel(TokenSelectParams p) {
-  __shared__ int32_t wsum[kTsWaves];
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * p.nqb;
-  int32_t* cnt = p.cnt + base;
-  int32_t* off = p.off + base;
-  const int per = (p.nqb + kTsThreads - 1) / kTsThreads;
-  const int c0 = min(static_cast<int>(threadIdx.x) * per, p.nqb), c1 = min(c0 + per, p.nqb);
-  int mine = 0;
-  for (int c = c0; c < c1; ++c) mine += cnt[c];
-  int at = block_excl_scan(mine, wsum);
-  for (int c = c0; c < c1; ++c) {
-    const int n = cnt[c];
-    off[c] = at;
-    at += n;
-    cnt[c] = 0;
+// 2. one workgroup per (b, h) builds the page buckets of its open rows:
+// counts the (row, slot) entries per page in LDS, scans the counts into
+// bucket offsets (written out with the counts for the score kernel), then
+// appends every entry qb * S + slot to its page's bucket through an LDS
+// cursor (the order inside a bucket is free: every entry has its own output
+// place).  Pages are taken kBkSeg at a time, so any nqb fits the LDS.
+constexpr int kBkThreads = 1024;
+constexpr int kBkSeg = 8192;
+
+__global__ __launch_bounds__(kBkThreads) void ts_buckets_kernel(TokenSelectParams p) {
+  __shared__ int32_t lc[kBkSeg];
+  __shared__ int32_t wsum[kBkThreads / 64];
+  __shared__ int32_t seg_end;
+  const int tid = threadIdx.x;
+  const int64_t rbase = static_cast<int64_t>(blockIdx.x) * p.nqb;  // first row (and page) of (b, h)
+  const int nent = p.nqb * p.S;
+  const int32_t* npg = p.npg + rbase;
+  const int32_t* pages = p.pages + rbase * p.S;
+  int32_t* ent = p.ent + rbase * p.S;
+  int base = 0;  // bucket offset of the segment's first page
+  for (int c0 = 0; c0 < p.nqb; c0 += kBkSeg) {
+    const int nc = min(kBkSeg, p.nqb - c0);
+    for (int c = tid; c < nc; c += kBkThreads) lc[c] = 0;
+    __syncthreads();
+    for (int i = tid; i < nent; i += kBkThreads) {
+      const int qb = i / p.S;
+      if (i - qb * p.S < npg[qb]) {
+        const int c = pages[i] - c0;
+        if (c >= 0 && c < nc) atomicAdd(&lc[c], 1);
+      }
+    }
+    __syncthreads();
+    const int per = (nc + kBkThreads - 1) / kBkThreads;  // a run of consecutive pages per thread
+    const int a0 = min(tid * per, nc), a1 = min(a0 + per, nc);
+    int mine = 0;
+    for (int c = a0; c < a1; ++c) mine += lc[c];
+    int at = base + block_excl_scan(mine, wsum);
+    for (int c = a0; c < a1; ++c) {
+      const int n = lc[c];
+      p.off[rbase + c0 + c] = at;
+      p.cnt[rbase + c0 + c] = n;
+      lc[c] = at;  // from here on the page's fill cursor
+      at += n;
+    }
+    if (tid == kBkThreads - 1) seg_end = at;
+    __syncthreads();
+    for (int i = tid; i < nent; i += kBkThreads) {
+      const int qb = i / p.S, slot = i - qb * p.S;
+      if (slot < npg[qb]) {
+        const int c = pages[i] - c0;
+        if (c >= 0 && c < nc) ent[atomicAdd(&lc[c], 1)] = qb * p.S + slot;
+      }
+    }
+    base = seg_end;
+    __syncthreads();  // lc and seg_end are reused by the next segment
   }
 }
 
-// 3. one wave per open row: (row, slot) into the bucket of each of its pages
-__global__ __launch_bounds__(kTsThreads) void ts_fill_kernel(TokenSelectParams p) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t R = static_cast<int64_t>(p.B) * p.Hq * p.nqb;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kTsWaves + wave;
-  if (row >= R) return;
-  const int npg = p.npg[row];
-  if (lane >= npg) return;
-  const int qb = static_cast<int>(row % p.nqb);
-  const int64_t bh = row / p.nqb;
-  const int c = p.pages[row * p.S + lane];
-  const int64_t pcix = bh * p.nqb + c;
-  const int pos = p.off[pcix] + atomicAdd(&p.cnt[pcix], 1);
-  p.ent[bh * p.nqb * p.S + pos] = qb * p.S + lane;
-}
-
-// 4. one workgroup of two waves per (b, h, page): lane l of wave w owns key
+// 3. one workgroup of two waves per (b, h, page): lane l of wave w owns key
 // row 64 w + l of the page.  On this chip fp64 FMAs on the vector units run
 // at the fp64 matrix rate, so the scores are plain dot products with no
 // padding of the recalling rows to a matrix tile (a page is recalled by ~8
@@ -321,7 +334,7 @@ __device__ __forceinline__ int rank_below(uint64_t b) {
                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u)));
 }
 
-// 5. one wave per open row, four rows per workgroup; everything stays inside
+// 4. one wave per open row, four rows per workgroup; everything stays inside
 // the wave (its own LDS regions, ballots and lane shuffles), so no workgroup
 // barrier is needed.  Candidate e = 64 i + lane of a row is lane's i-th key:
 // in registers when a row has at most NK * 64 candidates (NK > 0), else in
@@ -487,15 +500,10 @@ hipError_t launch_token_select(const TokenSelectParams& p, hipStream_t stream) {
   if (p.S < 0 || p.S > kMaxSlots) return hipErrorNotSupported;
   const int64_t R = static_cast<int64_t>(p.B) * p.Hq * p.nqb;
   const unsigned wave_groups = static_cast<unsigned>((R + kTsWaves - 1) / kTsWaves);
-  hipError_t e = launch_kernel(ts_zero_kernel, dim3(static_cast<unsigned>((R + kTsThreads - 1) / kTsThreads)),
-                               dim3(kTsThreads), 0, stream, p.cnt, R);
-  if (e != hipSuccess) return e;
-  e = launch_kernel(ts_rows_kernel, dim3(wave_groups), dim3(kTsThreads), 0, stream, p);
+  hipError_t e = launch_kernel(ts_rows_kernel, dim3(wave_groups), dim3(kTsThreads), 0, stream, p);
   if (e != hipSuccess) return e;
   if (p.K == 0 || p.S == 0) return hipSuccess;  // every row is final
-  e = launch_kernel(ts_offsets_kernel, dim3(static_cast<unsigned>(p.B * p.Hq)), dim3(kTsThreads), 0, stream, p);
-  if (e != hipSuccess) return e;
-  e = launch_kernel(ts_fill_kernel, dim3(wave_groups), dim3(kTsThreads), 0, stream, p);
+  e = launch_kernel(ts_buckets_kernel, dim3(static_cast<unsigned>(p.B * p.Hq)), dim3(kBkThreads), 0, stream, p);
   if (e != hipSuccess) return e;
   e = p.D == 128 ? launch_kernel(ts_score_kernel<128>, dim3(static_cast<unsigned>(R)), dim3(kScThreads), 0, stream, p)
                  : launch_kernel(ts_score_kernel<64>, dim3(static_cast<unsigned>(R)), dim3(kScThreads), 0, stream, p);
