@@ -97,8 +97,8 @@ __global__ __launch_bounds__(kSumThreads) void block_sums_kernel(PageSelectParam
 // row's 4 lanes read 64 contiguous bytes per load).  Each query block keeps
 // a sorted list of its best top_m pages across the lanes of one wave; a
 // chunk's candidate enters only if it beats the list's last entry (and, on a
-// row's first chunk, is no worse than the M-th best of the lanes' bests), by
-// an insertion at the rank a ballot gives.  "Beats" is a total order: higher
+// row's first chunk, is no worse than a lower bound on the chunk's M-th
+// best), by an insertion at the rank a ballot gives.  "Beats" is a total order: higher
 // score, equal scores -> lower page (a NaN score counts as -inf).
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 256;
@@ -209,9 +209,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(PageSelectParams p)
       double ts = read_lane_f64(ls[rr], M - 1);
       int tc = __builtin_amdgcn_readlane(li[rr], M - 1);
       // While the list is not full (a row's first chunk), bound the chunk's
-      // M-th best from below by the M-th best of the 64 per-lane bests: an
-      // item worse than that bar is beaten by M items of the chunk and can be
-      // skipped.  The bar comes from a bitonic sort across the lanes.
+      // M-th best from below: an item worse than that bar is beaten by M
+      // items of the chunk and can be skipped.
       double bs = -__builtin_inf();
       int bc = 0x7fffffff;
       if (tc == 0x7fffffff && M <= 8) {
@@ -235,6 +234,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(PageSelectParams p)
         bs = __builtin_fmin(__builtin_fmin(read_lane_f64(t2, 0), read_lane_f64(t2, 16)),
                             __builtin_fmin(read_lane_f64(t2, 32), read_lane_f64(t2, 48)));
       } else if (tc == 0x7fffffff) {
+        // more than 8 kept: the M-th best of the 64 per-lane bests, from a
+        // bitonic sort across the lanes
 #pragma unroll
         for (int k = 0; k < kChunk / 64; ++k) {
           const int c = cc + 64 * k + lane;
