@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kTsThreads) void ts_rows_kernel(TokenSelectParams p
 // cursor (the order inside a bucket is free: every entry has its own output
 // place).  Pages are taken kBkSeg at a time, so any nqb fits the LDS.
 constexpr int kBkThreads = 1024;
-constexpr int kBkSeg = 8192;
+constexpr int kBkSeg = 4096;
 
 __global__ __launch_bounds__(kBkThreads) void ts_buckets_kernel(TokenSelectParams p) {
   __shared__ int32_t lc[kBkSeg];

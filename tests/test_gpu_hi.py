@@ -61,6 +61,16 @@ def test_token_select_small(lib, L, Hq, Hkv, D, M, K):
     select_both(lib, q, k, qh, kh, M, K)
 
 
+def test_token_select_many_pages(lib):
+    """More pages per head than the bucket kernel counts in LDS at once
+    (4096): the buckets are built over several page segments."""
+    L, D, M, K = 128 * 4100 + 5, 64, 4, 256
+    qh, q = gen(63, synth.Q, 1, L, 1, D)
+    kh, k = gen(63, synth.K, 1, L, 1, D)
+    say(f"token_select L={L} (4101 query blocks) D={D} M={M} K={K}")
+    select_both(lib, q, k, qh, kh, M, K)
+
+
 def test_token_select_planted_and_ties(lib):
     """Keys planted along the query block's direction are the ones kept; an exact
     duplicate of the weakest planted key loses the tie to the lower token."""
