@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kSumThreads) void block_sums_kernel(PageSelectParam
 // ---------------------------------------------------------------------------
 // select: one workgroup of 4 waves per (b, query head, 16 query blocks).
 // Scores are a dense product: S[c][qb] = <ksum[c], qsum[qb]> over D
-// channels, taken 256 candidate pages at a time on v_mfma_f64_16x16x4_f64
+// channels, taken 128 candidate pages at a time on v_mfma_f64_16x16x4_f64
 // (16 candidates x 16 query blocks per tile; lane (n, g) feeds candidate /
 // query block n and channels 8m + 2g, 8m + 2g + 1 for m = 0 .. D/8-1, so a
 // row's 4 lanes read 64 contiguous bytes per load).  Each query block keeps
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kSumThreads) void block_sums_kernel(PageSelectParam
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 256;
 constexpr int kRows = 16;     // query blocks per workgroup
-constexpr int kChunk = 256;   // candidate pages scored per round
+constexpr int kChunk = 128;   // candidate pages scored per round
 constexpr int kPad = kChunk + 4;
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
@@ -138,7 +138,7 @@ __device__ __forceinline__ void top2_merge(double& t1, double& t2) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(PageSelectParams p) {
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(PageSelectParams p) {
   constexpr int NM = D / 8;  // 16-byte loads per operand row share; 2 MFMAs each
   __shared__ double sc[kRows][kPad];
 
@@ -159,14 +159,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(PageSelectParams p)
   const int qb_last = min(qb0 + kRows, p.nqb) - 1;
   const int ce = l_begin_of(qb_last);  // candidates of every row lie in [n_global, ce)
 
-  // B operand: query-block sums, lane (n, g) = query block qb0 + n
-  f64x2 qf[NM];
-  {
-    const int qrow = min(qb0 + n, p.nqb - 1);
+  // B operand: query-block sums of the 16 rows, staged in LDS (rows D + 2
+  // doubles apart: the 16 rows of a fragment read start 4 banks apart), read
+  // per product; lane (n, g) takes query block qb0 + n
+  __shared__ __attribute__((aligned(16))) double qsl[kRows][D + 2];
+  for (int i = threadIdx.x; i < kRows * D / 2; i += kSelThreads) {
+    const int r = i / (D / 2), c2 = i % (D / 2);
+    const int qrow = min(qb0 + r, p.nqb - 1);
     const double* qs = p.qsum + ((static_cast<int64_t>(b) * p.Hq + h) * p.nqb + qrow) * D;
-#pragma unroll
-    for (int m = 0; m < NM; ++m) qf[m] = *reinterpret_cast<const f64x2*>(qs + 8 * m + 2 * g);
+    *reinterpret_cast<f64x2*>(&qsl[r][2 * c2]) = *reinterpret_cast<const f64x2*>(qs + 2 * c2);
   }
+  __syncthreads();
+  const double* qrow_l = &qsl[n][2 * g];
   const double* kbase = p.ksum + (static_cast<int64_t>(b) * p.Hkv + hk) * p.nqb * D;
 
   // the rows of this wave: qb0 + wave + 4 rr; list entry i of a row on lane i
@@ -179,20 +183,31 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(PageSelectParams p)
   }
   const int M = p.top_m;
 
+  // A operand of this wave's next tile: its loads are issued while the
+  // previous tile's products run (each register reloaded once its product
+  // has read it), so a tile's L2 round trip hides behind the one before
+  f64x2 kf[NM];
+  auto load_tile = [&](int c0) {
+    const double* kr = kbase + static_cast<int64_t>(max(min(c0 + n, ce - 1), 0)) * D;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) kf[m] = *reinterpret_cast<const f64x2*>(kr + 8 * m + 2 * g);
+  };
+  load_tile(p.n_global + 16 * wave);
   for (int cc = p.n_global; cc < ce; cc += kChunk) {
     // scores of candidates cc .. cc+255 for the 16 query blocks
     for (int tt = wave; tt < kChunk / 16; tt += 4) {
       const int c0 = cc + tt * 16;
       if (c0 >= ce) break;
-      const double* kr = kbase + static_cast<int64_t>(min(c0 + n, ce - 1)) * D;
-      f64x2 kf[NM];
-#pragma unroll
-      for (int m = 0; m < NM; ++m) kf[m] = *reinterpret_cast<const f64x2*>(kr + 8 * m + 2 * g);
+      // this wave's next tile: 4 tiles on in this chunk, else its first of the next
+      const int nc0 = tt + 4 < kChunk / 16 ? c0 + 64 : cc + kChunk + 16 * wave;
+      const double* nkr = kbase + static_cast<int64_t>(max(min(nc0 + n, ce - 1), 0)) * D;
       f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(kf[m][0], qf[m][0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(kf[m][1], qf[m][1], acc, 0, 0, 0);
+        const f64x2 qv = *reinterpret_cast<const f64x2*>(qrow_l + 8 * m);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(kf[m][0], qv[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(kf[m][1], qv[1], acc, 0, 0, 0);
+        kf[m] = *reinterpret_cast<const f64x2*>(nkr + 8 * m + 2 * g);
       }
       // lane (n, g), register r holds candidate c0 + g + 4r of query block
       // qb0 + n (the f64 16x16 output puts row lane/16 + 4 r in register r)
