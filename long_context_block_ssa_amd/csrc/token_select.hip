@@ -274,9 +274,9 @@ __global__ __launch_bounds__(kScThreads) __attribute__((amdgpu_waves_per_eu(4)))
     const int my_ev = lane < ne ? eb[e0 + lane] : 0;
     const int my_qo = (my_ev / p.S) * D;
     // the batch's query-block sums into this wave's LDS rows (wave-local:
-    // the wave's own LDS accesses complete in order)
-    // (every row of the batch is loaded, past ne the first block's sums, so
-    // that all loads are in flight together)
+    // the wave's own LDS accesses complete in order); all kScEnt rows are
+    // loaded so that every load is in flight at once (rows past ne load
+    // query block 0's sums, unused)
     {
       constexpr int PL = (D + 127) / 128;  // 16-byte loads per lane and row
       f64x2 t[kScEnt][PL];
