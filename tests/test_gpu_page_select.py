@@ -24,7 +24,11 @@ def compare_lists(idx, cnt, qh, kh, top_m, ridx, rcnt, near, heads=None):
 
 
 @pytest.mark.parametrize("L,Hq,Hkv,D,M", [(128 * 40 + 17, 2, 1, 128, 8), (128 * 33, 2, 2, 64, 4),
-                                          (128 * 20, 1, 1, 128, 0), (2048, 2, 2, 128, 8)])
+                                          (128 * 20, 1, 1, 128, 0), (2048, 2, 2, 128, 8),
+                                          # several 128-page chunks; M = 1 and M = 8 take the DPP
+                                          # bar of a row's first chunk, M = 9, 16, 32 the bitonic one
+                                          (128 * 300 + 5, 2, 1, 128, 1), (128 * 300 + 5, 2, 1, 128, 9),
+                                          (128 * 300, 2, 2, 128, 16), (128 * 300, 1, 1, 64, 32)])
 def test_page_select_small(lib, L, Hq, Hkv, D, M):
     qh, q = gen(51, synth.Q, 1, L, Hq, D)
     kh, k = gen(51, synth.K, 1, L, Hkv, D)
