@@ -231,9 +231,8 @@ int ssa_decode(const ssa_decode_args* a, const ssa_window* win, void* stream);
 
 /* Bytes of workspace ssa_decode needs for these sizes and window, rounded up
  * to a multiple of 256: B * Hq * (n_global + n_local) * 2064 for Dqk = 576,
- * Dv = 512; B * Hq * ceil((n_global + n_local) / 4) * 520 for Dqk = Dv = 128
- * with 2 <= Hq/Hkv <= 16 and n_global + n_local > 4; otherwise 0.  Reads only
- * B, Hq, Hkv, Dqk, Dv and the window; 0 for NULL arguments. */
+ * Dv = 512; otherwise 0.  Reads only B, Hq, Dqk, Dv and the window; 0 for
+ * NULL arguments. */
 size_t ssa_decode_workspace_size(const ssa_decode_args* a, const ssa_window* win);
 
 /* ---------------------------------------------------------------------------

@@ -430,15 +430,6 @@ size_t ssa_decode_workspace_size(const ssa_decode_args* a, const ssa_window* win
   if (!a || !win || a->B < 1 || a->Hq < 1 || win->n_global < 0 || win->n_local < 0) return 0;
   const int width = win->n_global + win->n_local;
   if (a->Dqk == 576 && a->Dv == 512) return (ssa::decode_mla_workspace_bytes(a->B, a->Hq, width) + 255) / 256 * 256;
-  // grouped heads at d = 128 (the kernel's own test, on the same fields)
-  ssa::DecodeParams p{};
-  p.Hq = a->Hq;
-  p.Hkv = a->Hkv;
-  p.group = a->Hkv >= 1 && a->Hq % a->Hkv == 0 ? a->Hq / a->Hkv : 0;
-  p.n_global = win->n_global;
-  p.n_local = win->n_local;
-  if (ssa::decode_gqa_supports(p, a->Dqk, a->Dv))
-    return (ssa::decode_gqa_workspace_bytes(a->B, a->Hq, width) + 255) / 256 * 256;
   return 0;
 }
 

@@ -173,6 +173,7 @@ struct DecodeParams {
   float scale;
   float* work;  // Dqk = 576, and dense decode: per-(sequence, head, slot) partials
   int32_t nsplit;  // dense decode: block groups per sequence (the partials' slots)
+  int32_t head_splits;  // grouped heads: workgroups per (sequence, kv head), each a share of the query heads
 };
 
 struct PageSelectParams {
@@ -219,11 +220,9 @@ size_t prefill_backward_workspace_bytes(int32_t B, int32_t L, int32_t Hq, int32_
 
 hipError_t launch_decode(const DecodeParams& p, int dqk, int dv, hipStream_t stream);
 // d = 128 with 2..16 query heads per kv head: each K/V row read once for
-// all heads of its kv head.  A window of more than 4 blocks is split over
-// workgroups whose pieces go through p.work (decode_gqa_workspace_bytes) and
-// the dense decode's merge kernel.
+// all heads of its kv head (of a workgroup's share of them), a window of any
+// width in one workgroup, no workspace.
 bool decode_gqa_supports(const DecodeParams& p, int dqk, int dv);
-size_t decode_gqa_workspace_bytes(int32_t B, int32_t Hq, int32_t width);
 hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream);
 // merge p.nsplit pieces (o relative to m, m, l) per (sequence, head) of p.work
 hipError_t launch_decode_merge(const DecodeParams& p, int d, hipStream_t stream);
