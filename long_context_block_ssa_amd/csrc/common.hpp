@@ -224,7 +224,7 @@ hipError_t launch_decode(const DecodeParams& p, int dqk, int dv, hipStream_t str
 // width in one workgroup, no workspace.
 bool decode_gqa_supports(const DecodeParams& p, int dqk, int dv);
 hipError_t launch_decode_gqa(const DecodeParams& p, hipStream_t stream);
-// merge p.nsplit pieces (o relative to m, m, l) per (sequence, head) of p.work
+// merge p.nsplit pieces (o relative to m, m, l) per (sequence, head) of p.work (dense decode)
 hipError_t launch_decode_merge(const DecodeParams& p, int d, hipStream_t stream);
 
 // Dense decode (every cached key), MHA/GQA d = 64/128: nsplit groups of 16

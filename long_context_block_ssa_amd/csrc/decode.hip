@@ -271,8 +271,8 @@ __global__ __launch_bounds__(MAXT) __attribute__((amdgpu_waves_per_eu(4))) void 
   }
 }
 
-// Decode merge (the dense decode's block groups, the grouped-head decode's
-// window splits): one wave per (sequence, query head) combines the pieces, M = max m_s, o = sum o_s e^(m_s - M) / sum l_s e^(m_s - M)
+// Decode merge (the dense decode's block groups): one wave per (sequence,
+// query head) combines the pieces, M = max m_s, o = sum o_s e^(m_s - M) / sum l_s e^(m_s - M)
 // (the exact merge of max-subtracted softmax pieces, CSA/HCA tutorial page,
 // section 7.1); a NaN l in any group makes the row NaN.
 template <int D>
