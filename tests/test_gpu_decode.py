@@ -84,8 +84,8 @@ def test_decode_small_nan_poisoned(lib, D, Hq, Hkv):
                                          ((128, 0, 8), 128, 8, 2), ((128, 2, 10), 128, 8, 2)])
 def test_decode_other_windows(lib, win, D, Hq, Hkv):
     """Other window geometries; a 16-block window runs the 1024-thread
-    instantiation (one wave per block); grouped heads split a window of more
-    than 4 blocks over groups of 4 (12 blocks: 3 groups)."""
+    instantiation (one wave per block); grouped heads read a window of more
+    than 4 blocks in rounds of 4 (12 blocks: 3 rounds)."""
     lens = [1, 130, 700, 2048, 2049, 3001]
     w = oracle.Window(*win)
     dev, host = build_case(23, len(lens), Hq, Hkv, D, lens, head=win[1], tail=win[2])
@@ -102,6 +102,16 @@ def test_decode_cfg3_full(lib):
     lens = synth.decode_seq_lens(3, 64, 65536, 131072)
     dev, host = build_case(3, 64, 16, 16, 128, lens)
     run_and_check(lib, dev, host, 1 / math.sqrt(128), "cfg3 full")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv", [(32, 16, 8), (64, 12, 4)])
+def test_decode_gqa_one_workgroup_per_window(lib, B, Hq, Hkv):
+    """Grouped heads with B * Hkv >= 256 windows: one workgroup per window with
+    all of its query heads (fewer windows split the heads over two)."""
+    rng = np.random.default_rng(41)
+    lens = [int(x) for x in rng.integers(1, 6000, size=B)]
+    dev, host = build_case(41, B, Hq, Hkv, 128, lens)
+    run_and_check(lib, dev, host, 1 / math.sqrt(128), f"gqa {Hq}/{Hkv} B={B}")
 
 
 def test_decode_gqa_cfg3_full(lib):
