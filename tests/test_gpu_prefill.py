@@ -97,6 +97,27 @@ def test_ssa_prefill_other_windows(lib, win, D):
     check_close(to_f64(lse), rl, f"window {win} lse")
 
 
+@pytest.mark.parametrize("mode", ["dense", "window-2-14"])
+def test_f32_prefill_long_lists(lib, mode):
+    """fp32 at d = 64 with lists longer than the four waves of a workgroup
+    (each wave takes several key blocks before the merge): the dense layer,
+    and a 16-block window."""
+    B, L, H, D = 1, 128 * 20 + 77, 2, 64
+    qh, q = gen(17, synth.Q, B, L, H, D, "f32")
+    kh, k = gen(17, synth.K, B, L, H, D, "f32")
+    vh, v = gen(17, synth.V, B, L, H, D, "f32")
+    say(f"f32 prefill {mode}")
+    if mode == "dense":
+        o, lse = lib.dense_causal(q, k, v, with_lse=True)
+        ro, rl = oracle.dense_causal(qh.astype(np.float64), kh, vh, 1 / math.sqrt(D))
+    else:
+        o, lse = lib.ssa(q, k, v, window=lib.Window(128, 2, 14), with_lse=True)
+        ro, rl = oracle.ssa_attention(qh.astype(np.float64), kh, vh, 1 / math.sqrt(D), oracle.Window(128, 2, 14))
+    torch.cuda.synchronize()
+    check_close(to_f64(o), ro, f"f32 {mode} o")
+    check_close(to_f64(lse), rl, f"f32 {mode} lse")
+
+
 def test_dense_causal_parity_small(lib):
     B, L, Hq, Hkv, D = 1, 1500, 2, 1, 128
     qh, q = gen(5, synth.Q, B, L, Hq, D)
