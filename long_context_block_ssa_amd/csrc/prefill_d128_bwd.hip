@@ -388,14 +388,29 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p, int 
     }
   }
 
-  // stage s -> query head, first query row
-  auto stage_rows = [&](int s, int& hq, int& q0) {
-    const int ss = s < nst ? s : 0;  // past the end: stage 0 again (rows nobody reads)
-    const int gi = ss / (nq * 4);
-    const int qbi = (ss >> 2) % nq;
-    hq = hk * p.group + gi;
-    q0 = (q_begin + qbi) * kBlk + (ss & 3) * kSK;
+  // stage -> (query head of the group, query block, quarter), walked in stage
+  // order by two cursors (the stage being computed and the stage being
+  // loaded) instead of divided out per stage; past the last stage a cursor
+  // names stage 0 again (rows nobody reads)
+  struct Cursor {
+    int gi, qbi, qtr;
   };
+  auto advance = [&](Cursor& cu) {
+    if (++cu.qtr == 4) {
+      cu.qtr = 0;
+      if (++cu.qbi == nq) {
+        cu.qbi = 0;
+        ++cu.gi;
+      }
+    }
+  };
+  auto rows_of = [&](const Cursor& cu, int& hq, int& q0, int& qb) {
+    const bool past = cu.gi >= p.group;
+    hq = hk * p.group + (past ? 0 : cu.gi);
+    qb = q_begin + (past ? 0 : cu.qbi);
+    q0 = qb * kBlk + (past ? 0 : cu.qtr) * kSK;
+  };
+  Cursor cur_c = {0, 0, 0}, iss_c = {0, 0, 0};
 
   const int drow = 4 * wave + (lane >> 4);
   const int dunit = (lane & 15) ^ swz(drow);
@@ -427,9 +442,10 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p, int 
 #pragma unroll
     for (int i = 0; i < 16; ++i) dka[dt][i] = dva[dt][i] = 0.f;
 
-  auto issue = [&](int s, int slot) {
-    int hq, q0;
-    stage_rows(s, hq, q0);
+  auto issue = [&](int slot) {  // the stage under iss_c, which then moves on
+    int hq, q0, qbq;
+    rows_of(iss_c, hq, q0, qbq);
+    advance(iss_c);
     const __bf16* qs = static_cast<const __bf16*>(p.q) + b * p.qs_b + hq * p.qs_h;
     const __bf16* ds = static_cast<const __bf16*>(p.dout) + b * p.dos_b + hq * p.dos_h;
     SSA_LDS u32x4* qd = (SSA_LDS u32x4*)(ring) + slot * (kSlotBytes / 16) + wave * 64;
@@ -451,7 +467,8 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p, int 
       SSA_DMA(ds + r1 * p.dos_l + dunit * 8, dd + 256);
     }
     // the record: 16 lanes cover its 256 bytes, the other lanes repeat them
-    const float* rec = p.rec + (static_cast<int64_t>(b * p.Hq + hq) * (p.nqb * 4) + q0 / kSK) * kRec + (lane & 15) * 4;
+    static_assert(kSK == 32, "a record per 32 query rows");
+    const float* rec = p.rec + (static_cast<int64_t>(b * p.Hq + hq) * (p.nqb * 4) + (q0 >> 5)) * kRec + (lane & 15) * 4;
     SSA_DMA(rec, rd);
   };
 
@@ -459,12 +476,13 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p, int 
     constexpr int SLOT = decltype(slot_tag)::value;
     constexpr bool STEADY = decltype(steady_tag)::value;  // ns < nst is known
     constexpr int OFF = SLOT * kSlotBytes;
-    int hq, q0;
-    stage_rows(s, hq, q0);
-    const int qb = q0 / kBlk;
+    int hq, q0, qb;
+    rows_of(cur_c, hq, q0, qb);
+    advance(cur_c);
+    (void)hq;
     // nothing to do: no query of the stage reaches this wave's keys, or they do not exist
     const bool need = q0 < L && wave_keys && !(qb == kb && q0 + kSK - 1 < kb * kBlk + wave * 32);
-    if (STEADY || ns < nst) issue(ns, nslot);
+    if (STEADY || ns < nst) issue(nslot);
     if (!need) return;
     // S = Q K^T and dP = dO V^T: 32 queries x this wave's 32 keys, one key per lane
     f32x16 sc, dp;
@@ -547,7 +565,10 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p, int 
   };
 
 #pragma unroll
-  for (int i = 0; i < kSlots - 1; ++i) issue(i, i);
+  for (int i = 0; i < kSlots - 1; ++i) {
+    if (i >= nst) iss_c = Cursor{p.group, 0, 0};  // past the end: stage 0's rows again
+    issue(i);
+  }
   wait_stages5(kSlots - 2);
   stage_barrier();
   const int nst_pad = (nst + kSlots - 1) & ~(kSlots - 1);
