@@ -10,13 +10,13 @@
 //   dQ = scale dS K,   dK = scale dS^T Q.
 //
 // Kernels (one stream, in this order):
-//   - records: per (b, head, 32-row stage) a 64-float record: the stage's
-//     lse * log2(e), then its delta (rows past L: 0);
 //   - dq: one workgroup per (query block, b, head), laid out like the
 //     forward: the window's K and V stream through the LDS ring, S^T = K Q^T
 //     and dP^T = V dO^T on 32x32x16 MFMAs with Q and dO in registers (one
 //     query per lane), dQ^T += K^T dS^T with K^T read transposed
-//     (ds_read_b64_tr_b16);
+//     (ds_read_b64_tr_b16).  First it writes its rows' records: per (b,
+//     head, 32-row stage) 64 floats, the stage's lse * log2(e), then its
+//     delta (rows past L: 0);
 //   - dkdv: one workgroup per (key block, b, kv head) for the local blocks
 //     and per (global block, part of its readers, b, kv head): each wave
 //     keeps its 32 keys' K and V rows in registers, and the query stages
@@ -79,44 +79,6 @@ __device__ __forceinline__ void lds_read_rec(uint32_t a, f32x4 (&ls)[4], f32x4 (
 
 #define SSA_DMA(src, dst) \
   __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(src), (SSA_LDS void*)(dst), 16, 0, 0)
-
-// ---------------------------------------------------------------------------
-// records: one 16-lane group per (b, head, row < nqb*128), 8 channels a lane
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_records_kernel(BwdParams p) {
-  const int64_t Lp = static_cast<int64_t>(p.nqb) * kBlk;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);  // (b*Hq + h) * Lp + i
-  const int c = threadIdx.x & 15;
-  if (gid >= static_cast<int64_t>(p.B) * p.Hq * Lp) return;  // whole 16-lane groups
-  const int i = static_cast<int>(gid % Lp);
-  const int64_t bh = gid / Lp;
-  const int h = static_cast<int>(bh % p.Hq), b = static_cast<int>(bh / p.Hq);
-  float acc = 0.f, lse2 = 0.f;
-  if (i < p.L) {
-    const u32x4 ov = *reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.o) + b * p.os_b +
-                                                     static_cast<int64_t>(i) * p.os_l + h * p.os_h + c * 8);
-    const u32x4 dv = *reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.dout) + b * p.dos_b +
-                                                     static_cast<int64_t>(i) * p.dos_l + h * p.dos_h + c * 8);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      acc = __builtin_fmaf(__builtin_bit_cast(float, ov[w] << 16), __builtin_bit_cast(float, dv[w] << 16), acc);
-      acc = __builtin_fmaf(__builtin_bit_cast(float, ov[w] & 0xFFFF0000u), __builtin_bit_cast(float, dv[w] & 0xFFFF0000u),
-                           acc);
-    }
-    const float l = p.lse[bh * p.L + i];
-    // a row that admitted no key (lse = -inf) must give P = 0
-    lse2 = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e;
-  }
-  acc += __shfl_xor(acc, 8);
-  acc += __shfl_xor(acc, 4);
-  acc += __shfl_xor(acc, 2);
-  acc += __shfl_xor(acc, 1);
-  if (c == 0) {
-    float* r = p.rec + (bh * (p.nqb * 4) + i / kSK) * kRec;
-    r[i % kSK] = lse2;
-    r[kSK + i % kSK] = acc;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // dq: one workgroup per (query block, b, head), 4 waves x 32 queries
@@ -189,11 +151,35 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     qf[c] = __builtin_bit_cast(bf16x8, a);
     dof[c] = __builtin_bit_cast(bf16x8, d);
   }
+  // the row's record: lse * log2 e and delta = rowsum(dO * O) (this lane's 64
+  // channels, then its partner's 32 lanes away); written for the dk/dv kernel
+  // (rows past L: zeros; a row that admitted no key, lse = -inf, must give
+  // P = 0)
   float lse2 = 0.f, delta = 0.f;
-  if (row < L) {
-    const float* rec = p.rec + (static_cast<int64_t>(bh) * (p.nqb * 4) + row / kSK) * kRec;
-    lse2 = rec[row % kSK];
-    delta = rec[kSK + row % kSK];
+  {
+    float part = 0.f;
+    if (row < L) {
+      const __bf16* orow = static_cast<const __bf16*>(p.o) + b * p.os_b + h * p.os_h + static_cast<int64_t>(row) * p.os_l;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const u32x4 ov = *reinterpret_cast<const u32x4*>(orow + c * 16 + h32 * 8);
+        const u32x4 dv = __builtin_bit_cast(u32x4, dof[c]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          part = __builtin_fmaf(__builtin_bit_cast(float, ov[w] << 16), __builtin_bit_cast(float, dv[w] << 16), part);
+          part = __builtin_fmaf(__builtin_bit_cast(float, ov[w] & 0xFFFF0000u), __builtin_bit_cast(float, dv[w] & 0xFFFF0000u),
+                                part);
+        }
+      }
+      const float l = p.lse[static_cast<int64_t>(bh) * L + row];
+      lse2 = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e;
+    }
+    delta = part + __shfl_xor(part, 32);
+    if (h32 == 0) {
+      float* rec = p.rec + (static_cast<int64_t>(bh) * (p.nqb * 4) + row / kSK) * kRec;
+      rec[row % kSK] = lse2;
+      rec[kSK + row % kSK] = delta;
+    }
   }
   f32x16 acc[4];
 #pragma unroll
@@ -665,12 +651,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int n_glob
 
 template <typename GradT>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
-  const int64_t Lp = static_cast<int64_t>(p.nqb) * kBlk;
-  const int64_t rows = static_cast<int64_t>(p.B) * p.Hq * Lp;
-  hipError_t e = launch_kernel(bwd_records_kernel, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, stream, p);
-  if (e != hipSuccess) return e;
-  e = launch_kernel(bwd_dq_kernel<GradT>, dim3(static_cast<unsigned>(p.nqb) * p.B * p.Hq), dim3(kWaves * 64), 0, stream,
-                    p);
+  hipError_t e = launch_kernel(bwd_dq_kernel<GradT>, dim3(static_cast<unsigned>(p.nqb) * p.B * p.Hq),
+                               dim3(kWaves * 64), 0, stream, p);
   if (e != hipSuccess) return e;
   const int n_glob = min(p.n_global, p.nqb);
   const unsigned bh = static_cast<unsigned>(p.B) * p.Hkv;
