@@ -40,9 +40,14 @@ COMMON_FLAGS = [
 
 # Per-file additions.  prefill_d128.hip: no NaN can reach its max reductions
 # (rows past L are clamped to real data, masked scores are -inf), so the
-# compiler need not quiet NaN inputs before each v_max.
+# compiler need not quiet NaN inputs before each v_max.  prefill_d128_bwd.hip:
+# the dk/dv kernel needs more than 256 registers, and the compiler would then
+# put every MFMA accumulator in AGPRs, so the score and dP tiles that the
+# vector code reads would be copied out each stage; the VGPR form keeps those
+# in VGPRs and leaves the dK/dV accumulators in AGPRs.
 FILE_FLAGS = {
     "prefill_d128.hip": ["-fno-honor-nans"],
+    "prefill_d128_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

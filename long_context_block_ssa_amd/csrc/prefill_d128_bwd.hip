@@ -374,29 +374,22 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p, int 
     }
   }
 
-  // stage -> (query head of the group, query block, quarter), walked in stage
-  // order by two cursors (the stage being computed and the stage being
-  // loaded) instead of divided out per stage; past the last stage a cursor
-  // names stage 0 again (rows nobody reads)
+  // stage -> (query head of the group, first query row): the rows of a head's
+  // stages run from q_begin*128 to q_end*128 in steps of 32 and the heads
+  // follow in order, so two cursors (the stage being computed, the stage
+  // being loaded) walk them with an add
   struct Cursor {
-    int gi, qbi, qtr;
+    int gi, q0;
   };
-  auto advance = [&](Cursor& cu) {
-    if (++cu.qtr == 4) {
-      cu.qtr = 0;
-      if (++cu.qbi == nq) {
-        cu.qbi = 0;
-        ++cu.gi;
-      }
-    }
+  const int row_begin = q_begin * kBlk, row_end = q_end * kBlk;
+  auto advance = [&](Cursor& cu) -> bool {  // true when the head changes
+    cu.q0 += kSK;
+    if (cu.q0 != row_end) return false;
+    cu.q0 = row_begin;
+    ++cu.gi;
+    return true;
   };
-  auto rows_of = [&](const Cursor& cu, int& hq, int& q0, int& qb) {
-    const bool past = cu.gi >= p.group;
-    hq = hk * p.group + (past ? 0 : cu.gi);
-    qb = q_begin + (past ? 0 : cu.qbi);
-    q0 = qb * kBlk + (past ? 0 : cu.qtr) * kSK;
-  };
-  Cursor cur_c = {0, 0, 0}, iss_c = {0, 0, 0};
+  Cursor cur_c = {0, row_begin}, iss_c = {0, row_begin};
 
   const int drow = 4 * wave + (lane >> 4);
   const int dunit = (lane & 15) ^ swz(drow);
@@ -428,44 +421,55 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p, int 
 #pragma unroll
     for (int i = 0; i < 16; ++i) dka[dt][i] = dva[dt][i] = 0.f;
 
+  // the loaded stage's Q and dO row pointers and its record, moved with iss_c
+  const __bf16 *iss_q, *iss_d;
+  const float* iss_r;
+  auto point = [&]() {  // past the last head (never loaded): the first head's rows
+    const int hq = hk * p.group + (iss_c.gi >= p.group ? 0 : iss_c.gi);
+    const int q0 = iss_c.q0;
+    iss_q = static_cast<const __bf16*>(p.q) + b * p.qs_b + hq * p.qs_h + static_cast<int64_t>(q0) * p.qs_l;
+    iss_d = static_cast<const __bf16*>(p.dout) + b * p.dos_b + hq * p.dos_h + static_cast<int64_t>(q0) * p.dos_l;
+    static_assert(kSK == 32, "a record per 32 query rows");
+    iss_r = p.rec + (static_cast<int64_t>(b * p.Hq + hq) * (p.nqb * 4) + (q0 >> 5)) * kRec;
+  };
+  point();
+  const int64_t qstep = static_cast<int64_t>(kSK) * p.qs_l, dstep = static_cast<int64_t>(kSK) * p.dos_l;
+
   auto issue = [&](int slot) {  // the stage under iss_c, which then moves on
-    int hq, q0, qbq;
-    rows_of(iss_c, hq, q0, qbq);
-    advance(iss_c);
-    const __bf16* qs = static_cast<const __bf16*>(p.q) + b * p.qs_b + hq * p.qs_h;
-    const __bf16* ds = static_cast<const __bf16*>(p.dout) + b * p.dos_b + hq * p.dos_h;
+    const int q0 = iss_c.q0;
     SSA_LDS u32x4* qd = (SSA_LDS u32x4*)(ring) + slot * (kSlotBytes / 16) + wave * 64;
     SSA_LDS u32x4* dd = qd + kSlab;
     SSA_LDS u32x4* rd = (SSA_LDS u32x4*)(ring) + (kRingBytes + (slot * kWaves + wave) * kRecRegion) / 16;
     if (q0 + kSK <= L) {
-      const __bf16* a = qs + static_cast<int64_t>(q0) * p.qs_l + qoffs;
-      const __bf16* d = ds + static_cast<int64_t>(q0) * p.dos_l + dooffs;
-      SSA_DMA(a, qd);
-      SSA_DMA(a + q16, qd + 256);
-      SSA_DMA(d, dd);
-      SSA_DMA(d + do16, dd + 256);
+      SSA_DMA(iss_q + qoffs, qd);
+      SSA_DMA(iss_q + qoffs + q16, qd + 256);
+      SSA_DMA(iss_d + dooffs, dd);
+      SSA_DMA(iss_d + dooffs + do16, dd + 256);
     } else {
       // rows at or past L repeat row L-1 (finite, masked later)
-      const int64_t r0 = min(q0 + drow, L - 1), r1 = min(q0 + drow + 16, L - 1);
-      SSA_DMA(qs + r0 * p.qs_l + dunit * 8, qd);
-      SSA_DMA(qs + r1 * p.qs_l + dunit * 8, qd + 256);
-      SSA_DMA(ds + r0 * p.dos_l + dunit * 8, dd);
-      SSA_DMA(ds + r1 * p.dos_l + dunit * 8, dd + 256);
+      const int64_t r0 = min(drow, L - 1 - q0), r1 = min(drow + 16, L - 1 - q0);
+      SSA_DMA(iss_q + r0 * p.qs_l + dunit * 8, qd);
+      SSA_DMA(iss_q + r1 * p.qs_l + dunit * 8, qd + 256);
+      SSA_DMA(iss_d + r0 * p.dos_l + dunit * 8, dd);
+      SSA_DMA(iss_d + r1 * p.dos_l + dunit * 8, dd + 256);
     }
     // the record: 16 lanes cover its 256 bytes, the other lanes repeat them
-    static_assert(kSK == 32, "a record per 32 query rows");
-    const float* rec = p.rec + (static_cast<int64_t>(b * p.Hq + hq) * (p.nqb * 4) + (q0 >> 5)) * kRec + (lane & 15) * 4;
-    SSA_DMA(rec, rd);
+    SSA_DMA(iss_r + (lane & 15) * 4, rd);
+    if (advance(iss_c)) {
+      point();
+    } else {
+      iss_q += qstep;
+      iss_d += dstep;
+      iss_r += kRec;
+    }
   };
 
   auto stage = [&](auto slot_tag, auto steady_tag, int s, int ns, int nslot) {
     constexpr int SLOT = decltype(slot_tag)::value;
     constexpr bool STEADY = decltype(steady_tag)::value;  // ns < nst is known
     constexpr int OFF = SLOT * kSlotBytes;
-    int hq, q0, qb;
-    rows_of(cur_c, hq, q0, qb);
+    const int q0 = cur_c.q0, qb = q0 >> 7;
     advance(cur_c);
-    (void)hq;
     // nothing to do: no query of the stage reaches this wave's keys, or they do not exist
     const bool need = q0 < L && wave_keys && !(qb == kb && q0 + kSK - 1 < kb * kBlk + wave * 32);
     if (STEADY || ns < nst) issue(nslot);
@@ -552,7 +556,7 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p, int 
 
 #pragma unroll
   for (int i = 0; i < kSlots - 1; ++i) {
-    if (i >= nst) iss_c = Cursor{p.group, 0, 0};  // past the end: stage 0's rows again
+    static_assert(kSlots - 1 <= kBlk / kSK, "the prologue's stages exist (nst >= 4)");
     issue(i);
   }
   wait_stages5(kSlots - 2);
