@@ -23,7 +23,8 @@ The headline value is the SSA prefill throughput (algorithmic TFLOP/s: 4*d per
 (algorithmic bytes: every admitted key and value row once, plus q and o) at
 the ~128K-context decode workload is reported beside it, each with its
 fraction of the MI355X peak (bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s).  Kernel
-times come from HIP events recorded on the stream the kernels run on.
+times come from HIP timing events (no system-scope fence on completion)
+recorded on the stream the kernels run on.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
     python bench.py --zigzag     # f4: dense/SSA layer-stack prefill timing at 128K and 256K
@@ -50,6 +51,59 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_TFLOPS = 157.3
 PEAK_FP64_TFLOPS = 78.6
+
+
+class TimingEvent:
+    """A HIP event used only for timing, recorded on torch's current stream (the
+    stream the library's kernels are launched on).  It is created with
+    hipEventDisableSystemFence: a default event performs a system-scope memory
+    fence when it completes (cache writeback and invalidation), which puts
+    several microseconds between the kernels on either side of it; a timing
+    event needs none.  The calls go to the HIP runtime torch has loaded (found
+    in the process's memory map), so that its stream handles are valid."""
+
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+    _hip = None
+
+    @classmethod
+    def _runtime(cls):
+        if cls._hip is None:
+            import ctypes
+            with open("/proc/self/maps") as f:
+                paths = {line.split()[-1] for line in f if "libamdhip64.so" in line}
+            if len(paths) != 1:
+                raise RuntimeError(f"expected one loaded HIP runtime, found {sorted(paths)}")
+            cls._hip = ctypes.CDLL(paths.pop())
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._c = ctypes
+        hip = self._runtime()
+        self.ev = ctypes.c_void_p()
+        self._check(hip.hipEventCreateWithFlags(ctypes.byref(self.ev), ctypes.c_uint(self.FLAGS)), "create")
+
+    @staticmethod
+    def _check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"hipEvent {what} failed: error {rc}")
+
+    def record(self):
+        import torch
+        stream = self._c.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self._check(self._hip.hipEventRecord(self.ev, stream), "record")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end` (waits for `end`)."""
+        self._check(self._hip.hipEventSynchronize(end.ev), "synchronize")
+        ms = self._c.c_float()
+        self._check(self._hip.hipEventElapsedTime(self._c.byref(ms), self.ev, end.ev), "elapsed time")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
+
 
 # ----------------------------------------------------------------------------
 # workload sizes and algorithmic work (closed forms of the window)
@@ -918,7 +972,7 @@ def main():
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(nev)] for _ in range(args.steps)]
     print("[bench] timing", flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
