@@ -5,6 +5,8 @@
 
 #include "common.hpp"
 
+#include <utility>
+
 namespace ssa {
 namespace d128 {
 
@@ -40,6 +42,16 @@ __device__ __forceinline__ float pair_max(float x) {
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// f(integral_constant<int, k>) for k = 0 .. N-1, unrolled
+template <typename F, int... K>
+__device__ __forceinline__ void for_each_stage(F&& f, std::integer_sequence<int, K...>) {
+  (f(std::integral_constant<int, K>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void for_each_stage(F&& f) {
+  for_each_stage(f, std::make_integer_sequence<int, N>{});
 }
 
 // vmcnt(4 k) alone (expcnt and lgkmcnt left at their maximum): all but this

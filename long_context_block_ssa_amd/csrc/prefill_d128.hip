@@ -250,7 +250,14 @@ void prefill_d128_kernel(KernelParams<PAGED, TOKENS> p) {
   f32x16 acc[4];
 
   // ---- staging: this wave's four loads of stage s into ring slot `slot` ---
-  auto issue = [&](int s, int slot) {
+  // Stages are issued in order and QTR = s mod 4 is known where they are
+  // issued, so (non-paged) the first row of a block's K and V is found once,
+  // at its quarter 0, and stepped by 32 rows for the other three.
+  const __bf16 *iss_k = kbase, *iss_v = vbase;
+  int iss_key0 = 0;
+  const int64_t k32 = kSK * p.ks_l, v32 = kSK * p.vs_l;
+  auto issue = [&](auto qtr_tag, int s, int slot) {
+    constexpr int QTR = decltype(qtr_tag)::value;
     SSA_LDS u32x4* kd = (SSA_LDS u32x4*)(ring) + slot * (kSlotBytes / 16) + wave * 64;
     SSA_LDS u32x4* vd = kd + kSlab;
 #define SSA_DMA(src, dst) \
@@ -291,22 +298,28 @@ void prefill_d128_kernel(KernelParams<PAGED, TOKENS> p) {
           return;
         }
       }
-      const int kb = max(stage_block(s), 0);  // skipped entries stage block 0 (unused)
-      const int key0 = kb * kBlk + (s & 3) * kSK;
-      if (key0 + kSK <= p.L) {
-        const __bf16* ks = kbase + static_cast<int64_t>(key0) * p.ks_l + koff;
-        const __bf16* vs = vbase + static_cast<int64_t>(key0) * p.vs_l + voff;
-        SSA_DMA(ks, kd);
-        SSA_DMA(ks + k16, kd + 256);
-        SSA_DMA(vs, vd);
-        SSA_DMA(vs + v16, vd + 256);
+      if constexpr (QTR == 0 || DENSE) {  // (the dense layer: no registers to spare)
+        const int kb = max(stage_block(s), 0);  // skipped entries stage block 0 (unused)
+        iss_key0 = kb * kBlk + QTR * kSK;
+        iss_k = kbase + static_cast<int64_t>(iss_key0) * p.ks_l;
+        iss_v = vbase + static_cast<int64_t>(iss_key0) * p.vs_l;
+      } else {
+        iss_key0 += kSK;
+        iss_k += k32;
+        iss_v += v32;
+      }
+      if (iss_key0 + kSK <= p.L) {
+        SSA_DMA(iss_k + koff, kd);
+        SSA_DMA(iss_k + koff + k16, kd + 256);
+        SSA_DMA(iss_v + voff, vd);
+        SSA_DMA(iss_v + voff + v16, vd + 256);
       } else {
         // last block of a ragged L: rows at or past L repeat row L-1 (finite, masked later)
-        const int64_t r0 = min(key0 + drow, p.L - 1), r1 = min(key0 + drow + 16, p.L - 1);
-        SSA_DMA(kbase + r0 * p.ks_l + dunit * 8, kd);
-        SSA_DMA(kbase + r1 * p.ks_l + dunit * 8, kd + 256);
-        SSA_DMA(vbase + r0 * p.vs_l + dunit * 8, vd);
-        SSA_DMA(vbase + r1 * p.vs_l + dunit * 8, vd + 256);
+        const int64_t r0 = min(drow, p.L - 1 - iss_key0), r1 = min(drow + 16, p.L - 1 - iss_key0);
+        SSA_DMA(iss_k + r0 * p.ks_l + dunit * 8, kd);
+        SSA_DMA(iss_k + r1 * p.ks_l + dunit * 8, kd + 256);
+        SSA_DMA(iss_v + r0 * p.vs_l + dunit * 8, vd);
+        SSA_DMA(iss_v + r1 * p.vs_l + dunit * 8, vd + 256);
       }
     }
 #undef SSA_DMA
@@ -323,7 +336,7 @@ void prefill_d128_kernel(KernelParams<PAGED, TOKENS> p) {
     const int sub = s & 3;
     const int key0 = kb * kBlk + sub * kSK;
     const bool need = tst || (kb >= 0 && key0 < L && !(kb == qb && sub * kSK > qoff + 31));
-    if (STEADY || ns < nst) issue(ns, nslot);
+    if (STEADY || ns < nst) issue(std::integral_constant<int, (SLOT + kSlots - 1) % kSlots>{}, ns, nslot);
     if (!need) return;
     // S^T = K Q^T: 32 keys x 32 queries
     f32x16 sc;
@@ -416,8 +429,7 @@ void prefill_d128_kernel(KernelParams<PAGED, TOKENS> p) {
     // exist (a stage past the end stages rows of block 0 into a slot nobody
     // reads), so the number of loads behind the queries is fixed and the
     // compiler's wait for them is exact.
-#pragma unroll
-    for (int i = 0; i < kSlots - 1; ++i) issue(i, i);
+    for_each_stage<kSlots - 1>([&](auto i) { issue(i, decltype(i)::value, decltype(i)::value); });
     wait_stages(kSlots - 2);  // stage 0
     stage_barrier();
     // Whole groups of 4 stages, so that the loop is left only at its end;
