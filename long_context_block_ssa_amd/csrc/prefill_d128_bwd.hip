@@ -187,24 +187,36 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
-  auto issue = [&](int s, int slot) {
-    const int kb = max(stage_block(s), 0);  // past the end: rows of block 0 nobody reads
-    const int key0 = kb * kBlk + (s & 3) * kSK;
+  // stages are issued in order with QTR = s mod 4 known: a block's first K
+  // and V rows are found at its quarter 0 and stepped by 32 rows after that
+  const __bf16 *iss_k = kbase, *iss_v = vbase;
+  int iss_key0 = 0;
+  const int64_t k32 = kSK * p.ks_l, v32 = kSK * p.vs_l;
+  auto issue = [&](auto qtr_tag, int s, int slot) {
+    constexpr int QTR = decltype(qtr_tag)::value;
+    if constexpr (QTR == 0) {
+      const int kb = max(stage_block(s), 0);  // past the end: rows of block 0 nobody reads
+      iss_key0 = kb * kBlk;
+      iss_k = kbase + static_cast<int64_t>(iss_key0) * p.ks_l;
+      iss_v = vbase + static_cast<int64_t>(iss_key0) * p.vs_l;
+    } else {
+      iss_key0 += kSK;
+      iss_k += k32;
+      iss_v += v32;
+    }
     SSA_LDS u32x4* kd = (SSA_LDS u32x4*)(ring) + slot * (kSlotBytes / 16) + wave * 64;
     SSA_LDS u32x4* vd = kd + kSlab;
-    if (key0 + kSK <= L) {
-      const __bf16* ks = kbase + static_cast<int64_t>(key0) * p.ks_l + koff;
-      const __bf16* vs = vbase + static_cast<int64_t>(key0) * p.vs_l + voff;
-      SSA_DMA(ks, kd);
-      SSA_DMA(ks + k16, kd + 256);
-      SSA_DMA(vs, vd);
-      SSA_DMA(vs + v16, vd + 256);
+    if (iss_key0 + kSK <= L) {
+      SSA_DMA(iss_k + koff, kd);
+      SSA_DMA(iss_k + koff + k16, kd + 256);
+      SSA_DMA(iss_v + voff, vd);
+      SSA_DMA(iss_v + voff + v16, vd + 256);
     } else {
-      const int64_t r0 = min(key0 + drow, L - 1), r1 = min(key0 + drow + 16, L - 1);
-      SSA_DMA(kbase + r0 * p.ks_l + dunit * 8, kd);
-      SSA_DMA(kbase + r1 * p.ks_l + dunit * 8, kd + 256);
-      SSA_DMA(vbase + r0 * p.vs_l + dunit * 8, vd);
-      SSA_DMA(vbase + r1 * p.vs_l + dunit * 8, vd + 256);
+      const int64_t r0 = min(drow, L - 1 - iss_key0), r1 = min(drow + 16, L - 1 - iss_key0);
+      SSA_DMA(iss_k + r0 * p.ks_l + dunit * 8, kd);
+      SSA_DMA(iss_k + r1 * p.ks_l + dunit * 8, kd + 256);
+      SSA_DMA(iss_v + r0 * p.vs_l + dunit * 8, vd);
+      SSA_DMA(iss_v + r1 * p.vs_l + dunit * 8, vd + 256);
     }
   };
 
@@ -216,7 +228,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     const int sub = s & 3;
     const int key0 = kb * kBlk + sub * kSK;
     const bool need = kb >= 0 && key0 < L && !(kb == qb && sub * kSK > qoff + 31);
-    if (STEADY || ns < nst) issue(ns, nslot);
+    if (STEADY || ns < nst) issue(std::integral_constant<int, (SLOT + kSlots - 1) % kSlots>{}, ns, nslot);
     if (!need) return;
     f32x16 sc, dp;
 #pragma unroll
@@ -275,8 +287,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     stage_barrier();
   };
 
-#pragma unroll
-  for (int i = 0; i < kSlots - 1; ++i) issue(i, i);
+  for_each_stage<kSlots - 1>([&](auto i) { issue(i, decltype(i)::value, decltype(i)::value); });
   wait_stages(kSlots - 2);
   stage_barrier();
   const int nst_pad = (nst + kSlots - 1) & ~(kSlots - 1);
