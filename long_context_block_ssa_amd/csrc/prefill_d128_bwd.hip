@@ -16,7 +16,7 @@
 //     query per lane), dQ^T += K^T dS^T with K^T read transposed
 //     (ds_read_b64_tr_b16).  First it writes its rows' records: per (b,
 //     head, 32-row stage) 64 floats, the stage's lse * log2(e), then its
-//     delta (rows past L: 0);
+//     -delta (rows past L: 0);
 //   - dkdv: one workgroup per (key block, b, kv head) for the local blocks
 //     and per (global block, part of its readers, b, kv head): each wave
 //     keeps its 32 keys' K and V rows in registers, and the query stages
@@ -54,7 +54,7 @@ __device__ __forceinline__ void wait_stages5(int k) {
     __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-// the stage record's lse*log2(e) and delta of the 16 query rows a lane holds
+// the stage record's lse*log2(e) and -delta of the 16 query rows a lane holds
 // (rows 8j + 4h .. +3 for j = 0..3): 8 reads at the wave's record region
 template <int SLOT>
 __device__ __forceinline__ void lds_read_rec(uint32_t a, f32x4 (&ls)[4], f32x4 (&dl)[4]) {
@@ -151,10 +151,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     qf[c] = __builtin_bit_cast(bf16x8, a);
     dof[c] = __builtin_bit_cast(bf16x8, d);
   }
-  // the row's record: lse * log2 e and delta = rowsum(dO * O) (this lane's 64
-  // channels, then its partner's 32 lanes away); written for the dk/dv kernel
-  // (rows past L: zeros; a row that admitted no key, lse = -inf, must give
-  // P = 0)
+  // the row's record: lse * log2 e and -delta, delta = rowsum(dO * O) (this
+  // lane's 64 channels, then its partner's 32 lanes away); written for the
+  // dk/dv kernel, whose dP MFMAs start from -delta (rows past L: zeros; a row
+  // that admitted no key, lse = -inf, must give P = 0)
   float lse2 = 0.f, delta = 0.f;
   {
     float part = 0.f;
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     if (h32 == 0) {
       float* rec = p.rec + (static_cast<int64_t>(bh) * (p.nqb * 4) + row / kSK) * kRec;
       rec[row % kSK] = lse2;
-      rec[kSK + row % kSK] = delta;
+      rec[kSK + row % kSK] = -delta;
     }
   }
   f32x16 acc[4];
@@ -485,10 +485,11 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p, int 
     const bool need = q0 < L && wave_keys && !(qb == kb && q0 + kSK - 1 < kb * kBlk + wave * 32);
     if (STEADY || ns < nst) issue(nslot);
     if (!need) return;
-    // S = Q K^T and dP = dO V^T: 32 queries x this wave's 32 keys, one key per lane
-    f32x16 sc, dp;
+    // S = Q K^T and dP - delta = dO V^T - delta: 32 queries x this wave's 32
+    // keys, one key per lane (the dP MFMAs start from the record's -delta)
+    f32x16 sc;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
+    for (int i = 0; i < 16; ++i) sc[i] = 0.f;
     {
       u32x4 qr[8];
       lds_read_k8<OFF>(faddr, qr);
@@ -496,6 +497,11 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p, int 
       for (int c = 0; c < 8; ++c)
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qr[c]), kf[c], sc, 0, 0, 0);
     }
+    f32x4 ls[4], dl[4];
+    lds_read_rec<SLOT>(raddr, ls, dl);
+    f32x16 dp;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dp[i] = dl[i >> 2][i & 3];
     {
       u32x4 dr[8];
       lds_read_k8<OFF + kSlab * 16>(faddr, dr);
@@ -503,8 +509,6 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p, int 
       for (int c = 0; c < 8; ++c)
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, dr[c]), vf[c], dp, 0, 0, 0);
     }
-    f32x4 ls[4], dl[4];
-    lds_read_rec<SLOT>(raddr, ls, dl);
     // register i holds query q0 + 8(i/4) + 4 h32 + (i%4): it must not precede the key and must exist
     if (qb == kb || q0 + kSK > L) {
 #pragma unroll
@@ -516,7 +520,7 @@ __global__ __launch_bounds__(kWaves * 64) void bwd_dkdv_kernel(BwdParams p, int 
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       sc[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], p.c1, -ls[i >> 2][i & 3]));  // P
-      dp[i] = sc[i] * (dp[i] - dl[i >> 2][i & 3]);                                       // dS
+      dp[i] = sc[i] * dp[i];                                                             // dS
     }
     bf16x8 pf[2], df[2];
 #pragma unroll
