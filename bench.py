@@ -972,7 +972,13 @@ def main():
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    evs = [[TimingEvent() for _ in range(nev)] for _ in range(args.steps)]
+    try:
+        evs = [[TimingEvent() for _ in range(nev)] for _ in range(args.steps)]
+        timing = "HIP timing events (hipEventDisableSystemFence)"
+    except (OSError, RuntimeError, AttributeError) as exc:  # keep measuring with torch's events
+        print(f"[bench] timing events unavailable ({exc}); torch events instead", flush=True)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+        timing = "torch events"
     print("[bench] timing", flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -1095,6 +1101,7 @@ def main():
                         "at ctx U[65536,131072] over a paged cache + SSA backward of the prefill workload + "
                         "hierarchical second stage (top-512 tokens of the 8 recalled pages) and attention over "
                         "window + tokens at the page-selection shape",
+            "timing": timing,
             "prefill_tokens_per_s": L2 / t2,
             "decode_gbps": gb3,
             "decode_frac_hbm": gb3 / PEAK_HBM_GBS,
