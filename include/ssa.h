@@ -42,7 +42,7 @@ extern "C" {
 typedef enum ssa_status {
   SSA_OK = 0,
   SSA_ERR_INVALID = 1,     /* a null pointer, a bad size, stride or alignment */
-  SSA_ERR_UNSUPPORTED = 2, /* a valid request this build has no kernel for   */
+  SSA_ERR_UNSUPPORTED = 2, /* a valid request the library has no kernel for */
   SSA_ERR_DEVICE = 3,      /* the HIP runtime refused a launch               */
   SSA_ERR_WORKSPACE = 4    /* workspace missing or too small                 */
 } ssa_status;

@@ -197,7 +197,7 @@ int ssa_prefill(const ssa_attn_args* a, const ssa_block_lists* lists, void* stre
   ssa::PrefillParams p = make_prefill(a);
   set_lists(p, lists);
   hipError_t e = ssa::launch_prefill(p, a->dtype, a->Dqk, a->Dv, a->out_dtype == SSA_DTYPE_F32, as_stream(stream));
-  if (e == hipErrorNotSupported) return fail(SSA_ERR_UNSUPPORTED, "%s: no kernel for Dqk=%d Dv=%d in this build", who, a->Dqk, a->Dv);
+  if (e == hipErrorNotSupported) return fail(SSA_ERR_UNSUPPORTED, "%s: the library has no kernel for Dqk=%d Dv=%d", who, a->Dqk, a->Dv);
   return device_status(e, who);
 }
 
@@ -247,7 +247,7 @@ int ssa_dense_causal(const ssa_attn_args* a, void* stream) {
   p.dense = 1;
   p.W = 0;
   hipError_t e = ssa::launch_prefill(p, a->dtype, a->Dqk, a->Dv, a->out_dtype == SSA_DTYPE_F32, as_stream(stream));
-  if (e == hipErrorNotSupported) return fail(SSA_ERR_UNSUPPORTED, "%s: no kernel for Dqk=%d Dv=%d in this build", who, a->Dqk, a->Dv);
+  if (e == hipErrorNotSupported) return fail(SSA_ERR_UNSUPPORTED, "%s: the library has no kernel for Dqk=%d Dv=%d", who, a->Dqk, a->Dv);
   return device_status(e, who);
 }
 
@@ -525,7 +525,7 @@ static int decode_impl(const ssa_decode_args* a, const ssa_window* win, void* st
   p.nsplit = static_cast<int32_t>(ceil_div(a->max_blocks, 16));
   hipError_t e = dense ? ssa::launch_decode_dense(p, a->Dqk, as_stream(stream))
                        : ssa::launch_decode(p, a->Dqk, a->Dv, as_stream(stream));
-  if (e == hipErrorNotSupported) return fail(SSA_ERR_UNSUPPORTED, "%s: no kernel for Dqk=%d Dv=%d in this build", who, a->Dqk, a->Dv);
+  if (e == hipErrorNotSupported) return fail(SSA_ERR_UNSUPPORTED, "%s: the library has no kernel for Dqk=%d Dv=%d", who, a->Dqk, a->Dv);
   return device_status(e, who);
 }
 
