@@ -751,8 +751,8 @@ def main():
         write_traffic(*args.write_traffic)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(every row of the path fits one MI355X; sharding is described in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(every row of the path fits one MI355X)", file=sys.stderr)
         sys.exit(2)
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_budget)
