@@ -263,28 +263,33 @@ void prefill_d128_kernel(KernelParams<PAGED, TOKENS> p) {
 #define SSA_DMA(src, dst) \
   __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(src), (SSA_LDS void*)(dst), 16, 0, 0)
     if constexpr (PAGED) {
-      // block kb lives in its page: rows r0 .. r0+31 of the page
+      // block kb lives in its page: the stage takes rows 32 QTR .. 32 QTR + 31 of it
       const int sb = stage_block(s);
-      const int kb = max(sb, 0);  // skipped entries stage block 0 (unused)
-      const int pg = sb >= 0 ? __builtin_amdgcn_readlane(plane, s >> 2) : page0;
-      const __bf16* kpg = kbase + static_cast<int64_t>(pg) * p.ks_b;
-      const __bf16* vpg = vbase + static_cast<int64_t>(pg) * p.vs_b;
-      const int r0 = (s & 3) * kSK;
-      if (kb * kBlk + r0 + kSK <= L) {
-        const __bf16* ks = kpg + static_cast<int64_t>(r0) * p.ks_l + koff;
-        const __bf16* vs = vpg + static_cast<int64_t>(r0) * p.vs_l + voff;
-        SSA_DMA(ks, kd);
-        SSA_DMA(ks + k16, kd + 256);
-        SSA_DMA(vs, vd);
-        SSA_DMA(vs + v16, vd + 256);
+      // iss_key0: the stage's first key; iss_k, iss_v: its first row in the page
+      if constexpr (QTR == 0) {
+        const int kb = max(sb, 0);  // skipped entries stage block 0 (unused)
+        const int pg = sb >= 0 ? __builtin_amdgcn_readlane(plane, s >> 2) : page0;
+        iss_key0 = kb * kBlk;
+        iss_k = kbase + static_cast<int64_t>(pg) * p.ks_b;
+        iss_v = vbase + static_cast<int64_t>(pg) * p.vs_b;
+      } else {
+        iss_key0 += kSK;
+        iss_k += k32;
+        iss_v += v32;
+      }
+      if (iss_key0 + kSK <= L) {
+        SSA_DMA(iss_k + koff, kd);
+        SSA_DMA(iss_k + koff + k16, kd + 256);
+        SSA_DMA(iss_v + voff, vd);
+        SSA_DMA(iss_v + voff + v16, vd + 256);
       } else {
         // the sequence's last block: rows at or past n repeat row n-1
-        const int last = L - 1 - kb * kBlk;
-        const int64_t ra = min(r0 + drow, last), rb = min(r0 + drow + 16, last);
-        SSA_DMA(kpg + ra * p.ks_l + dunit * 8, kd);
-        SSA_DMA(kpg + rb * p.ks_l + dunit * 8, kd + 256);
-        SSA_DMA(vpg + ra * p.vs_l + dunit * 8, vd);
-        SSA_DMA(vpg + rb * p.vs_l + dunit * 8, vd + 256);
+        const int last = L - 1 - iss_key0;
+        const int64_t ra = min(drow, last), rb = min(drow + 16, last);
+        SSA_DMA(iss_k + ra * p.ks_l + dunit * 8, kd);
+        SSA_DMA(iss_k + rb * p.ks_l + dunit * 8, kd + 256);
+        SSA_DMA(iss_v + ra * p.vs_l + dunit * 8, vd);
+        SSA_DMA(iss_v + rb * p.vs_l + dunit * 8, vd + 256);
       }
     } else {
       if constexpr (TOKENS) {
