@@ -330,6 +330,7 @@ void prefill_d128_kernel(KernelParams<PAGED, TOKENS> p) {
 #undef SSA_DMA
   };
 
+  int cur_kb = -1;  // the block of the stage being computed
   // ---- one stage: keys of stage s in ring slot SLOT; first this wave's
   // loads of stage ns (if any) into slot nslot ------------------------------
   auto stage = [&](auto slot_tag, auto steady_tag, int s, int ns, int nslot) {
@@ -337,8 +338,10 @@ void prefill_d128_kernel(KernelParams<PAGED, TOKENS> p) {
     constexpr bool STEADY = decltype(steady_tag)::value;  // ns < nst is known
     constexpr int OFF = SLOT * kSlotBytes;
     const bool tst = TOKENS && s >= nbs;  // a token stage
-    const int kb = stage_block(s);
-    const int sub = s & 3;
+    // stages come in order with s mod 4 = SLOT: a block's list entry is read at its first quarter
+    if constexpr (SLOT == 0) cur_kb = stage_block(s);
+    const int kb = cur_kb;
+    constexpr int sub = SLOT;
     const int key0 = kb * kBlk + sub * kSK;
     const bool need = tst || (kb >= 0 && key0 < L && !(kb == qb && sub * kSK > qoff + 31));
     if (STEADY || ns < nst) issue(std::integral_constant<int, (SLOT + kSlots - 1) % kSlots>{}, ns, nslot);
