@@ -26,6 +26,8 @@
 //   - the running max is refreshed lazily: the accumulator is rescaled only
 //     when the max grows by more than 2^8, which is exact because the final
 //     normalisation uses the same reference max.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace ssa {
@@ -86,6 +88,11 @@ struct WideGeom {
   static constexpr int VUNITS = SHARED ? 0 : kStageKeys * UV;
   static constexpr int SLOT = KUNITS + VUNITS;  // multiple of 64 units
   static constexpr int NSLOTS = 2 * SLOT * 16 <= 160 * 1024 ? 2 : 1;
+  // 576/512 with the latent shared by K and V: 32 queries per wave take a
+  // 256-register accumulator and 144 registers of Q^T, so one wave per SIMD;
+  // each 64-key stage then runs as two 32-key halves (SUBS) to keep the score
+  // tile small
+  static constexpr int SUBS = KSW ? 2 : 1;
   static_assert(KUNITS % 64 == 0 && VUNITS % 64 == 0, "slab = whole 1 KB wave writes");
 };
 
@@ -149,12 +156,16 @@ struct Stager {
   }
 };
 
+// waves per SIMD: one for the 576-wide kernel with 32 queries per wave, else two
+constexpr int wide_wpe(int dqk, int nq) { return dqk == 576 && nq == 2 ? 1 : 2; }
+
 // NQ = 16-query tiles per wave; the workgroup's 128 / (16 NQ) waves cover one
 // query block.  Two waves per SIMD: one 8-wave workgroup (NQ = 1) or two
 // independent 4-wave workgroups (NQ = 2) per CU.  DENSE: every block
 // 0 .. qb, own block first (the dense comparison layer); else the block list.
 template <int DQK, int DV, bool SHARED, int NQ, bool DENSE, typename OutT>
-__global__ __launch_bounds__(kBlk / (16 * NQ) * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kBlk / (16 * NQ) * 64)
+__attribute__((amdgpu_waves_per_eu(wide_wpe(DQK, NQ), wide_wpe(DQK, NQ))))
 void prefill_wide_kernel(PrefillParams p) {
   using G = WideGeom<DQK, DV, SHARED>;
   constexpr int kNQ = NQ;
@@ -228,7 +239,7 @@ void prefill_wide_kernel(PrefillParams p) {
     for (int n = 0; n < kNQ; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int NS = G::NSLOTS;
-  Stager<DQK, G::UK, kWWaves, (kNQ >= 2), G::KSW> kst;
+  Stager<DQK, G::UK, kWWaves, (kNQ >= 2 && !G::KSW), G::KSW> kst;
   kst.init(p.ks_l, wave, lane);
   Stager<DV, G::UV, kWWaves, (kNQ >= 2)> vst;
   if constexpr (!SHARED) vst.init(p.vs_l, wave, lane);
@@ -241,11 +252,24 @@ void prefill_wide_kernel(PrefillParams p) {
     if constexpr (!SHARED) vst.issue(slot + G::KUNITS, vbase, p.vs_l, key0, p.L, wave, lane);
   };
 
-  // one stage: keys (s>>1)*128 + (s&1)*64 .. +63, staged in `cur`
-  auto compute = [&](int s, const u32x4* cur) {
+  // one call: keys (s>>1)*128 + (s&1)*64 + sub*16*KT .. +16*KT-1 of the
+  // stage staged in `cur` (KT 16-key tiles; SUBS calls per stage)
+  constexpr int SUBS = kNQ >= 2 ? G::SUBS : 1;
+  constexpr int KT = 4 / SUBS;
+  constexpr int NCH = KT / 2;  // 32-key chunks of the output product
+  // FIXREF: each row's reference max is the max of the first call that admits
+  // one of its keys, and is never raised (no accumulator rescale, which would
+  // take the 256 accumulator registers through the vector unit); else the
+  // lazy refresh below
+  constexpr bool FIXREF = G::KSW;
+  bool ref_set = false;  // wave-uniform: the first call of the first pass has run
+  // MODE 0: the first pass; 1: row maxima only; 2: the final pass of a rerun
+  auto compute = [&](auto mode_c, int s, const u32x4* cur, int sub) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_c)::value;
     const int kb = block_of(s >> 1);
     const int half = s & 1;
-    const bool work = kb >= 0 && !(kb == qb && half * kStageKeys > wave * kRows + kRows - 1);
+    const int key_lo = half * kStageKeys + sub * 16 * KT;  // first key of the call within its block
+    const bool work = kb >= 0 && !(kb == qb && key_lo > wave * kRows + kRows - 1);
     if (!work) return;
     const SSA_LDS u32x4* kslab = (const SSA_LDS u32x4*)(cur);
     const SSA_LDS u32x4* vslab = SHARED ? kslab : kslab + G::KUNITS;
@@ -254,20 +278,20 @@ void prefill_wide_kernel(PrefillParams p) {
     // the lane's unit within each 4-unit group of a K fragment read (rows
     // t*16 + r share f(r))
     const int kg = G::KSW ? g ^ wswz(r) : g;
-    f32x4 sc[4][kNQ];
+    f32x4 sc[KT][kNQ];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < KT; ++t)
 #pragma unroll
       for (int n = 0; n < kNQ; ++n) sc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (kNQ >= 2) {
       // K fragments are read KD channel chunks ahead of their MFMAs so that the
       // LDS latency is covered by the MFMAs of the chunks in between
       constexpr int KD = 1;
-      bf16x8 kf[KD + 1][4];
+      bf16x8 kf[KD + 1][KT];
       auto load_k = [&](int c) {
   #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          kf[c % (KD + 1)][t] = __builtin_bit_cast(bf16x8, kslab[(t * 16 + r) * G::UK + c * 4 + kg]);
+        for (int t = 0; t < KT; ++t)
+          kf[c % (KD + 1)][t] = __builtin_bit_cast(bf16x8, kslab[((sub * KT + t) * 16 + r) * G::UK + c * 4 + kg]);
       };
   #pragma unroll
       for (int c = 0; c < KD && c < NC; ++c) load_k(c);
@@ -275,18 +299,18 @@ void prefill_wide_kernel(PrefillParams p) {
       for (int c = 0; c < NC; ++c) {
         if (c + KD < NC) load_k(c + KD);
   #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < KT; ++t)
   #pragma unroll
           for (int n = 0; n < kNQ; ++n)
             sc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c % (KD + 1)][t], qf[n][c], sc[t][n], 0, 0, 0);
       }
       // keep that order: first reads, then per chunk its MFMAs after the next reads
   #pragma unroll
-      for (int c = 0; c < KD && c < NC; ++c) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      for (int c = 0; c < KD && c < NC; ++c) __builtin_amdgcn_sched_group_barrier(0x100, KT, 0);
   #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        if (c + KD < NC) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4 * kNQ, 0);
+        if (c + KD < NC) __builtin_amdgcn_sched_group_barrier(0x100, KT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, KT * kNQ, 0);
       }
     } else {
       // the 512-wide accumulator leaves no registers for read-ahead here
@@ -307,23 +331,54 @@ void prefill_wide_kernel(PrefillParams p) {
       for (int n = 0; n < kNQ; ++n) {
         const int qi = wave * kRows + n * 16 + r;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < KT; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int kk = half * kStageKeys + t * 16 + g * 4 + i;
+            const int kk = key_lo + t * 16 + g * 4 + i;
             const bool dead = (kb == qb && kk > qi) || kb * kBlk + kk >= p.L;
             if (dead) sc[t][n][i] = kNegInf;
           }
       }
     }
-#pragma unroll
-    for (int n = 0; n < kNQ; ++n) {
+    auto row_max = [&](int n) {
       float mx = kNegInf;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < KT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[t][n][i]);
-      mx = xlane_max(mx);
+      return xlane_max(mx);
+    };
+    if constexpr (FIXREF) {
+#pragma unroll
+      for (int n = 0; n < kNQ; ++n) {
+        if constexpr (MODE == 1) {
+          m[n] = fmaxf(m[n], row_max(n));
+        } else {
+          // the reference: the row max of the wave's first call (which
+          // admits key 0 of its block, so every row of the wave has one
+          // unless the list is invalid; a row left at -inf weighs its scores
+          // against 0, and any overflow that causes is caught by the rerun)
+          if constexpr (MODE == 0)
+            if (!ref_set) m[n] = row_max(n);
+          const float mc = m[n] == kNegInf ? 0.f : m[n] * p.c1;
+          float rs = 0.f;
+#pragma unroll
+          for (int t = 0; t < KT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][n][i], p.c1, -mc));
+              sc[t][n][i] = e;
+              rs += e;
+            }
+          l[n] += rs;  // this lane's part of the row sum, reduced across lanes at the end
+        }
+      }
+      if constexpr (MODE == 0) ref_set = true;
+      if constexpr (MODE == 1) return;
+    } else {
+#pragma unroll
+    for (int n = 0; n < kNQ; ++n) {
+      const float mx = row_max(n);
       const float m_new = fmaxf(m[n], mx);
       // lazy refresh of the reference max
       const bool refresh = (m_new - m[n]) * p.c1 > kLazy;
@@ -338,7 +393,7 @@ void prefill_wide_kernel(PrefillParams p) {
       const float mc = m_use * p.c1;
       float rs = 0.f;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < KT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][n][i], p.c1, -mc));
@@ -347,6 +402,7 @@ void prefill_wide_kernel(PrefillParams p) {
         }
       l[n] += xlane_sum(rs);
     }
+    }
     // O^T += V^T P^T over two 32-key chunks.  Step st = c * NJ + jt: the
     // V^T fragment of (chunk c, channel tile jt) is two transposed reads --
     // lane j of group g points at key c*32 + h2*16 + 4g + j/4, channels
@@ -354,11 +410,11 @@ void prefill_wide_kernel(PrefillParams p) {
     // c*32 + h2*16 + 4g .. +3 -- issued VD steps ahead of its MFMAs.
     if constexpr (kNQ >= 2) {
       constexpr int VD = 4;
-      constexpr int NSTEP = 2 * NJ;
+      constexpr int NSTEP = NCH * NJ;
       bf16x8 vfr[VD + 1];
       auto load_v = [&](int st) {
         const int c = st / NJ, jt = st % NJ;
-        const int krow = c * 32 + 4 * g + (r >> 2);
+        const int krow = (sub * NCH + c) * 32 + 4 * g + (r >> 2);
         const int ch = jt * 16 + 4 * (r & 3);
         const int vu = VSW ? 4 * (jt >> 1) + ((2 * (jt & 1) + ((r & 3) >> 1)) ^ wswz(krow)) : (ch >> 3);
         const SSA_LDS char* base0 = (const SSA_LDS char*)(vslab + krow * UV + vu) + (ch & 7) * 2;
@@ -367,9 +423,9 @@ void prefill_wide_kernel(PrefillParams p) {
         const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSA_LDS bf16x4*)base1);
         vfr[st % (VD + 1)] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       };
-      bf16x8 pf[2][kNQ];
+      bf16x8 pf[NCH][kNQ];
   #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < NCH; ++c)
   #pragma unroll
         for (int n = 0; n < kNQ; ++n) {
           const bf16x4 a = __builtin_convertvector(sc[2 * c][n], bf16x4);
@@ -424,28 +480,57 @@ void prefill_wide_kernel(PrefillParams p) {
     }
   };
 
-  if constexpr (NS == 2) {
-    if (nst > 0) issue(0, slot_a);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int s = 0; s < nst; s += 2) {
-      if (s + 1 < nst) issue(s + 1, slot_b);
-      compute(s, slot_a);
+  auto run = [&](auto mode_c) __attribute__((always_inline)) {
+    if constexpr (NS == 2) {
+      if (nst > 0) issue(0, slot_a);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (s + 1 >= nst) break;
-      if (s + 2 < nst) issue(s + 2, slot_a);
-      compute(s + 1, slot_b);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      for (int s = 0; s < nst; s += 2) {
+        if (s + 1 < nst) issue(s + 1, slot_b);
+#pragma unroll
+        for (int sub = 0; sub < SUBS; ++sub) compute(mode_c, s, slot_a, sub);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (s + 1 >= nst) break;
+        if (s + 2 < nst) issue(s + 2, slot_a);
+#pragma unroll
+        for (int sub = 0; sub < SUBS; ++sub) compute(mode_c, s + 1, slot_b, sub);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    } else {
+      for (int s = 0; s < nst; ++s) {
+        issue(s, slot_a);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        compute(mode_c, s, slot_a, 0);
+        __syncthreads();
+      }
     }
-  } else {
-    for (int s = 0; s < nst; ++s) {
-      issue(s, slot_a);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      compute(s, slot_a);
-      __syncthreads();
+  };
+  run(std::integral_constant<int, 0>{});
+  if constexpr (FIXREF) {
+#pragma unroll
+    for (int n = 0; n < kNQ; ++n) l[n] = xlane_sum(l[n]);
+    // a weight above 2^64 (sums and outputs could then approach the fp32
+    // range) shows as a row sum above 2^64, inf or NaN: then the whole
+    // workgroup reruns the tile, first for the exact row maxima, then with
+    // them as the reference (weights <= 1)
+    bool bad = false;
+#pragma unroll
+    for (int n = 0; n < kNQ; ++n) bad |= !(l[n] <= 0x1p64f);
+    if (__syncthreads_or(bad)) {
+#pragma unroll
+      for (int n = 0; n < kNQ; ++n) {
+        m[n] = kNegInf;
+        l[n] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      run(std::integral_constant<int, 1>{});
+      run(std::integral_constant<int, 2>{});
+#pragma unroll
+      for (int n = 0; n < kNQ; ++n) l[n] = xlane_sum(l[n]);
     }
   }
 
@@ -480,17 +565,19 @@ hipError_t launch_mode(const PrefillParams& p, bool out_f32, hipStream_t stream)
                  : launch_one<DQK, DV, SHARED, NQ, false, __bf16>(p, stream);
 }
 
-template <int DQK, int DV, int NQ>
+// NQS / NQA: 16-query tiles per wave with K and V shared / apart
+template <int DQK, int DV, int NQS, int NQA>
 hipError_t launch_dims(const PrefillParams& p, bool shared, bool out_f32, hipStream_t stream) {
-  return shared ? launch_mode<DQK, DV, true, NQ>(p, out_f32, stream) : launch_mode<DQK, DV, false, NQ>(p, out_f32, stream);
+  return shared ? launch_mode<DQK, DV, true, NQS>(p, out_f32, stream)
+                : launch_mode<DQK, DV, false, NQA>(p, out_f32, stream);
 }
 
 }  // namespace
 
 hipError_t launch_prefill_wide(const PrefillParams& p, int dqk, int dv, bool out_f32, hipStream_t stream) {
   const bool shared = p.v == p.k && p.vs_b == p.ks_b && p.vs_l == p.ks_l && p.vs_h == p.ks_h;
-  if (dqk == 576 && dv == 512) return launch_dims<576, 512, 1>(p, shared, out_f32, stream);
-  if (dqk == 64 && dv == 64) return launch_dims<64, 64, 2>(p, shared, out_f32, stream);
+  if (dqk == 576 && dv == 512) return launch_dims<576, 512, 2, 1>(p, shared, out_f32, stream);
+  if (dqk == 64 && dv == 64) return launch_dims<64, 64, 2, 2>(p, shared, out_f32, stream);
   return hipErrorNotSupported;
 }
 

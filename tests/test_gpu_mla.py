@@ -43,6 +43,34 @@ def test_mla_prefill_small(lib, L, Hq, shared, out):
     check_close(to_f64(lse), rl, f"mla L={L} lse")
 
 
+@pytest.mark.parametrize("jump,dense", [(40.0, False), (60.0, False), (100.0, False), (60.0, True)])
+def test_mla_prefill_reference_max_rerun(lib, jump, dense):
+    """Scores jump by `jump` nats at block 3, far above the reference max the
+    576-wide kernel takes from the first keys a row sees.  40: weights up to
+    2^58, whose sums pass 2^64; 60: up to 2^87; 100: fp32 overflow on the
+    first pass.  In each case the tile is rerun with the exact row maxima, and
+    every row must match (the dense layer sees its own block first)."""
+    B, L, H = 1, 1024, 2
+    g = torch.Generator().manual_seed(int(jump) + 7)
+    q = torch.ones((B, L, H, DQK)).bfloat16()
+    c = (0.05 * torch.randn((B, L, 1, DQK), generator=g)).bfloat16()
+    c[:, 3 * 128:4 * 128] = jump / (DQK * SCALE)  # q.k * scale = jump (up to bf16 rounding)
+    c[:, 3 * 128:4 * 128, :, :DV] = torch.randn((128, DV), generator=g).bfloat16()[None, :, None]
+    c[:, 3 * 128:4 * 128, :, DV:] = jump / ((DQK - DV) * SCALE)  # only the rope part carries the jump
+    say(f"mla reference-max rerun jump={jump} dense={dense}")
+    qd, cd = q.cuda(), c.cuda()
+    if dense:
+        o, lse = lib.dense_causal(qd, cd, cd[..., :DV], scale=SCALE, with_lse=True)
+    else:
+        o, lse = lib.ssa(qd, cd, cd[..., :DV], scale=SCALE, with_lse=True)
+    torch.cuda.synchronize()
+    f64 = lambda t: t.float().double().numpy()
+    ref = oracle.dense_causal if dense else oracle.ssa_attention
+    ro, rl = ref(f64(q), f64(c), f64(c[..., :DV]), SCALE)
+    check_close(to_f64(o), ro, f"mla rerun jump={jump} o")
+    check_close(to_f64(lse), rl, f"mla rerun jump={jump} lse")
+
+
 def test_mla_dense_small(lib):
     qh, kh, vh, q, k, v = mla_inputs(72, 1, 700, 16)
     say("mla dense")
