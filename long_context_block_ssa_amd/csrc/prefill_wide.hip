@@ -8,24 +8,33 @@
 // ZigZag sparse attention" page, section 2.1, causal in the own block
 // (section 2.2.1), evaluated as an exact online softmax.
 //
-// One workgroup = one 128-query block of one head, 16*NQ queries per wave
-// (NQ = 2 for d = 64: 4 waves; NQ = 1 for the 512-wide accumulator:
-// 8 waves), two waves per SIMD.  Keys stream in 64-key stages through two
-// LDS slots:
+// One workgroup = one 128-query block of one head, 16*NQ queries per wave.
+// d = 64: NQ = 2, 4 waves, two workgroups (two waves per SIMD) per CU.  The
+// latent-shared 576/512 shape: NQ = 2, 4 waves, one wave per SIMD (the
+// 32 x 512 fp32 accumulator fills the 256 AGPRs, Q^T 144 VGPRs), since 16
+// queries per wave left each byte read from LDS feeding too few MFMA flops;
+// with V staged apart it keeps NQ = 1 (8 waves).  Keys stream in 64-key
+// stages through two LDS slots:
 //   - staging uses global_load_lds_dwordx4 (global -> LDS, no registers);
 //     d = 64 rows are padded by one 16-byte unit so that the 16 lanes
 //     reading a fragment column hit 16 distinct bank groups; the 576-wide
-//     latent rows are XOR-swizzled instead (see wswz), which also spreads
-//     the transposed V reads;
+//     latent has its own layout (value rows of one wave-instruction each,
+//     XOR-swizzled, and a rope tail: see lswz), which also spreads the
+//     transposed V reads;
 //   - S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K rows, ds_read_b128;
-//     B = Q^T held in registers), so each lane owns one query column;
+//     B = Q^T held in registers), so each lane owns one query column; at
+//     576 a stage runs as two 32-key calls to keep the score tile small;
 //   - O^T = V^T P^T: P^T comes from the S^T accumulators converted to bf16;
 //     the V^T operand is read from the row-major V slab with
 //     ds_read_b64_tr_b16, which hands each lane 4 keys of one channel, so the
 //     latent is staged once and serves as both K and V;
-//   - the running max is refreshed lazily: the accumulator is rescaled only
-//     when the max grows by more than 2^8, which is exact because the final
-//     normalisation uses the same reference max.
+//   - d = 64: the running max is refreshed lazily: the accumulator is
+//     rescaled only when the max grows by more than 2^8, which is exact
+//     because the final normalisation uses the same reference max;
+//   - 576: a fixed reference max per row (the max of the wave's first call),
+//     never raised, so the accumulator is never rescaled; a row sum above
+//     2^64 (or inf / NaN) makes the workgroup rerun the tile, first for the
+//     exact row maxima, then with them as the reference.
 #include <type_traits>
 
 #include "common.hpp"
@@ -67,24 +76,32 @@ __device__ __forceinline__ void store4<__bf16>(__bf16* dst, f32x4 v) {
   *reinterpret_cast<bf16x4*>(dst) = __builtin_convertvector(v, bf16x4);
 }
 
-// Row layout of the 576-wide latent slab: rows 76 units (1216 bytes) apart,
-// so that rows r, r+1, r+2, r+3 start 48 banks apart modulo 64 banks of 4
-// bytes, and unit u of row r at u ^ f(r) with f(r) = 2 ((r >> 2) mod 2) +
-// (r >> 3) mod 2 (an XOR of the unit's two low bits only, so the fragment
-// offsets stay immediates).  On that bank model the fragment reads (16 rows,
-// one unit) and the transposed reads (per 32 lanes 8 rows x 2 units x 2
-// halves) each cover the banks once.  Measured, bank-conflict cycles fell
-// from 49% of the LDS cycles (one pad unit per row, 73 units) to 34%.
-constexpr int kWidePitch576 = 76;
-__device__ __forceinline__ int wswz(int row) { return (((row >> 2) & 1) << 1) | ((row >> 3) & 1); }
+// Layout of the 576-wide latent in a stage slot, in 16-byte units: the 512
+// value channels (units 0..63) of key row k as one 1 KB row at k * 64, unit u
+// at u ^ lswz(k), lswz(k) = 4 (k mod 4) + (k / 4) mod 4 (a bijection on k mod
+// 16, so the 16 rows of a fragment read and the 4 rows x 2 units of a
+// transposed read fall on distinct bank groups of the 64 banks); the 64 rope
+// channels (units 64..71) in a tail after the 64 rows, 8 units per key, unit
+// u of row k at kLatMain + 8 k + ((u - 64) ^ tswz(k)), tswz(k) = (k / 2) mod 8.
+// Rows are whole wave-instructions of the direct-to-LDS staging, so a row's
+// source address is uniform and a lane's offset within it takes one of a few
+// values (no per-stage address arithmetic).
+constexpr int kLatMain = 64 * 64;           // units of the 64 value rows
+constexpr int kLatUnits = kLatMain + 64 * 8;  // plus the rope tail
+__device__ __forceinline__ int lswz(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
+__device__ __forceinline__ int tswz(int row) { return (row >> 1) & 7; }
+// unit index of logical unit u (0..71) of staged row `row`
+__device__ __forceinline__ int lat_unit(int row, int u) {
+  return u < 64 ? row * 64 + (u ^ lswz(row)) : kLatMain + row * 8 + ((u - 64) ^ tswz(row));
+}
 
 // LDS geometry of one stage slot, in 16-byte units.
 template <int DQK, int DV, bool SHARED>
 struct WideGeom {
-  static constexpr bool KSW = DQK == 576;  // K slab swizzled instead of padded by one unit
-  static constexpr int UK = KSW ? kWidePitch576 : DQK / 8 + 1;  // K row pitch
+  static constexpr bool KSW = DQK == 576;  // the latent layout above instead of rows padded by one unit
+  static constexpr int UK = KSW ? 64 : DQK / 8 + 1;  // K row pitch (the value rows of the latent)
   static constexpr int UV = DV / 8 + 1;   // V row pitch when V is staged apart
-  static constexpr int KUNITS = kStageKeys * UK;
+  static constexpr int KUNITS = KSW ? kLatUnits : kStageKeys * UK;
   static constexpr int VUNITS = SHARED ? 0 : kStageKeys * UV;
   static constexpr int SLOT = KUNITS + VUNITS;  // multiple of 64 units
   static constexpr int NSLOTS = 2 * SLOT * 16 <= 160 * 1024 ? 2 : 1;
@@ -104,22 +121,17 @@ struct WideGeom {
 // is recomputed per stage (the 512-wide accumulator leaves no registers).  A
 // lane on a row's pad unit loads unit 0 of its row.  Keys at or past L are
 // clamped to row L-1 (finite data, masked later).
-template <int D, int U, int NW, bool CACHE, bool SW = false>
+template <int D, int U, int NW, bool CACHE>
 struct Stager {
   static constexpr int TOTAL = kStageKeys * U / 64;  // wave-instructions per slab
   static constexpr int PER = (TOTAL + NW - 1) / NW;  // per wave
   int32_t off[CACHE ? PER : 1];
 
-  // SW: the lane at unit position pos of a row loads logical unit pos ^ f(row)
-  // (f flips the two low bits only, so pos < D/8 stays below D/8)
   __device__ __forceinline__ static void place(int i, int lane, int& row, int& unit) {
     const int pidx = i * 64 + lane;
     row = pidx / U;
     const int pos = pidx - row * U;
-    if constexpr (SW)
-      unit = pos < D / 8 ? pos ^ wswz(row) : 0;
-    else
-      unit = pos < D / 8 ? pos : 0;
+    unit = pos < D / 8 ? pos : 0;
   }
   __device__ __forceinline__ void init(int64_t stride_l, int wave, int lane) {
     if constexpr (CACHE) {
@@ -152,6 +164,64 @@ struct Stager {
       const int key = min(key0 + row, L - 1);
       const __bf16* src = base + static_cast<int64_t>(key) * stride_l + unit * 8;
       __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(src), (SSA_LDS void*)(slab + i * 64), 16, 0, 0);
+    }
+  }
+};
+
+// Stages latent rows key0 .. key0+63 (576 channels) in the layout above:
+// the wave issues value rows wave, wave + NW, ... (a row per instruction, its
+// source row uniform, the lane's byte offset one of NX values by the row's
+// swizzle) and tail instructions wave, wave + NW, ... (8 rows of 8 units
+// each; a lane's offset from the instruction's first row is fixed).  Keys
+// at or past L are clamped to row L-1 (finite data, masked later).
+template <int NW>
+struct LatentStager {
+  static constexpr int NX = 16 / NW;  // swizzles among a wave's value rows
+  static constexpr int NT = 8 / NW;   // tail instructions per wave
+  uint32_t moff[NX];
+  uint32_t toff;
+  __device__ __forceinline__ void init(int64_t stride_l, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < NX; ++j) moff[j] = static_cast<uint32_t>((lane ^ lswz(wave + NW * j)) * 16);
+    // rows 8 (wave + NW m) + lane / 8 share one tail swizzle for every m
+    const int trow = 8 * wave + (lane >> 3);
+    toff = static_cast<uint32_t>((lane >> 3) * stride_l * 2 + (64 + ((lane & 7) ^ tswz(trow))) * 16);
+  }
+  __device__ __forceinline__ void issue(SSA_LDS u32x4* slab, const __bf16* base, int64_t stride_l, int key0, int L,
+                                        int wave, int lane) const {
+    const bool ragged = key0 + kStageKeys > L;  // uniform: only the last block of a ragged L
+    const char* b = reinterpret_cast<const char*>(base);
+    const int64_t sb = stride_l * 2;
+    if (!ragged) {
+      // one uniform row pointer, stepped by NW rows
+      const char* rp = b + (key0 + wave) * sb;
+#pragma unroll
+      for (int j = 0; j < kStageKeys / NW; ++j) {
+        __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(rp + moff[j % NX]),
+                                         (SSA_LDS void*)(slab + (wave + NW * j) * 64), 16, 0, 0);
+        rp += NW * sb;
+      }
+    } else {
+#pragma unroll 1
+      for (int j = 0; j < kStageKeys / NW; ++j) {
+        const int row = wave + NW * j;
+        const int key = min(key0 + row, L - 1);  // uniform
+        __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(b + key * sb + moff[j % NX]),
+                                         (SSA_LDS void*)(slab + row * 64), 16, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      const int t = wave + NW * m;
+      if (!ragged) {
+        __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(b + (key0 + 8 * t) * sb + toff),
+                                         (SSA_LDS void*)(slab + kLatMain + t * 64), 16, 0, 0);
+      } else {
+        const int row = 8 * t + (lane >> 3);
+        const int key = min(key0 + row, L - 1);
+        __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(b + key * sb + (64 + ((lane & 7) ^ tswz(row))) * 16),
+                                         (SSA_LDS void*)(slab + kLatMain + t * 64), 16, 0, 0);
+      }
     }
   }
 };
@@ -239,8 +309,16 @@ void prefill_wide_kernel(PrefillParams p) {
     for (int n = 0; n < kNQ; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int NS = G::NSLOTS;
-  Stager<DQK, G::UK, kWWaves, (kNQ >= 2 && !G::KSW), G::KSW> kst;
+  std::conditional_t<G::KSW, LatentStager<kWWaves>, Stager<DQK, G::UK, kWWaves, (kNQ >= 2)>> kst;
   kst.init(p.ks_l, wave, lane);
+  // per-lane unit indices of the latent fragment reads: value chunk c (units
+  // 4c .. 4c+3) of row 16 T + r at kb4[c mod 4] + 16 (c / 4) + 1024 T, rope
+  // chunk c' of that row at tb2[c'] + 128 T
+  int kb4[4], tb2[2];
+#pragma unroll
+  for (int b4 = 0; b4 < 4; ++b4) kb4[b4] = r * 64 + ((4 * b4 + g) ^ lswz(r));
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) tb2[c2] = kLatMain + r * 8 + ((4 * c2 + g) ^ tswz(r));
   Stager<DV, G::UV, kWWaves, (kNQ >= 2)> vst;
   if constexpr (!SHARED) vst.init(p.vs_l, wave, lane);
   auto issue = [&](int s, u32x4* slot_generic) {
@@ -275,9 +353,14 @@ void prefill_wide_kernel(PrefillParams p) {
     const SSA_LDS u32x4* vslab = SHARED ? kslab : kslab + G::KUNITS;
     constexpr int UV = SHARED ? G::UK : G::UV;
     constexpr bool VSW = SHARED && G::KSW;  // V read from the swizzled latent slab
-    // the lane's unit within each 4-unit group of a K fragment read (rows
-    // t*16 + r share f(r))
-    const int kg = G::KSW ? g ^ wswz(r) : g;
+    // K fragment: chunk c (32 channels) of rows 16 rt + (lane mod 16)
+    auto kfrag = [&](int rt, int c) -> bf16x8 {
+      if constexpr (G::KSW)
+        return __builtin_bit_cast(bf16x8, c < 16 ? kslab[kb4[c & 3] + 16 * (c >> 2) + 1024 * rt]
+                                                 : kslab[tb2[c - 16] + 128 * rt]);
+      else
+        return __builtin_bit_cast(bf16x8, kslab[(rt * 16 + r) * G::UK + c * 4 + g]);
+    };
     f32x4 sc[KT][kNQ];
 #pragma unroll
     for (int t = 0; t < KT; ++t)
@@ -291,7 +374,7 @@ void prefill_wide_kernel(PrefillParams p) {
       auto load_k = [&](int c) {
   #pragma unroll
         for (int t = 0; t < KT; ++t)
-          kf[c % (KD + 1)][t] = __builtin_bit_cast(bf16x8, kslab[((sub * KT + t) * 16 + r) * G::UK + c * 4 + kg]);
+          kf[c % (KD + 1)][t] = kfrag(sub * KT + t, c);
       };
   #pragma unroll
       for (int c = 0; c < KD && c < NC; ++c) load_k(c);
@@ -318,7 +401,7 @@ void prefill_wide_kernel(PrefillParams p) {
       for (int c = 0; c < NC; ++c) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const bf16x8 kf1 = __builtin_bit_cast(bf16x8, kslab[(t * 16 + r) * G::UK + c * 4 + kg]);
+          const bf16x8 kf1 = kfrag(t, c);
 #pragma unroll
           for (int n = 0; n < kNQ; ++n)
             sc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf1, qf[n][c], sc[t][n], 0, 0, 0);
@@ -416,7 +499,7 @@ void prefill_wide_kernel(PrefillParams p) {
         const int c = st / NJ, jt = st % NJ;
         const int krow = (sub * NCH + c) * 32 + 4 * g + (r >> 2);
         const int ch = jt * 16 + 4 * (r & 3);
-        const int vu = VSW ? 4 * (jt >> 1) + ((2 * (jt & 1) + ((r & 3) >> 1)) ^ wswz(krow)) : (ch >> 3);
+        const int vu = VSW ? 16 * (jt >> 3) + ((2 * (jt & 7) + ((r & 3) >> 1)) ^ lswz(krow)) : (ch >> 3);
         const SSA_LDS char* base0 = (const SSA_LDS char*)(vslab + krow * UV + vu) + (ch & 7) * 2;
         const SSA_LDS char* base1 = base0 + 16 * UV * 16;
         const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSA_LDS bf16x4*)base0);
@@ -464,9 +547,10 @@ void prefill_wide_kernel(PrefillParams p) {
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt) {
           const int ch = jt * 16 + ch_off;
-          // unit 2jt + (r mod 4)/2 of row krow, its two low bits XOR f(krow): a
-          // per-lane unit for even and for odd jt plus an immediate 4 (jt / 2)
-          const int vu = VSW ? 4 * (jt >> 1) + ((2 * (jt & 1) + ((r & 3) >> 1)) ^ wswz(krow)) : (ch >> 3);
+          // unit 2jt + (r mod 4)/2 of row krow, its four low bits XOR lswz(krow)
+          // (krow mod 16 = 4g + r/4 whatever the chunk): a per-lane unit for
+          // each jt mod 8 plus an immediate 16 (jt / 8)
+          const int vu = VSW ? 16 * (jt >> 3) + ((2 * (jt & 7) + ((r & 3) >> 1)) ^ lswz(krow)) : (ch >> 3);
           const SSA_LDS char* base0 = (const SSA_LDS char*)(vslab + krow * UV + vu) + (ch & 7) * 2;
           const SSA_LDS char* base1 = base0 + 16 * UV * 16;  // rows krow + 16: the same swizzle
           const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSA_LDS bf16x4*)base0);
