@@ -170,58 +170,60 @@ struct Stager {
 
 // Stages latent rows key0 .. key0+63 (576 channels) in the layout above:
 // the wave issues value rows wave, wave + NW, ... (a row per instruction, its
-// source row uniform, the lane's byte offset one of NX values by the row's
-// swizzle) and tail instructions wave, wave + NW, ... (8 rows of 8 units
-// each; a lane's offset from the instruction's first row is fixed).  Keys
-// at or past L are clamped to row L-1 (finite data, masked later).
+// source row uniform, the lane's byte offset (lane ^ lswz(row)) * 16) and
+// tail instructions wave, wave + NW, ... (8 rows of 8 units each).  Keys at
+// or past L are clamped to row L-1 (finite data, masked later).
 template <int NW>
 struct LatentStager {
-  static constexpr int NX = 16 / NW;  // swizzles among a wave's value rows
-  static constexpr int NT = 8 / NW;   // tail instructions per wave
-  uint32_t moff[NX];
-  uint32_t toff;
-  __device__ __forceinline__ void init(int64_t stride_l, int wave, int lane) {
-#pragma unroll
-    for (int j = 0; j < NX; ++j) moff[j] = static_cast<uint32_t>((lane ^ lswz(wave + NW * j)) * 16);
-    // rows 8 (wave + NW m) + lane / 8 share one tail swizzle for every m
-    const int trow = 8 * wave + (lane >> 3);
-    toff = static_cast<uint32_t>((lane >> 3) * stride_l * 2 + (64 + ((lane & 7) ^ tswz(trow))) * 16);
-  }
+  static constexpr int NT = 8 / NW;  // tail instructions per wave
+  __device__ __forceinline__ void init(int64_t, int, int) {}
   __device__ __forceinline__ void issue(SSA_LDS u32x4* slab, const __bf16* base, int64_t stride_l, int key0, int L,
                                         int wave, int lane) const {
     const bool ragged = key0 + kStageKeys > L;  // uniform: only the last block of a ragged L
     const char* b = reinterpret_cast<const char*>(base);
     const int64_t sb = stride_l * 2;
+    // The wave's row offset and the lane index made opaque here, so that
+    // nothing derived from them is computed once and kept live across the
+    // stage loop (the slot pointer itself stays transparent: the compiler
+    // must see which of the two LDS objects an in-flight load writes, or it
+    // waits for the loads before every LDS read):
+    // the compiler otherwise held the 18 x 2 row addresses (M0) and the lane
+    // offsets in registers, spilled them, and each reload's vmcnt(0) also
+    // waited for the loads just issued.  Per load this costs one scalar add
+    // (M0), one XOR and one shift.
+    int w64 = wave * 64;  // the wave's first row, in units (opaque; the slot keeps its identity)
+    asm volatile("" : "+s"(w64));
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
     if (!ragged) {
-      // one uniform row pointer, stepped by NW rows
       const char* rp = b + (key0 + wave) * sb;
 #pragma unroll
       for (int j = 0; j < kStageKeys / NW; ++j) {
-        __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(rp + moff[j % NX]),
-                                         (SSA_LDS void*)(slab + (wave + NW * j) * 64), 16, 0, 0);
+        const int row = wave + NW * j;
+        const uint32_t off = static_cast<uint32_t>(ln ^ lswz(row)) * 16;
+        __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(rp + off), (SSA_LDS void*)(slab + w64 + NW * 64 * j),
+                                         16, 0, 0);
         rp += NW * sb;
+        asm volatile("" : "+s"(rp));  // stepped in place, not 16 precomputed row addresses
       }
     } else {
 #pragma unroll 1
       for (int j = 0; j < kStageKeys / NW; ++j) {
         const int row = wave + NW * j;
-        const int key = min(key0 + row, L - 1);  // uniform
-        __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(b + key * sb + moff[j % NX]),
-                                         (SSA_LDS void*)(slab + row * 64), 16, 0, 0);
+        const char* src = b + min(key0 + row, L - 1) * sb;  // uniform
+        const uint32_t off = static_cast<uint32_t>(ln ^ lswz(row)) * 16;
+        __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(src + off), (SSA_LDS void*)(slab + row * 64), 16, 0,
+                                         0);
       }
     }
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
       const int t = wave + NW * m;
-      if (!ragged) {
-        __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(b + (key0 + 8 * t) * sb + toff),
-                                         (SSA_LDS void*)(slab + kLatMain + t * 64), 16, 0, 0);
-      } else {
-        const int row = 8 * t + (lane >> 3);
-        const int key = min(key0 + row, L - 1);
-        __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(b + key * sb + (64 + ((lane & 7) ^ tswz(row))) * 16),
-                                         (SSA_LDS void*)(slab + kLatMain + t * 64), 16, 0, 0);
-      }
+      const int row = 8 * t + (ln >> 3);
+      const int key = ragged ? min(key0 + row, L - 1) : key0 + row;
+      const uint32_t uoff = static_cast<uint32_t>(64 + ((ln & 7) ^ tswz(row))) * 16;
+      __builtin_amdgcn_global_load_lds((const SSA_GLB void*)(b + key * sb + uoff),
+                                       (SSA_LDS void*)(slab + kLatMain + t * 64), 16, 0, 0);
     }
   }
 };
